@@ -1,0 +1,201 @@
+"""CPU oracle for the NVFP4 paged KV cache -- TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes/numpy marshalling around ``nvfp4_oracle.c`` (plain scalar C in
+float64; every function there cites the page passage it follows).  Only the
+test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never imports, links or
+calls it, and the two share no code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libnvfp4_oracle.so")
+_lib = None
+
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_flt = ctypes.c_float
+_dbl = ctypes.c_double
+
+
+def build() -> str:
+    """Compile the oracle with gcc (strict IEEE: no contraction, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+           "-shared", "-fPIC", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    L = ctypes.CDLL(_LIB_PATH)
+    L.nvfp4o_e2m1_value.argtypes = [_int]
+    L.nvfp4o_e2m1_value.restype = _dbl
+    L.nvfp4o_e4m3_value.argtypes = [_int]
+    L.nvfp4o_e4m3_value.restype = _dbl
+    L.nvfp4o_e4m3_encode.argtypes = [_dbl]
+    L.nvfp4o_e4m3_encode.restype = _int
+    L.nvfp4o_e2m1_encode.argtypes = [_dbl]
+    L.nvfp4o_e2m1_encode.restype = _int
+    L.nvfp4o_quantize_rows.argtypes = [_f32p, _i64, _flt, _u8p, _u8p]
+    L.nvfp4o_quantize_rows.restype = None
+    L.nvfp4o_dequantize_rows.argtypes = [_u8p, _u8p, _i64, _flt, _f64p]
+    L.nvfp4o_dequantize_rows.restype = None
+    L.nvfp4o_scatter_rows.argtypes = [_u8p, _u8p, _i64, _int, _i32p, _int, _u8p, _u8p]
+    L.nvfp4o_scatter_rows.restype = None
+    L.nvfp4o_gather_rows.argtypes = [_u8p, _u8p, _i64, _int, _i32p, _int, _u8p, _u8p]
+    L.nvfp4o_gather_rows.restype = None
+    L.nvfp4o_decode_attention.argtypes = [_u8p, _u8p, _u8p, _u8p, _int, _flt, _flt, _f32p, _int, _i32p, _int,
+                                          _i32p, _flt, _i64p, _i64, _f64p]
+    L.nvfp4o_decode_attention.restype = None
+    L.nvfp4o_fp8_workspace.argtypes = [_u8p, _u8p, _int, _int, _flt, _i32p, _int, _int, _i32p, _i32p, _flt, _u8p]
+    L.nvfp4o_fp8_workspace.restype = None
+    L.nvfp4o_page_mode_dequant.argtypes = [_f64p, _i64, _i64, _f64p]
+    L.nvfp4o_page_mode_dequant.restype = None
+    L.nvfp4o_bytes_per_token_head.argtypes = []
+    L.nvfp4o_bytes_per_token_head.restype = _i64
+    L.nvfp4o_max_threads.argtypes = []
+    L.nvfp4o_max_threads.restype = _int
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ formats
+def e2m1_value(code: int) -> float:
+    return lib().nvfp4o_e2m1_value(int(code))
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().nvfp4o_e4m3_value(int(byte))
+
+
+def e4m3_encode(r: float) -> int:
+    return lib().nvfp4o_e4m3_encode(float(r))
+
+
+def e2m1_encode(y: float) -> int:
+    return lib().nvfp4o_e2m1_encode(float(y))
+
+
+# ------------------------------------------------------------- quantization
+def quantize_rows(x: np.ndarray, g: float):
+    """x: float32 [..., 128] -> (codes uint8 [n, 64], scales uint8 [n, 8])."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, 128)
+    n = x.shape[0]
+    codes = np.zeros((n, 64), np.uint8)
+    scales = np.zeros((n, 8), np.uint8)
+    lib().nvfp4o_quantize_rows(x, n, float(np.float32(g)), codes, scales)
+    return codes, scales
+
+
+def dequantize_rows(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, 64)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, 8)
+    out = np.zeros((codes.shape[0], 128), np.float64)
+    lib().nvfp4o_dequantize_rows(codes, scales, codes.shape[0], float(np.float32(g)), out)
+    return out
+
+
+class Planes:
+    """One layer's paged NVFP4 cache as four byte planes (host memory)."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int):
+        self.num_pages = int(num_pages)
+        self.H = int(num_kv_heads)
+        self.k_codes = np.zeros(self.num_pages * self.H * 1024, np.uint8)
+        self.k_scales = np.zeros(self.num_pages * self.H * 128, np.uint8)
+        self.v_codes = np.zeros(self.num_pages * self.H * 1024, np.uint8)
+        self.v_scales = np.zeros(self.num_pages * self.H * 128, np.uint8)
+
+
+def scatter_rows(codes, scales, slot_mapping, H: int, is_v: bool, code_plane, scale_plane):
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    assert codes.size == slots.size * H * 64 and scales.size == slots.size * H * 8
+    lib().nvfp4o_scatter_rows(codes, scales, slots.size, int(H), slots, int(bool(is_v)), code_plane, scale_plane)
+
+
+def gather_rows(code_plane, scale_plane, slot_mapping, H: int, is_v: bool):
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    codes = np.zeros((slots.size * H, 64), np.uint8)
+    scales = np.zeros((slots.size * H, 8), np.uint8)
+    lib().nvfp4o_gather_rows(code_plane, scale_plane, slots.size, int(H), slots, int(bool(is_v)), codes, scales)
+    return codes, scales
+
+
+def quantize_append(planes: Planes, k: np.ndarray, v: np.ndarray, slot_mapping, g_k: float, g_v: float):
+    """Quantize new tokens k, v (float32 [T, H, 128]) and write them at their slots."""
+    H = planes.H
+    kc, ks = quantize_rows(k, g_k)
+    vc, vs = quantize_rows(v, g_v)
+    scatter_rows(kc, ks, slot_mapping, H, False, planes.k_codes, planes.k_scales)
+    scatter_rows(vc, vs, slot_mapping, H, True, planes.v_codes, planes.v_scales)
+    return kc, ks, vc, vs
+
+
+# --------------------------------------------------------- decode attention
+def decode_attention(planes: Planes, g_k: float, g_v: float, q: np.ndarray, block_table: np.ndarray,
+                     seq_lens: np.ndarray, sm_scale: float, rows=None) -> np.ndarray:
+    """q: float32 [B, Hq, 128]; rows: flat indices b*Hq + qh (default: all).
+
+    Returns float64 [len(rows), 128]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    assert D == 128 and Hq % planes.H == 0
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    assert bt.shape[0] == B
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if rows is None:
+        rows = np.arange(B * Hq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, 128), np.float64)
+    lib().nvfp4o_decode_attention(planes.k_codes, planes.k_scales, planes.v_codes, planes.v_scales, planes.H,
+                                  float(np.float32(g_k)), float(np.float32(g_v)), q, Hq, bt, bt.shape[1], sl,
+                                  float(np.float32(sm_scale)), rows, rows.size, out)
+    return out
+
+
+def fp8_workspace(planes: Planes, is_v: bool, g: float, block_table, prefix_lens, ws_offsets, ws_scale: float,
+                  total_tokens: int) -> np.ndarray:
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    pl = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+    wo = np.ascontiguousarray(ws_offsets, dtype=np.int32)
+    out = np.zeros(int(total_tokens) * planes.H * 128, np.uint8)
+    cp, sp = (planes.v_codes, planes.v_scales) if is_v else (planes.k_codes, planes.k_scales)
+    lib().nvfp4o_fp8_workspace(cp, sp, int(bool(is_v)), planes.H, float(np.float32(g)), bt, bt.shape[1], pl.size,
+                               pl, wo, float(np.float32(ws_scale)), out)
+    return out.reshape(int(total_tokens), planes.H, 128)
+
+
+# ------------------------------------------------------ the page experiment
+def page_mode_dequant(x, block: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    lib().nvfp4o_page_mode_dequant(x, x.size, int(block), out)
+    return out
+
+
+def bytes_per_token_head() -> int:
+    return int(lib().nvfp4o_bytes_per_token_head())
+
+
+def max_threads() -> int:
+    return int(lib().nvfp4o_max_threads())

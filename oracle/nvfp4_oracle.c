@@ -1,0 +1,351 @@
+/*
+ * NVFP4 paged KV cache -- CPU ORACLE.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, scalar, float64 statement of what the NVFP4 KV-cache hot path
+ * computes.  Only the test suite, the smoke check and the bench's CPU-baseline
+ * leg load this file; the HIP library never includes, links or calls it, and
+ * it shares no code, header, table or helper with that library.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [MW]  grer.cn blog, "NVFP4 KV cache and the memory wall"
+ *         §1 memory accounting, §2 two-level scaling (value list + stdlib
+ *         experiment), §3 the three data flows in the serving engine.
+ *   [NV]  nmedialink.com, "NVIDIA NVFP4: LLM memory doubled, inference 3x"
+ *         section on the KV-cache quantize/dequantize flow (Fig. 3).
+ *   [TC]  cloud.tencent.com.cn, "NVFP4: breaking the memory wall of GPU
+ *         inference", section "E2M1 encoding and two-level scaling".
+ *
+ * Readings where the pages leave a step open (each also listed in the design
+ * notes):
+ *   R1 ties go to the even code (E2M1) / even byte (E4M3); the page's own
+ *      stdlib snap takes the first list entry instead -- kept only in
+ *      nvfp4o_page_mode_dequant() to reproduce the page's printed RMSE.
+ *   R2 block scale = E4M3 value nearest to amax/(6*g) (the page's script keeps
+ *      it unrounded and has no g); saturates at 448, values below the E4M3
+ *      grid's half-step round to 0.
+ *   R3 codes saturate at magnitude 6 (code 7).
+ *   R4 E4M3 is OCP E4M3FN: bias 7, subnormals m*2^-9, max 448, no infinity.
+ *   R5 the sign bit of a code is the sign bit of the input (so -0.0 and small
+ *      negatives that round to 0 give code 0x8).
+ *   R6 blocks are 16 consecutive values along head_dim of one (token, head).
+ *   R7 low nibble = even element.
+ *   R8 a zero scale (amax == 0 or amax/(6g) rounding to 0) gives scale byte 0
+ *      and magnitude code 0 for every element.
+ *
+ * Exactness of the float64 quotients used below.  Inputs are float32 (24-bit
+ * significands), g is float32, block scales are E4M3 (4-bit significands) and
+ * every rounding boundary (a midpoint between two adjacent grid values) has at
+ * most 5 significant bits.  A boundary times the divisor therefore has at most
+ * 5 + 24 + 2 = 31 significant bits, while the dividend has 24 (or 30 for a
+ * dequantized value), so a dividend that is not exactly on a boundary is at
+ * least 2^-32 (relative) away from it -- far more than the 2^-53 error of one
+ * correctly rounded float64 division.  Exact ties divide exactly.  Hence
+ * rounding the float64 quotient gives the same grid point as rounding the
+ * exact real quotient.  Products bs*g (28 bits) and e2m1*bs*g (30 bits) are
+ * exact in float64.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- formats */
+
+/* E2M1 value of a 4-bit code: bit 3 sign, bits 2..1 exponent (bias 1),
+ * bit 0 mantissa; exponent 0 is subnormal (mantissa * 0.5).  [TC] encoding
+ * section (1 sign, 2 exponent, 1 mantissa bit); the resulting magnitudes are
+ * the list in [MW] §2. */
+double nvfp4o_e2m1_value(int code) {
+  int e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return (code & 8) ? -mag : mag;
+}
+
+/* OCP E4M3FN value of a byte (reading R4): bit 7 sign, bits 6..3 exponent
+ * (bias 7), bits 2..0 mantissa; exponent 0 subnormal m/8 * 2^-6; 0x7F/0xFF NaN.
+ * [MW] §2 and [TC]: the per-16 block scale is FP8 E4M3. */
+double nvfp4o_e4m3_value(int byte) {
+  int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest non-negative finite E4M3 value to r >= 0; ties to the even byte;
+ * everything above 448 goes to 448 (readings R2, R4).  Brute force over the
+ * 127 finite non-negative bytes. */
+int nvfp4o_e4m3_encode(double r) {
+  if (r >= 448.0) return 0x7E; /* saturation: 448 is the nearest finite value */
+  int best = 0;
+  double bestd = fabs(r - 0.0);
+  for (int b = 1; b <= 0x7E; ++b) {
+    double d = fabs(r - nvfp4o_e4m3_value(b));
+    if (d < bestd || (d == bestd && (b & 1) == 0 && (best & 1) == 1)) {
+      best = b;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* Nearest E2M1 magnitude code (0..7) to y >= 0; ties to the even code;
+ * y above 6 goes to code 7 (readings R1, R3).  Brute force over 8 values. */
+int nvfp4o_e2m1_encode(double y) {
+  if (y >= 6.0) return 7; /* saturation: 6 is the nearest value */
+  int best = 0;
+  double bestd = fabs(y);
+  for (int c = 1; c < 8; ++c) {
+    double d = fabs(y - nvfp4o_e2m1_value(c));
+    if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* ----------------------------------------------------------- quantization */
+
+/* Two-level NVFP4 quantization of rows of 128 values (one row = one token of
+ * one KV head) with FP32 global scale g ([MW] §2: 16 consecutive values share
+ * one E4M3 scale, the whole tensor shares one FP32 scale; [TC] same).
+ *   codes : n_rows x 64 bytes, byte j = code(2j) | code(2j+1) << 4   (R7)
+ *   scales: n_rows x 8 bytes, byte b = E4M3 scale of values 16b..16b+15 (R6)
+ * Per block: amax = max|x|, bs = E4M3(amax/(6g)) (R2), each code = sign(x) |
+ * E2M1(|x|/(bs*g)) (R1, R3, R5), zero scale -> magnitude 0 (R8). */
+void nvfp4o_quantize_rows(const float* x, int64_t n_rows, float g, uint8_t* codes, uint8_t* scales) {
+  const double gd = (double)g;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const float* xr = x + r * 128;
+    uint8_t* cr = codes + r * 64;
+    uint8_t* sr = scales + r * 8;
+    memset(cr, 0, 64);
+    for (int b = 0; b < 8; ++b) {
+      double amax = 0.0;
+      for (int i = 0; i < 16; ++i) {
+        double a = fabs((double)xr[16 * b + i]);
+        if (a > amax) amax = a;
+      }
+      int sb = nvfp4o_e4m3_encode(amax / (6.0 * gd));
+      double bs = nvfp4o_e4m3_value(sb);
+      sr[b] = (uint8_t)sb;
+      for (int i = 0; i < 16; ++i) {
+        int d = 16 * b + i;
+        double v = (double)xr[d];
+        int mag = (bs == 0.0) ? 0 : nvfp4o_e2m1_encode(fabs(v) / (bs * gd));
+        int code = (signbit(v) ? 8 : 0) | mag;
+        cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
+      }
+    }
+  }
+}
+
+/* x_hat = E2M1(code) * E4M3(scale) * g, the dequantized value ([MW] §2 and
+ * §3: the block scale and the tensor-wide FP32 scale multiply the 4-bit
+ * value).  Exact in float64. */
+void nvfp4o_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, float g, double* out) {
+  for (int64_t r = 0; r < n_rows; ++r)
+    for (int d = 0; d < 128; ++d) {
+      int code = (codes[r * 64 + d / 2] >> (4 * (d & 1))) & 15;
+      out[r * 128 + d] = nvfp4o_e2m1_value(code) * nvfp4o_e4m3_value(scales[r * 8 + d / 16]) * (double)g;
+    }
+}
+
+/* ------------------------------------------------------------- page layout
+ * A page holds 16 token slots; slot s -> page p = s/16, offset o = s%16.
+ * Per (page, kv head) each plane holds a 1 KiB code tile and a 128 B scale
+ * tile (64 + 8 bytes per token and head: 9/16 byte per value, [MW] §1).
+ *   K codes : tile byte o*64 + d/2                              nibble d%2
+ *   K scales: tile byte o*8 + d/16
+ *   V codes : tile byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2 nibble d%2
+ *   V scales: tile byte (d/16)*16 + o
+ * Tile (p, h) starts at (p*H + h)*1024 in a code plane and at (p*H + h)*128
+ * in a scale plane. */
+static int64_t k_code_byte(int64_t p, int h, int H, int o, int d) { return (p * H + h) * 1024 + o * 64 + d / 2; }
+static int64_t k_scale_byte(int64_t p, int h, int H, int o, int b) { return (p * H + h) * 128 + o * 8 + b; }
+static int64_t v_code_byte(int64_t p, int h, int H, int o, int d) {
+  return (p * H + h) * 1024 + (o / 4) * 256 + (d / 8) * 16 + (o % 4) * 4 + (d % 8) / 2;
+}
+static int64_t v_scale_byte(int64_t p, int h, int H, int o, int b) { return (p * H + h) * 128 + b * 16 + o; }
+
+/* Write quantized rows (row index t*H + h) into the planes at slot_mapping[t];
+ * negative slots are skipped. is_v selects the V layout. */
+void nvfp4o_scatter_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_tokens, int H, const int32_t* slot_mapping,
+                         int is_v, uint8_t* code_plane, uint8_t* scale_plane) {
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t p = s / 16;
+    int o = (int)(s % 16);
+    for (int h = 0; h < H; ++h) {
+      const uint8_t* cr = codes + (t * H + h) * 64;
+      const uint8_t* sr = scales + (t * H + h) * 8;
+      for (int d = 0; d < 128; ++d) {
+        int code = (cr[d / 2] >> (4 * (d & 1))) & 15;
+        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+        int sh = 4 * (d & 1);
+        code_plane[at] = (uint8_t)((code_plane[at] & ~(15 << sh)) | (code << sh));
+      }
+      for (int b = 0; b < 8; ++b)
+        scale_plane[is_v ? v_scale_byte(p, h, H, o, b) : k_scale_byte(p, h, H, o, b)] = sr[b];
+    }
+  }
+}
+
+/* Dequantized value of dimension d of (slot s, head h) read from the planes. */
+static double plane_value(const uint8_t* code_plane, const uint8_t* scale_plane, int is_v, int64_t s, int h, int H, int d,
+                          double g) {
+  int64_t p = s / 16;
+  int o = (int)(s % 16);
+  int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+  int code = (code_plane[at] >> (4 * (d & 1))) & 15;
+  int sb = scale_plane[is_v ? v_scale_byte(p, h, H, o, d / 16) : k_scale_byte(p, h, H, o, d / 16)];
+  return nvfp4o_e2m1_value(code) * nvfp4o_e4m3_value(sb) * g;
+}
+
+/* Read logical rows back out of the planes (codes and scale bytes), for the
+ * layout tests. */
+void nvfp4o_gather_rows(const uint8_t* code_plane, const uint8_t* scale_plane, int64_t n_tokens, int H,
+                        const int32_t* slot_mapping, int is_v, uint8_t* codes, uint8_t* scales) {
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    int64_t p = s / 16;
+    int o = (int)(s % 16);
+    for (int h = 0; h < H; ++h) {
+      uint8_t* cr = codes + (t * H + h) * 64;
+      memset(cr, 0, 64);
+      for (int d = 0; d < 128; ++d) {
+        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+        int code = (code_plane[at] >> (4 * (d & 1))) & 15;
+        cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
+      }
+      for (int b = 0; b < 8; ++b)
+        scales[(t * H + h) * 8 + b] = scale_plane[is_v ? v_scale_byte(p, h, H, o, b) : k_scale_byte(p, h, H, o, b)];
+    }
+  }
+}
+
+/* ------------------------------------------------------ decode attention
+ * One decode step over the paged NVFP4 cache ([MW] §3, third data flow: the
+ * decode kernel dequantizes K/V where it reads them; [NV] KV-cache primer:
+ * the new query attends over every cached K/V).  For each selected query row
+ * (b, qh), with kv head h = qh / (Hq/Hkv) (grouped-query heads, [MW] §1):
+ *   s_t = sm_scale * sum_d q[d] * K_hat[t][d]   for t < seq_lens[b]
+ *   p   = softmax(s)                            (float64, max-subtracted)
+ *   o   = sum_t p_t * V_hat[t]
+ * token t lives in slot block_table[b*bt_stride + t/16]*16 + t%16.  An empty
+ * sequence gives o = 0.  rows[i] = b*Hq + qh; out is n_rows x 128 float64. */
+void nvfp4o_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int Hkv, float g_k,
+                             float g_v, const float* q, int Hq, const int32_t* block_table, int bt_stride,
+                             const int32_t* seq_lens, float sm_scale, const int64_t* rows, int64_t n_rows, double* out) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t b = rows[i] / Hq;
+    int qh = (int)(rows[i] % Hq);
+    int h = qh / G;
+    int64_t n = seq_lens[b];
+    const float* qr = q + rows[i] * 128;
+    double* o = out + i * 128;
+    for (int d = 0; d < 128; ++d) o[d] = 0.0;
+    if (n <= 0) continue;
+    double* s = (double*)malloc((size_t)n * sizeof(double));
+    double m = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+      int64_t slot = (int64_t)block_table[b * bt_stride + t / 16] * 16 + t % 16;
+      double acc = 0.0;
+      for (int d = 0; d < 128; ++d) acc += (double)qr[d] * plane_value(kc, ks, 0, slot, h, Hkv, d, g_k);
+      s[t] = (double)sm_scale * acc;
+      if (s[t] > m) m = s[t];
+    }
+    double l = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+      int64_t slot = (int64_t)block_table[b * bt_stride + t / 16] * 16 + t % 16;
+      double pt = exp(s[t] - m);
+      l += pt;
+      for (int d = 0; d < 128; ++d) o[d] += pt * plane_value(vc, vs, 1, slot, h, Hkv, d, g_v);
+    }
+    free(s);
+    for (int d = 0; d < 128; ++d) o[d] /= l;
+  }
+}
+
+/* ----------------------------------------------------- FP8 workspace dequant
+ * Extend / chunked-prefill flow ([MW] §3 second data flow; [NV] Fig. 3: the
+ * NVFP4 cache is dequantized to FP8 before the attention that consumes it).
+ * For extend sequence i and cached token t < prefix_lens[i]:
+ *   ws[(ws_offsets[i] + t)*Hkv*128 + h*128 + d] =
+ *       sign(x_hat) | E4M3(|x_hat| / ws_scale)       x_hat = E2M1*bs*g
+ * E4M3 rounding as the block scale (nearest, ties to even, saturate at 448);
+ * the sign bit follows x_hat, so -0.0 and tiny negatives give 0x80. */
+void nvfp4o_fp8_workspace(const uint8_t* code_plane, const uint8_t* scale_plane, int is_v, int Hkv, float g,
+                          const int32_t* block_table, int bt_stride, int num_seqs, const int32_t* prefix_lens,
+                          const int32_t* ws_offsets, float ws_scale, uint8_t* ws) {
+  for (int i = 0; i < num_seqs; ++i) {
+    int64_t n = prefix_lens[i];
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+      int64_t slot = (int64_t)block_table[(int64_t)i * bt_stride + t / 16] * 16 + t % 16;
+      for (int h = 0; h < Hkv; ++h)
+        for (int d = 0; d < 128; ++d) {
+          double xh = plane_value(code_plane, scale_plane, is_v, slot, h, Hkv, d, (double)g);
+          int byte = nvfp4o_e4m3_encode(fabs(xh) / (double)ws_scale);
+          if (signbit(xh)) byte |= 0x80;
+          ws[((int64_t)ws_offsets[i] + t) * Hkv * 128 + h * 128 + d] = (uint8_t)byte;
+        }
+    }
+  }
+}
+
+/* --------------------------------------------------- the page's experiment
+ * [MW] §2 stdlib experiment, reproduced operation for operation: per block of
+ * `block` values, scale = amax/6 (1.0 when amax <= 1e-12, no rounding, no
+ * global scale) and each value becomes snap(v/scale)*scale, where snap picks
+ * the first entry of the 16-value list (ordered -6 .. -0.0, 0.0 .. 6) with the
+ * smallest |entry - x|.  block = n gives the global-only comparator. */
+void nvfp4o_page_mode_dequant(const double* x, int64_t n, int64_t block, double* out) {
+  static const double grid[16] = {-6.0, -4.0, -3.0, -2.0, -1.5, -1.0, -0.5, -0.0,
+                                  0.0,  0.5,  1.0,  1.5,  2.0,  3.0,  4.0,  6.0};
+  for (int64_t s = 0; s < n; s += block) {
+    int64_t e = s + block < n ? s + block : n;
+    double amax = 0.0;
+    for (int64_t i = s; i < e; ++i)
+      if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    double scale = amax > 1e-12 ? amax / 6.0 : 1.0;
+    for (int64_t i = s; i < e; ++i) {
+      double y = x[i] / scale;
+      int best = 0;
+      double bestd = fabs(grid[0] - y);
+      for (int k = 1; k < 16; ++k) {
+        double d = fabs(grid[k] - y);
+        if (d < bestd) {
+          best = k;
+          bestd = d;
+        }
+      }
+      out[i] = grid[best] * scale;
+    }
+  }
+}
+
+/* Bytes the cache planes take per (token, kv head): 64 code bytes + 8 scale
+ * bytes for each of K and V ([MW] §1: 16 E2M1 values in 8 bytes plus one
+ * E4M3 byte = 9/16 byte per value). */
+int64_t nvfp4o_bytes_per_token_head(void) { return 2 * (64 + 8); }
+
+/* Threads OpenMP will use (for the reported CPU-baseline core count). */
+int nvfp4o_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
