@@ -1,0 +1,168 @@
+/*
+ * nvfp4_kv.h -- C ABI of the MI355X (gfx950) NVFP4 paged KV-cache library.
+ *
+ * NVFP4 stores each K/V value as a 4-bit E2M1 code (values +-{0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6}), every 16 consecutive values along head_dim share one FP8 E4M3
+ * block scale, and each tensor has one FP32 global scale: 9/16 byte per value
+ * (grer.cn blog "NVFP4 KV cache and the memory wall", section 2, two-level
+ * scaling, and section 1 for the 9/16 byte accounting; cloud.tencent.com.cn
+ * "NVFP4: breaking the memory wall of GPU inference", E2M1 encoding section).
+ *
+ * The three entry points are the three cache data flows of section 3 of the
+ * same blog: quantize-on-write of new K/V, decode attention that dequantizes
+ * inside the kernel, and extend-path dequantization into one FP8 workspace
+ * that is reused across layers.
+ *
+ * Conventions for every function
+ *   - All array arguments are DEVICE pointers unless marked "host".  The caller
+ *     owns every buffer; the library never allocates, frees, synchronizes, or
+ *     reads device memory from the host.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; results are visible after the caller's stream sync.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns a status and enqueues nothing.  A launch failure returns
+ *     NVFP4_ERR_HIP.  Functions are stateless and thread-safe.
+ *   - Supported shapes: head_dim 128 and page_size 16 only (others return
+ *     NVFP4_ERR_UNSUPPORTED); at most 16 query heads per KV head.
+ *   - Device-side index data (slot_mapping, block_table, seq_lens, prefix_lens,
+ *     ws_offsets) is bounds-checked in the kernels: an out-of-range slot or page
+ *     index is skipped (its tokens are ignored), never dereferenced.
+ *
+ * Cache layout (one layer; 16 token slots per page; slot s is page s/16,
+ * offset o = s%16; tile (p, h) = page p, KV head h):
+ *   k_codes  [num_pages][H][1024] u8: byte o*64 + d/2 of the tile holds dims
+ *            d (even: low nibble) and d+1 (high nibble) of token o.
+ *   k_scales [num_pages][H][128]  u8: byte o*8 + b = E4M3 scale of dims 16b..16b+15.
+ *   v_codes  [num_pages][H][1024] u8: byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2
+ *            holds dims d (low nibble, d even) and d+1 of token o.
+ *   v_scales [num_pages][H][128]  u8: byte (d/16)*16 + o.
+ *   An E2M1 code is sign<<3 | magnitude code (0..7 <-> 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *   A value reads back as E2M1(code) * E4M3(scale) * global (k_global or v_global).
+ */
+#ifndef NVFP4_KV_H
+#define NVFP4_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define NVFP4_API __attribute__((visibility("default")))
+#else
+#define NVFP4_API
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad scale, inconsistent sizes */
+  NVFP4_ERR_UNSUPPORTED = 2,      /* head_dim != 128, page_size != 16, >16 q heads per kv head, alignment */
+  NVFP4_ERR_WORKSPACE_TOO_SMALL = 3,
+  NVFP4_ERR_HIP = 4               /* a HIP launch reported an error */
+} nvfp4_status_t;
+
+typedef enum nvfp4_dtype {
+  NVFP4_DTYPE_F32 = 0,
+  NVFP4_DTYPE_BF16 = 1
+} nvfp4_dtype_t;
+
+/* One layer's NVFP4 cache.  Plane pointers are device memory with the sizes
+ * given in the layout above; code planes 16-byte aligned, scale planes 4-byte
+ * aligned.  k_global / v_global are the FP32 per-tensor scales; they must be
+ * finite with 2^-100 <= g <= 2^100. */
+typedef struct nvfp4_kv_layer {
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;  /* must be 128 */
+  int32_t page_size; /* must be 16 */
+  float k_global;
+  float v_global;
+} nvfp4_kv_layer_t;
+
+/* Quantize-on-append (blog section 3, first data flow: new K/V are written to
+ * the cache as NVFP4; nmedialink.com "NVIDIA NVFP4: LLM memory doubled,
+ * inference 3x", Fig. 3: new keys and values are quantized before they are
+ * appended).  For each new token t < num_tokens with slot = slot_mapping[t]
+ * (skipped when slot < 0 or slot >= num_pages*16), and each KV head h and
+ * 16-value block b along head_dim:
+ *   amax = max |x|,  bs = E4M3 nearest to amax/(6*g) (ties to even, saturating
+ *   at 448, 0 below half the smallest step), code = sign(x) | E2M1 nearest to
+ *   |x|/(bs*g) (ties to even, saturating at 6; magnitude 0 when bs = 0).
+ *   k_new, v_new : [num_tokens][num_kv_heads][128] of `dtype`; consecutive tokens
+ *                  are token_stride_elems elements apart (>= num_kv_heads*128);
+ *                  16-byte aligned base and token stride.  Values must be finite.
+ *   slot_mapping : [num_tokens] int32.
+ * Slots that appear twice in one call are written by both tokens in an
+ * unspecified order.  num_tokens == 0 is a no-op. */
+NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                  const int32_t* slot_mapping, void* stream);
+
+/* Bytes of device workspace nvfp4_paged_decode_attn needs for these (host)
+ * sizes; 0 when batch or max_seq_len is 0.  Returns 0 for invalid sizes too. */
+NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t max_seq_len);
+
+/* Decode attention over the paged NVFP4 cache, dequantizing inside the kernel
+ * (blog section 3, third data flow: decode is bound by reading the cache, so
+ * no separate dequant pass; the 4-bit values are widened in registers and the
+ * block scale is applied there).  For each sequence b < batch and query head
+ * j < num_q_heads, with KV head h = j / (num_q_heads / num_kv_heads):
+ *   s_t = sm_scale * q[b][j] . K_hat[t]   for t < seq_lens[b],
+ *   out[b][j] = sum_t softmax(s)_t * V_hat[t]            (fp32 accumulate)
+ * where token t sits in slot block_table[b*block_table_stride + t/16]*16 + t%16
+ * and K_hat/V_hat are the dequantized values.  seq_lens[b] == 0 gives zeros.
+ *   q            : [batch][num_q_heads][128] of q_dtype (16-byte aligned).
+ *   block_table  : [batch][block_table_stride] int32 page indices.
+ *   seq_lens     : [batch] int32, each <= max_seq_len (larger values are
+ *                  clamped to max_seq_len).
+ *   max_seq_len  : host bound used to size the launch; block_table_stride must
+ *                  be >= ceil(max_seq_len/16).
+ *   out          : [batch][num_q_heads][128] float32.
+ *   workspace    : >= nvfp4_paged_decode_workspace_bytes(...) bytes, 16-byte
+ *                  aligned; holds split-K partial results; contents on entry are
+ *                  ignored.  Calls that share a workspace must be ordered on
+ *                  one stream. */
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream);
+
+/* Extend-path dequantization into one FP8 workspace pair (blog section 3,
+ * second data flow: cached NVFP4 pages are dequantized into a single FP8
+ * workspace that every layer reuses; nmedialink.com, Fig. 3: values are taken
+ * from NVFP4 back to FP8 before attention).  For extend sequence i < num_seqs
+ * and cached token t < prefix_lens[i] (slot from block_table row i as above):
+ *   ws_k[(ws_offsets[i] + t)][h][d] = sign(x) | E4M3 nearest to |x|/k_ws_scale
+ *   (x = K_hat value; ties to even, saturating at 448; sign bit kept, so -0.0
+ *   gives 0x80), and likewise ws_v with V_hat and v_ws_scale.
+ *   prefix_lens : [num_seqs] int32;  ws_offsets : [num_seqs+1] int32 token
+ *                 offsets into the workspace.
+ *   max_prefix_len: host bound, >= every prefix_lens[i] (sizes the launch;
+ *                 larger prefix_lens are clamped to it); block_table_stride
+ *                 must be >= ceil(max_prefix_len/16).
+ *   ws_k, ws_v  : [ws_capacity_tokens][num_kv_heads][128] uint8; rows at or
+ *                 beyond ws_capacity_tokens are never written.
+ *   k_ws_scale, v_ws_scale: finite, 2^-100 <= s <= 2^100. */
+NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* layer, const int32_t* block_table,
+                                                        int32_t block_table_stride, int32_t num_seqs,
+                                                        const int32_t* prefix_lens, const int32_t* ws_offsets,
+                                                        int32_t max_prefix_len, float k_ws_scale, float v_ws_scale,
+                                                        uint8_t* ws_k, uint8_t* ws_v, int32_t ws_capacity_tokens,
+                                                        void* stream);
+
+/* Static string for a status code. */
+NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_KV_H */

@@ -1,0 +1,232 @@
+"""NVFP4 paged KV cache for MI355X (gfx950): Python binding of ``libnvfp4kv.so``.
+
+Argument marshalling only: every step of quantize-append, decode attention and
+the FP8 workspace dequant runs in the library's HIP kernels.  The functions
+take torch tensors (device memory) and enqueue on torch's current HIP stream.
+The C ABI and the cache layout are documented in ``include/nvfp4_kv.h``.
+
+Importing this module raises if the library has not been built (there is no
+fallback implementation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libnvfp4kv.so")
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+TILE_CODE_BYTES = 1024
+TILE_SCALE_BYTES = 128
+
+NVFP4_OK = 0
+NVFP4_ERR_INVALID_ARGUMENT = 1
+NVFP4_ERR_UNSUPPORTED = 2
+NVFP4_ERR_WORKSPACE_TOO_SMALL = 3
+NVFP4_ERR_HIP = 4
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+# Every function the public header declares.
+EXPORTED_SYMBOLS = (
+    "nvfp4_kv_quantize_append",
+    "nvfp4_paged_decode_workspace_bytes",
+    "nvfp4_paged_decode_attn",
+    "nvfp4_dequant_to_fp8_workspace",
+    "nvfp4_status_string",
+)
+
+
+class CKVLayer(ctypes.Structure):
+    """Mirror of ``nvfp4_kv_layer_t``."""
+
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("k_global", ctypes.c_float),
+        ("v_global", ctypes.c_float),
+    ]
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python nvfp4_quantized_paged_kv_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lp = ctypes.POINTER(CKVLayer)
+    L.nvfp4_kv_quantize_append.argtypes = [lp, vp, vp, ctypes.c_int, i32, i64, vp, vp]
+    L.nvfp4_kv_quantize_append.restype = ctypes.c_int
+    L.nvfp4_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.nvfp4_paged_decode_workspace_bytes.restype = sz
+    L.nvfp4_paged_decode_attn.argtypes = [lp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    L.nvfp4_paged_decode_attn.restype = ctypes.c_int
+    L.nvfp4_dequant_to_fp8_workspace.argtypes = [lp, vp, i32, i32, vp, vp, i32, f32, f32, vp, vp, i32, vp]
+    L.nvfp4_dequant_to_fp8_workspace.restype = ctypes.c_int
+    L.nvfp4_status_string.argtypes = [ctypes.c_int]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.nvfp4_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != NVFP4_OK:
+        raise NVFP4Error(status, what)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dev_i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+@dataclass
+class KVCacheLayer:
+    """One layer's paged NVFP4 cache: four byte planes in device memory."""
+
+    k_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_codes: torch.Tensor
+    v_scales: torch.Tensor
+    num_pages: int
+    num_kv_heads: int
+    k_global: float
+    v_global: float
+
+    @staticmethod
+    def allocate(num_pages: int, num_kv_heads: int, k_global: float, v_global: float,
+                 device="cuda") -> "KVCacheLayer":
+        n = int(num_pages) * int(num_kv_heads)
+        z = lambda per: torch.zeros(n * per, dtype=torch.uint8, device=device)
+        return KVCacheLayer(z(TILE_CODE_BYTES), z(TILE_SCALE_BYTES), z(TILE_CODE_BYTES), z(TILE_SCALE_BYTES),
+                            int(num_pages), int(num_kv_heads), float(k_global), float(v_global))
+
+    def c_struct(self) -> CKVLayer:
+        return CKVLayer(self.k_codes.data_ptr(), self.k_scales.data_ptr(), self.v_codes.data_ptr(),
+                        self.v_scales.data_ptr(), self.num_pages, self.num_kv_heads, HEAD_DIM, PAGE_SIZE,
+                        self.k_global, self.v_global)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+
+
+def quantize_append(layer: KVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    stream=None) -> None:
+    """Quantize k, v ([T, H, 128] or [T, H*128], bf16/f32, token-strided) into their slots."""
+    if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape, dtype and strides")
+    T = k.shape[0]
+    _dev_i32(slot_mapping, "slot_mapping")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    if k.dim() == 3:
+        if (k.shape[1:] != (layer.num_kv_heads, HEAD_DIM) or k.stride(2) != 1
+                or (k.shape[1] > 1 and k.stride(1) != HEAD_DIM)):
+            raise ValueError("k/v must be [T, H, 128] with contiguous heads")
+    elif k.dim() != 2 or k.shape[1] != layer.num_kv_heads * HEAD_DIM or k.stride(1) != 1:
+        raise ValueError("k/v must be [T, H, 128] or [T, H*128]")
+    c = layer.c_struct()
+    st = lib.nvfp4_kv_quantize_append(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), T,
+                                      k.stride(0) if T > 0 else layer.num_kv_heads * HEAD_DIM,
+                                      _ptr(slot_mapping), _stream(stream))
+    _check(st, "nvfp4_kv_quantize_append")
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int) -> int:
+    return int(lib.nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
+
+
+def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                      max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention of q [B, Hq, 128] (bf16/f32) over the cache; returns f32 [B, Hq, 128]."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    B, Hq, _ = q.shape
+    _dev_i32(block_table, "block_table")
+    _dev_i32(seq_lens, "seq_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table must be [B, stride] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be a contiguous float32 [B, Hq, 128] tensor")
+    need = decode_workspace_bytes(B, Hq, layer.num_kv_heads, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = layer.c_struct()
+    st = lib.nvfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), B, Hq, _ptr(block_table),
+                                     block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+                                     _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_paged_decode_attn")
+    return out
+
+
+def dequant_to_fp8_workspace(layer: KVCacheLayer, block_table: torch.Tensor, prefix_lens: torch.Tensor,
+                             ws_offsets: torch.Tensor, max_prefix_len: int, k_ws_scale: float, v_ws_scale: float,
+                             ws_k: torch.Tensor, ws_v: torch.Tensor, stream=None) -> None:
+    """Dequantize the cached prefixes into the FP8 E4M3 workspace pair ws_k, ws_v [cap, H, 128] (uint8)."""
+    _dev_i32(block_table, "block_table")
+    _dev_i32(prefix_lens, "prefix_lens")
+    _dev_i32(ws_offsets, "ws_offsets")
+    n = prefix_lens.numel()
+    if block_table.dim() != 2 or block_table.shape[0] != n or ws_offsets.numel() != n + 1:
+        raise ValueError("block_table [n, stride], prefix_lens [n], ws_offsets [n+1]")
+    for w in (ws_k, ws_v):
+        if w.dtype not in (torch.uint8, torch.float8_e4m3fn) or not w.is_contiguous():
+            raise ValueError("workspace must be contiguous uint8 / float8_e4m3fn")
+        if w.dim() != 3 or w.shape[1:] != (layer.num_kv_heads, HEAD_DIM):
+            raise ValueError("workspace must be [capacity, H, 128]")
+    if ws_k.shape != ws_v.shape:
+        raise ValueError("ws_k and ws_v must have the same shape")
+    c = layer.c_struct()
+    st = lib.nvfp4_dequant_to_fp8_workspace(ctypes.byref(c), _ptr(block_table), block_table.shape[1], n,
+                                            _ptr(prefix_lens), _ptr(ws_offsets), int(max_prefix_len),
+                                            float(k_ws_scale), float(v_ws_scale), _ptr(ws_k), _ptr(ws_v),
+                                            ws_k.shape[0], _stream(stream))
+    _check(st, "nvfp4_dequant_to_fp8_workspace")

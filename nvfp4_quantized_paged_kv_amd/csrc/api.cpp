@@ -1,0 +1,165 @@
+// Host side of the C ABI declared in include/nvfp4_kv.h: argument validation
+// (pure host code, before any HIP call) and kernel launches on the caller's
+// stream.  The library allocates nothing and never synchronizes.
+#include <cmath>
+#include <cstdint>
+
+#include "nvfp4_kv.h"
+#include "nvfp4_kv_internal.h"
+
+using namespace nvfp4kv;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// FP32 scales the exact-rounding arguments of the kernels cover.
+bool scale_ok(float s) { return std::isfinite(s) && s >= 0x1p-100f && s <= 0x1p100f; }
+
+nvfp4_status_t check_layer(const nvfp4_kv_layer_t* L) {
+  if (L == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (L->head_dim != kHeadDim || L->page_size != kPageSize) return NVFP4_ERR_UNSUPPORTED;
+  if (!L->k_codes || !L->k_scales || !L->v_codes || !L->v_scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (L->num_pages <= 0 || L->num_kv_heads <= 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((int64_t)L->num_pages * kPageSize > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;  // slots are int32
+  if (!aligned(L->k_codes, 16) || !aligned(L->v_codes, 16) || !aligned(L->k_scales, 4) || !aligned(L->v_scales, 4))
+    return NVFP4_ERR_UNSUPPORTED;
+  if (!scale_ok(L->k_global) || !scale_ok(L->v_global)) return NVFP4_ERR_INVALID_ARGUMENT;
+  return NVFP4_OK;
+}
+
+bool dtype_ok(nvfp4_dtype_t d) { return d == NVFP4_DTYPE_F32 || d == NVFP4_DTYPE_BF16; }
+
+nvfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported shape, layout or alignment";
+    case NVFP4_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case NVFP4_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                  const int32_t* slot_mapping, void* stream) {
+  const nvfp4_status_t st = check_layer(layer);
+  if (st != NVFP4_OK) return st;
+  if (!dtype_ok(dtype) || num_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return NVFP4_OK;
+  if (!k_new || !v_new || !slot_mapping) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (token_stride_elems < (int64_t)layer->num_kv_heads * kHeadDim) return NVFP4_ERR_INVALID_ARGUMENT;
+  const int64_t esize = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || (token_stride_elems * esize) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  AppendParams p;
+  p.t[0] = AppendTensor{k_new, layer->k_codes, layer->k_scales, layer->k_global};
+  p.t[1] = AppendTensor{v_new, layer->v_codes, layer->v_scales, layer->v_global};
+  p.slots = slot_mapping;
+  p.token_stride = token_stride_elems;
+  p.num_tokens = num_tokens;
+  p.H = layer->num_kv_heads;
+  p.num_pages = layer->num_pages;
+  return from_hip(launch_quantize_append(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t max_seq_len) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return 0;
+  return decode_geometry(batch, num_q_heads, num_kv_heads, max_seq_len).workspace_bytes;
+}
+
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  const nvfp4_status_t st = check_layer(layer);
+  if (st != NVFP4_OK) return st;
+  if (!dtype_ok(q_dtype) || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % layer->num_kv_heads != 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_q_heads / layer->num_kv_heads > kMaxGroup) return NVFP4_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return NVFP4_OK;
+  if (!q || !block_table || !seq_lens || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((int64_t)block_table_stride * kPageSize < (int64_t)max_seq_len || block_table_stride < 0)
+    return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16)) return NVFP4_ERR_UNSUPPORTED;
+  const DecodeGeometry geo = decode_geometry(batch, num_q_heads, layer->num_kv_heads, max_seq_len);
+  if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
+  if (geo.workspace_bytes > 0 && (!workspace || !aligned(workspace, 16))) return NVFP4_ERR_INVALID_ARGUMENT;
+  const double qk = (double)sm_scale * (double)layer->k_global * 1.4426950408889634;  // log2(e)
+  if (!std::isfinite(qk)) return NVFP4_ERR_INVALID_ARGUMENT;
+  DecodeParams p;
+  p.k_codes = layer->k_codes;
+  p.k_scales = layer->k_scales;
+  p.v_codes = layer->v_codes;
+  p.v_scales = layer->v_scales;
+  p.q = q;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  const int64_t G = num_q_heads / layer->num_kv_heads;
+  const int64_t units = (int64_t)batch * layer->num_kv_heads * geo.num_splits * G;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_ml = geo.workspace_bytes > 0 ? static_cast<float*>(workspace) + units * kHeadDim : nullptr;
+  p.out = out;
+  p.num_pages = layer->num_pages;
+  p.H = layer->num_kv_heads;
+  p.G = (int32_t)G;
+  p.Hq = num_q_heads;
+  p.batch = batch;
+  p.bt_stride = block_table_stride;
+  p.max_seq_len = max_seq_len;
+  p.pages_per_split = geo.pages_per_split > 0 ? geo.pages_per_split : 4;
+  p.num_splits = geo.num_splits;
+  p.qk_scale_log2 = (float)qk;
+  p.v_global = layer->v_global;
+  return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* layer, const int32_t* block_table,
+                                                        int32_t block_table_stride, int32_t num_seqs,
+                                                        const int32_t* prefix_lens, const int32_t* ws_offsets,
+                                                        int32_t max_prefix_len, float k_ws_scale, float v_ws_scale,
+                                                        uint8_t* ws_k, uint8_t* ws_v, int32_t ws_capacity_tokens,
+                                                        void* stream) {
+  const nvfp4_status_t st = check_layer(layer);
+  if (st != NVFP4_OK) return st;
+  if (num_seqs < 0 || max_prefix_len < 0 || ws_capacity_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(k_ws_scale) || !scale_ok(v_ws_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0 || max_prefix_len == 0) return NVFP4_OK;
+  if (!block_table || !prefix_lens || !ws_offsets || !ws_k || !ws_v) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (block_table_stride < 0 || (int64_t)block_table_stride * kPageSize < (int64_t)max_prefix_len)
+    return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(ws_k, 16) || !aligned(ws_v, 16)) return NVFP4_ERR_UNSUPPORTED;
+  DequantWsParams p;
+  p.codes[0] = layer->k_codes;
+  p.codes[1] = layer->v_codes;
+  p.scales[0] = layer->k_scales;
+  p.scales[1] = layer->v_scales;
+  p.ws[0] = ws_k;
+  p.ws[1] = ws_v;
+  p.g[0] = layer->k_global;
+  p.g[1] = layer->v_global;
+  p.ws_scale[0] = k_ws_scale;
+  p.ws_scale[1] = v_ws_scale;
+  p.block_table = block_table;
+  p.prefix_lens = prefix_lens;
+  p.ws_offsets = ws_offsets;
+  p.bt_stride = block_table_stride;
+  p.num_seqs = num_seqs;
+  p.max_prefix_len = max_prefix_len;
+  p.ws_capacity = ws_capacity_tokens;
+  p.H = layer->num_kv_heads;
+  p.num_pages = layer->num_pages;
+  return from_hip(launch_dequant_ws(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the host shim and the gfx950 kernels of the
+// NVFP4 paged KV-cache library (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_kv.h"
+
+namespace nvfp4kv {
+
+// Cache geometry (fixed by the public header).
+constexpr int kHeadDim = 128;
+constexpr int kPageSize = 16;
+constexpr int kTileCodeBytes = 1024;  // 16 tokens x 64 code bytes, per (page, kv head)
+constexpr int kTileScaleBytes = 128;  // 16 tokens x 8 E4M3 scale bytes
+constexpr int kMaxGroup = 16;         // query heads per kv head handled by one MFMA tile
+
+// One tensor (K or V) of a quantize-append call.
+struct AppendTensor {
+  const void* x;         // [num_tokens][H][128], token stride `token_stride` elements
+  uint8_t* codes;        // code plane
+  uint8_t* scales;       // scale plane
+  float g;               // FP32 global scale
+};
+
+struct AppendParams {
+  AppendTensor t[2];     // [0] = K (token-major tile layout), [1] = V (decode-friendly tile layout)
+  const int32_t* slots;  // [num_tokens]
+  int64_t token_stride;
+  int32_t num_tokens;
+  int32_t H;
+  int32_t num_pages;
+};
+
+hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream);
+
+struct DecodeParams {
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const void* q;           // [B][Hq][128]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* part_o;           // [B][H][S][G][128] unnormalised split outputs
+  float* part_ml;          // [B][H][S][G][2]   (running max in log2 units, sum of weights)
+  float* out;              // [B][Hq][128]
+  int32_t num_pages;
+  int32_t H;
+  int32_t G;
+  int32_t Hq;
+  int32_t batch;
+  int32_t bt_stride;
+  int32_t max_seq_len;
+  int32_t pages_per_split;
+  int32_t num_splits;
+  float qk_scale_log2;     // sm_scale * k_global * log2(e)
+  float v_global;
+};
+
+// Split-K geometry for a decode call (shared by the workspace query and the launch).
+struct DecodeGeometry {
+  int32_t pages_per_split;
+  int32_t num_splits;
+  size_t workspace_bytes;
+};
+DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len);
+
+hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
+
+struct DequantWsParams {
+  const uint8_t* codes[2];
+  const uint8_t* scales[2];
+  uint8_t* ws[2];
+  float g[2];
+  float ws_scale[2];
+  const int32_t* block_table;
+  const int32_t* prefix_lens;
+  const int32_t* ws_offsets;
+  int32_t bt_stride;
+  int32_t num_seqs;
+  int32_t max_prefix_len;
+  int32_t ws_capacity;
+  int32_t H;
+  int32_t num_pages;
+};
+
+hipError_t launch_dequant_ws(const DequantWsParams& p, hipStream_t stream);
+
+}  // namespace nvfp4kv

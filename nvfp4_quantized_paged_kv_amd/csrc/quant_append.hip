@@ -1,0 +1,141 @@
+// NVFP4 quantize-on-append for gfx950.
+//
+// grer.cn blog "NVFP4 KV cache and the memory wall", section 2 (two-level
+// scaling: 16 consecutive values share an E4M3 scale, the tensor shares an FP32
+// scale, each block's amax maps to the E2M1 maximum 6) and section 3 (new K/V
+// are quantized to NVFP4 when written to the cache); nmedialink.com "NVIDIA
+// NVFP4: LLM memory doubled, inference 3x", Fig. 3 (quantize before append).
+//
+// One thread owns one 16-value block of one (token, kv head): it reads the 16
+// inputs (32 B bf16 / 64 B f32), so the block's amax needs no cross-lane work,
+// and writes 8 code bytes plus 1 scale byte.  Consecutive threads own
+// consecutive blocks, so both the loads and the stores of a wave are
+// contiguous.
+//
+// Exact rounding.  bs = E4M3 nearest to amax/(6g): the float64 quotient of the
+// float32 amax and the exact float64 6g is correctly rounded, and no float64
+// rounding can cross or land on an E4M3 midpoint (a midpoint times 6g has at
+// most 31 significant bits, amax 24), so rounding that quotient is exact.
+// Codes: the E2M1 magnitude of x is the number of midpoints T_k = mid_k*bs*g
+// (mid = 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) that |x| passes, where passing
+// an exact tie counts only when it rounds to the even code (k odd).  Each T_k
+// is turned into a float32 threshold u_k with "|x| passes T_k <=> |x| > u_k"
+// exactly: a_k = mid_k*bs is exact in float32 (7 significant bits),
+// hi = RN(a_k*g) and lo = fma(a_k, g, -hi) is the exact residual, so
+//   k even: u_k = lo < 0  ? pred(hi) : hi      (|x| > T_k)
+//   k odd : u_k = lo <= 0 ? pred(hi) : hi      (|x| >= T_k)
+// (global scales are restricted to [2^-100, 2^100], which keeps a_k*g in the
+// float32 normal range).  The magnitude then follows from three comparisons
+// (binary search over the 7 thresholds).
+#include "nvfp4_device.h"
+#include "nvfp4_kv_internal.h"
+
+namespace nvfp4kv {
+namespace {
+
+__device__ __forceinline__ float threshold_f32(float a, float g, bool odd) {
+  const float hi = a * g;                      // rounded product (no contraction in this file)
+  const float lo = __builtin_fmaf(a, g, -hi);  // exact residual a*g - hi
+  const float pred = __int_as_float(__float_as_int(hi) - 1);
+  const bool down = odd ? (lo <= 0.0f) : (lo < 0.0f);
+  return down ? pred : hi;
+}
+
+template <typename InT>
+__device__ __forceinline__ void load_block(const InT* src, float (&x)[16]);
+
+template <>
+__device__ __forceinline__ void load_block<uint16_t>(const uint16_t* src, float (&x)[16]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_block<float>(const float* src, float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+}
+
+template <typename InT>
+__global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p) {
+  const int which = blockIdx.y;  // 0 = K, 1 = V
+  const AppendTensor& T = p.t[which];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n_blocks = (int64_t)p.num_tokens * p.H * 8;
+  if (i >= n_blocks) return;
+  const int b = (int)(i & 7);
+  const int64_t row = i >> 3;
+  const int h = (int)(row % p.H);
+  const int64_t t = row / p.H;
+  const int32_t slot = p.slots[t];
+  if (slot < 0 || (int64_t)slot >= (int64_t)p.num_pages * kPageSize) return;
+
+  float x[16];
+  load_block<InT>(reinterpret_cast<const InT*>(T.x) + t * p.token_stride + (int64_t)h * kHeadDim + 16 * b, x);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+
+  const float g = T.g;
+  const uint32_t sb = e4m3_encode_rne_sat((double)amax / (6.0 * (double)g));
+  const float bs = e4m3_value(sb);
+
+  float u[7];
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+  for (int k = 0; k < 7; ++k) u[k] = bs == 0.0f ? __builtin_inff() : threshold_f32(mids[k] * bs, g, (k & 1) != 0);
+
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float ax = fabsf(x[k]);
+    const bool c2 = ax > u[3];
+    const bool c1 = ax > (c2 ? u[5] : u[1]);
+    const float t0 = c2 ? (c1 ? u[6] : u[4]) : (c1 ? u[2] : u[0]);
+    const bool c0 = ax > t0;
+    const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
+    const uint32_t code = mag | ((__float_as_uint(x[k]) >> 28) & 8u);
+    packed[k >> 3] |= code << (4 * (k & 7));
+  }
+
+  const int64_t page = slot / kPageSize;
+  const int o = slot % kPageSize;
+  const int64_t tile = page * p.H + h;
+  if (which == 0) {
+    *reinterpret_cast<uint2*>(T.codes + tile * kTileCodeBytes + o * 64 + 8 * b) = make_uint2(packed[0], packed[1]);
+    T.scales[tile * kTileScaleBytes + o * 8 + b] = (uint8_t)sb;
+  } else {
+    uint8_t* base = T.codes + tile * kTileCodeBytes + (o >> 2) * 256 + (o & 3) * 4;
+    *reinterpret_cast<uint32_t*>(base + (2 * b) * 16) = packed[0];
+    *reinterpret_cast<uint32_t*>(base + (2 * b + 1) * 16) = packed[1];
+    T.scales[tile * kTileScaleBytes + b * 16 + o] = (uint8_t)sb;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream) {
+  const int64_t n_blocks = (int64_t)p.num_tokens * p.H * 8;
+  if (n_blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_blocks + 255) / 256), 2, 1);
+  if (dtype == NVFP4_DTYPE_BF16)
+    hipLaunchKernelGGL(quantize_append_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(quantize_append_kernel<float>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

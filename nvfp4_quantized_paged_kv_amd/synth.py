@@ -1,0 +1,124 @@
+"""Seeded synthetic workloads for tests and the bench (no NVFP4 arithmetic here).
+
+The shapes and value distributions stand in for the pages' workloads: 80-layer
+/ 8-KV-head / head_dim-128 GQA models, 32K-1M-token contexts and
+multi-million-token agentic sessions (grer.cn blog "NVFP4 KV cache and the
+memory wall", sections 1 and 4).  K/V values are mostly small Gaussians with
+rare large outliers, as in the blog's section-2 experiment (gauss(0, 0.02)
+with a few values of 6.0).  Nothing here reads a dataset; every tensor comes
+from a seeded torch generator, so the oracle and the GPU path can be given the
+same inputs.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+BASE_SEED = 20261106  # the seed of the blog's section-2 experiment
+HEAD_DIM = 128
+PAGE = 16
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    ctx: int                  # context length per sequence (max for ragged)
+    layers: int               # layers the bench rotates over
+    in_dtype: torch.dtype     # K/V/Q input dtype
+    dist: str                 # "sparse6" (random +-6.0 entries) or "chan50" (2 K channels x50)
+    outlier_frac: float = 0.0
+    global_one: bool = False  # g = 1.0 instead of amax / (6*448)
+    lens: tuple = field(default=())  # ragged lengths (mixed step); empty = all `ctx`
+
+    @property
+    def group(self) -> int:
+        return self.q_heads // self.kv_heads
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 4, 1, 256, 1, torch.float32, "sparse6", 0.005, True),
+    "gqa70b_b32_8k": Workload("gqa70b_b32_8k", 32, 64, 8, 8192, 4, torch.bfloat16, "chan50"),
+    "long_b8_128k": Workload("long_b8_128k", 8, 64, 8, 131072, 4, torch.bfloat16, "chan50"),
+    "agentic_b1_2m": Workload("agentic_b1_2m", 1, 96, 8, 2_000_000, 8, torch.bfloat16, "sparse6", 0.002),
+}
+
+
+def mixed_lengths(n: int = 64, lo: int = 512, hi: int = 65536, seed: int = BASE_SEED + 5) -> list[int]:
+    """Log-uniform ragged lengths for the mixed serving step."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in np.exp(rng.uniform(math.log(lo), math.log(hi), n)).astype(np.int64)]
+
+
+def seed_of(*parts: int) -> int:
+    """Deterministic 63-bit seed from integer parts (the blog's seed first)."""
+    h = BASE_SEED
+    for p in parts:
+        h = (h * 1_000_003 + int(p) + 0x9E3779B9) % (1 << 63)
+    return h
+
+
+def generator(device, *parts: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(*parts))
+    return g
+
+
+def kv_values(n_tokens: int, H: int, dist: str, outlier_frac: float, which: int, dtype: torch.dtype, device,
+              *seed_parts: int) -> torch.Tensor:
+    """K (which=0) or V (which=1) values [n_tokens, H, 128] in `dtype` (generated in f32, RNE-rounded)."""
+    g = generator(device, *seed_parts, which)
+    x = torch.randn((n_tokens, H, HEAD_DIM), generator=g, device=device, dtype=torch.float32) * 0.02
+    if dist == "sparse6" and outlier_frac > 0:
+        u = torch.rand((n_tokens, H, HEAD_DIM), generator=g, device=device)
+        sign = torch.where(torch.rand((n_tokens, H, HEAD_DIM), generator=g, device=device) < 0.5, -6.0, 6.0)
+        x = torch.where(u < outlier_frac, sign, x)
+    elif dist == "chan50" and which == 0:
+        ch = channel_outliers(seed_parts[0] if seed_parts else 0)
+        x[:, :, ch] *= 50.0
+    return x.to(dtype)
+
+
+def channel_outliers(cfg_id: int) -> list[int]:
+    """The 2 (of 128) K channels scaled by 50, the same for every head and token."""
+    rng = np.random.default_rng(seed_of(cfg_id, 777))
+    return sorted(int(c) for c in rng.choice(HEAD_DIM, 2, replace=False))
+
+
+def queries(B: int, Hq: int, dtype: torch.dtype, device, *seed_parts: int) -> torch.Tensor:
+    g = generator(device, *seed_parts, 99)
+    q = torch.randn((B, Hq, HEAD_DIM), generator=g, device=device, dtype=torch.float32) / math.sqrt(HEAD_DIM)
+    return q.to(dtype)
+
+
+def global_scale(amax: float) -> float:
+    """Calibrated FP32 global scale amax / (6 * 448) (E2M1 max times E4M3 max)."""
+    return float(np.float32(amax) / np.float32(6 * 448))
+
+
+def page_tables(lens, num_pages: int | None = None, seed: int = 0):
+    """Block table [B, max_pages] int32 drawn from a seeded random permutation of the page pool."""
+    pages_per = [(int(n) + PAGE - 1) // PAGE for n in lens]
+    total = sum(pages_per)
+    pool = total if num_pages is None else int(num_pages)
+    assert pool >= total
+    rng = np.random.default_rng(seed_of(seed, 4242))
+    perm = rng.permutation(pool).astype(np.int32)
+    width = max(max(pages_per), 1)
+    bt = np.zeros((len(lens), width), np.int32)
+    at = 0
+    for b, n in enumerate(pages_per):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    return bt, pool
+
+
+def slots_for(bt_row: np.ndarray, start: int, n: int) -> np.ndarray:
+    """Slots of tokens start..start+n-1 of one sequence."""
+    t = np.arange(start, start + n, dtype=np.int64)
+    return (bt_row[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)

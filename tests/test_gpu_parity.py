@@ -1,0 +1,215 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU
+oracle on the same seeded inputs.  Codes and scale bytes must match bit for
+bit; decode attention must agree to 1e-3 row-normalised max relative error."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from nvfp4_quantized_paged_kv_amd import synth
+from tests.gpu_cases import ATTN_TOL, build_cache, decode_both, host_f32, planes_equal, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_quantized_paged_kv_amd as nk  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+# ------------------------------------------------------------ quantize-append
+
+
+def test_append_tiny_fp32_bitexact():
+    _say("case: append tiny fp32 H=1 T=256 g=1")
+    c = build_cache([256], 1, torch.float32, "sparse6", 0.005, True, seed=1)
+    assert planes_equal(c.layer, c.planes) == []
+
+
+@pytest.mark.parametrize("H,dist,frac", [(8, "chan50", 0.0), (8, "sparse6", 0.002), (3, "sparse6", 0.05)])
+def test_append_bf16_ragged_bitexact(H, dist, frac):
+    _say(f"case: append bf16 ragged H={H} {dist}")
+    c = build_cache([1, 15, 16, 17, 100, 333], H, torch.bfloat16, dist, frac, False, seed=2 + H)
+    assert planes_equal(c.layer, c.planes) == []
+
+
+def test_append_strided_and_skipped_slots():
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: append strided input, negative and out-of-range slots")
+    H, T = 4, 50
+    big_k = synth.kv_values(T, H + 2, "sparse6", 0.01, 0, torch.bfloat16, "cpu", 77, 0)
+    big_v = synth.kv_values(T, H + 2, "sparse6", 0.01, 1, torch.bfloat16, "cpu", 77, 0)
+    k, v = big_k[:, :H, :], big_v[:, :H, :]
+    k_dev, v_dev = big_k.cuda()[:, :H, :], big_v.cuda()[:, :H, :]  # token stride (H+2)*128 elements
+    assert k_dev.stride(0) == (H + 2) * 128
+    pool = 8
+    rng = np.random.default_rng(3)
+    slots = rng.permutation(pool * 16)[:T].astype(np.int32)
+    slots[::7] = -1
+    slots[3] = pool * 16 + 5  # beyond the pool: must be skipped
+    planes = oracle.Planes(pool, H)
+    ok = slots.copy()
+    ok[ok >= pool * 16] = -1
+    oracle.quantize_append(planes, host_f32(k), host_f32(v), ok, 0.01, 0.02)
+    layer = nk.KVCacheLayer.allocate(pool, H, 0.01, 0.02)
+    nk.quantize_append(layer, k_dev, v_dev, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert planes_equal(layer, planes) == []
+
+
+def _tie_rows():
+    """Rows whose values sit exactly on E2M1 midpoints / whose amax sits on E4M3 midpoints."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows = []
+    r = np.zeros(128, np.float32)
+    for b in range(8):
+        r[16 * b:16 * b + 16] = ([6.0] + mids + [-m for m in mids] + [-0.0])[:16]
+    rows.append((r, 1.0))
+    r = np.zeros(128, np.float32)
+    for b in range(8):
+        r[16 * b:16 * b + 16] = ([4.5] + [m * 0.75 for m in mids] + [-m * 0.75 for m in mids] + [0.0])[:16]
+    rows.append((r, 0.5))
+    e4 = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    r = np.zeros(128, np.float32)
+    for b, k in enumerate([0, 1, 7, 8, 30, 63, 100, 124]):
+        amax = np.float32((e4[k] + e4[k + 1]) / 2 * 3)  # g = 0.5 -> amax/(6g) = midpoint exactly
+        r[16 * b] = amax
+        r[16 * b + 1:16 * b + 16] = np.linspace(-amax, amax, 15)
+    rows.append((r, 0.5))
+    r = np.zeros(128, np.float32)
+    r[16:32] = 1e-30
+    r[32:48] = -1e-30
+    r[48:64] = 3e38
+    r[64:80] = np.float32(1.5e-45)  # float32 subnormals
+    rows.append((r, 1.0))
+    return rows
+
+
+def test_append_exact_ties_fp32():
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: append exact ties")
+    for r, g in _tie_rows():
+        k = np.stack([r, -r])[:, None, :]
+        planes = oracle.Planes(1, 1)
+        slots = np.array([0, 5], np.int32)
+        oracle.quantize_append(planes, k, k, slots, g, g)
+        layer = nk.KVCacheLayer.allocate(1, 1, g, g)
+        kt = torch.from_numpy(k).cuda()
+        nk.quantize_append(layer, kt, kt, torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        assert planes_equal(layer, planes) == [], g
+
+
+def test_append_random_scales_fuzz():
+    """Many global scales and magnitudes: every code and scale byte bit-exact."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: append fuzz over scales")
+    rng = np.random.default_rng(11)
+    for it in range(12):
+        g = float(np.float32(np.exp(rng.uniform(-60, 60))))
+        T, H = 64, 2
+        x = (rng.standard_cauchy((T, H, 128)) * g * np.exp(rng.uniform(-8, 8, (T, H, 1)))).astype(np.float32)
+        x = np.clip(x, -3e38, 3e38).astype(np.float32)
+        slots = np.arange(T, dtype=np.int32)
+        planes = oracle.Planes(4, H)
+        oracle.quantize_append(planes, x, -x, slots, g, g)
+        layer = nk.KVCacheLayer.allocate(4, H, g, g)
+        xt = torch.from_numpy(x).cuda()
+        nk.quantize_append(layer, xt, -xt, torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        assert planes_equal(layer, planes) == [], (it, g)
+
+
+# ---------------------------------------------------------- decode attention
+
+
+def test_decode_tiny_workload():
+    """1 layer, batch 1, 4 q heads / 1 kv head, 256 tokens, fp32, g = 1."""
+    _say("case: decode tiny")
+    c = build_cache([256], 1, torch.float32, "sparse6", 0.005, True, seed=1)
+    assert planes_equal(c.layer, c.planes) == []
+    got, ref = decode_both(c, 4, torch.float32, seed=1)
+    err = row_rel_err(got, ref)
+    assert err.max() <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("lens,H,G,qdt", [
+    ([1], 1, 1, torch.bfloat16),
+    ([15, 16, 17], 2, 4, torch.bfloat16),
+    ([0, 33, 64, 65], 2, 8, torch.bfloat16),
+    ([1000, 7, 513], 8, 8, torch.bfloat16),
+    ([300, 2049], 8, 12, torch.bfloat16),
+    ([200], 2, 16, torch.float32),
+    ([4097], 1, 3, torch.float32),
+])
+def test_decode_matches_oracle(lens, H, G, qdt):
+    _say(f"case: decode lens={lens} H={H} G={G} q={qdt}")
+    c = build_cache(lens, H, torch.bfloat16, "chan50" if H == 8 else "sparse6", 0.003, False, seed=sum(lens) + G)
+    got, ref = decode_both(c, H * G, qdt, seed=G)
+    err = row_rel_err(got, ref)
+    assert err.max() <= ATTN_TOL, (err.max(), np.argmax(err))
+
+
+@pytest.mark.parametrize("q_scale", [30.0, 300.0])
+def test_decode_peaked_softmax(q_scale):
+    """Large queries: a peaked softmax (exercises the running-max rescale)."""
+    _say(f"case: decode peaked q_scale={q_scale}")
+    c = build_cache([777, 129], 2, torch.bfloat16, "sparse6", 0.01, False, seed=5)
+    got, ref = decode_both(c, 2 * 8, torch.bfloat16, seed=9, q_scale=q_scale)
+    err = row_rel_err(got, ref)
+    assert err.max() <= ATTN_TOL, err.max()
+
+
+def test_decode_split_count_invariance():
+    """A larger max_seq_len changes the split geometry; both results stay within the parity bound.
+
+    The softmax weights enter the PV product as f16 relative to a running
+    maximum that depends on how tokens are grouped into splits, so two split
+    geometries differ at the f16 rounding level (~1e-4), not bit for bit."""
+    _say("case: decode split invariance")
+    c = build_cache([1500, 900], 2, torch.bfloat16, "sparse6", 0.005, False, seed=21)
+    a, ref = decode_both(c, 16, torch.bfloat16, seed=3)
+    b, _ = decode_both(c, 16, torch.bfloat16, seed=3, max_seq_len=64 * 1024)
+    assert row_rel_err(a, ref).max() <= ATTN_TOL
+    assert row_rel_err(b, ref).max() <= ATTN_TOL
+    assert row_rel_err(a, b).max() <= ATTN_TOL
+
+
+# ------------------------------------------------------- FP8 workspace dequant
+
+
+@pytest.mark.parametrize("g_one", [True, False])
+def test_dequant_ws_bitexact(g_one):
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say(f"case: fp8 workspace g_one={g_one}")
+    lens = [100, 37, 0, 256]
+    H = 4
+    c = build_cache(lens, H, torch.bfloat16, "sparse6", 0.01, g_one, seed=31)
+    prefix = np.array([100, 20, 0, 256], np.int32)
+    offs = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32)
+    total = int(offs[-1])
+    ks = 6 * c.g_k if not g_one else 6.0 / 448
+    vs = 6 * c.g_v if not g_one else 6.0 / 448
+    ref_k = oracle.fp8_workspace(c.planes, False, c.g_k, c.bt, prefix, offs, ks, total)
+    ref_v = oracle.fp8_workspace(c.planes, True, c.g_v, c.bt, prefix, offs, vs, total)
+    ws_k = torch.zeros((total + 5, H, 128), dtype=torch.uint8, device="cuda")
+    ws_v = torch.zeros_like(ws_k)
+    nk.dequant_to_fp8_workspace(c.layer, torch.from_numpy(c.bt).cuda(), torch.from_numpy(prefix).cuda(),
+                                torch.from_numpy(offs).cuda(), int(prefix.max()), ks, vs, ws_k, ws_v)
+    torch.cuda.synchronize()
+    assert np.array_equal(ws_k[:total].cpu().numpy(), ref_k)
+    assert np.array_equal(ws_v[:total].cpu().numpy(), ref_v)
+    assert not ws_k[total:].any() and not ws_v[total:].any()
