@@ -1,0 +1,303 @@
+"""Benchmark of the NVFP4 paged-KV hot path on one MI355X.
+
+Default workload: 70B-class GQA decode, one layer per step -- batch 32, 64 query
+heads / 8 KV heads, head_dim 128, 8192-token contexts, 16-token pages, bf16
+K/V ~ N(0, 0.02) with 2 of 128 K channels scaled x50, FP32 global scales
+amax/(6*448).  Four layer caches are filled (bulk quantize-append, timed) and
+the timed step rotates over them so consecutive steps never re-read a cache
+that could sit in the 256 MB Infinity Cache.  One step = append the batch's new
+token (one per sequence) + decode attention over the 8192-token caches.
+
+Printed: one JSON line.  `value` is decode-step effective HBM bandwidth
+(algorithmic bytes of append + decode per step / step wall time); the same line
+carries the bulk quantize-append GB/s, the FP8 workspace dequant GB/s, the
+roofline of the dominant kernel (decode attention, timed with HIP events on the
+launch stream) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s) + quantize-append GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa70b_b32_8k",
+                    choices=["gqa70b_b32_8k", "long_b8_128k", "agentic_b1_2m", "tiny"])
+    ap.add_argument("--layers", type=int, default=0, help="override the number of rotated layer caches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_file: str, workload: str):
+    """HBM traffic per decode call from a committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source; else None."""
+    prof = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.txt")
+    if not os.path.exists(prof):
+        return None
+    vals = {}
+    with open(prof) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != src_hash(kernel_file):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole sequences (all KV heads, the full context) generated on the host,
+    quantized and attended by the oracle; rate in the metric's unit."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from nvfp4_quantized_paged_kv_amd import synth
+
+    H, ctx = wl.kv_heads, min(wl.ctx, 8192)
+    in_b = 2 if wl.in_dtype == torch.bfloat16 else 4
+    sm = float(np.float32(1 / math.sqrt(128)))
+    done_bytes = 0
+    t_dec = 0.0
+    t_q = 0.0
+    q_bytes = 0
+    seqs = 0
+    while t_dec + t_q < target_s and seqs < wl.batch:
+        k = synth.kv_values(ctx, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, "cpu", 900 + seqs)
+        v = synth.kv_values(ctx, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, "cpu", 900 + seqs)
+        g_k = 1.0 if wl.global_one else synth.global_scale(float(k.float().abs().max()))
+        g_v = 1.0 if wl.global_one else synth.global_scale(float(v.float().abs().max()))
+        kf = k.float().numpy()
+        vf = v.float().numpy()
+        n_pages = (ctx + 15) // 16
+        planes = oracle.Planes(n_pages, H)
+        slots = np.arange(ctx, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.quantize_append(planes, kf, vf, slots, g_k, g_v)
+        t_q += time.perf_counter() - t0
+        q_bytes += ctx * H * (2 * 128 * k.element_size() + 144) + 4 * ctx
+        q = synth.queries(1, wl.q_heads, wl.in_dtype, "cpu", 900 + seqs).float().numpy()
+        bt = np.arange(n_pages, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        oracle.decode_attention(planes, g_k, g_v, q, bt, np.array([ctx], np.int32), sm)
+        t_dec += time.perf_counter() - t0
+        done_bytes += ctx * H * 144 + n_pages * 4 + wl.q_heads * 128 * (in_b + 4)
+        seqs += 1
+    return {
+        "value": round(done_bytes / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{seqs} sequence(s) x {ctx} tokens x {H} kv heads x {wl.q_heads} q heads: "
+                  f"oracle decode {t_dec:.2f} s; oracle quantize {t_q:.2f} s "
+                  f"({q_bytes / t_q / 1e9:.4f} GB/s)",
+        "quantize_gbps": round(q_bytes / t_q / 1e9, 4),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_quantized_paged_kv_amd as nk
+    from nvfp4_quantized_paged_kv_amd import synth
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    L = args.layers or wl.layers
+    B, Hq, H, ctx = wl.batch, wl.q_heads, wl.kv_heads, wl.ctx
+    pages_per_seq = (ctx + 15) // 16
+    num_pages = B * pages_per_seq
+    stream = torch.cuda.current_stream()
+    print(f"[bench] workload {wl.name}: B={B} Hq={Hq} H={H} ctx={ctx} layers={L}", file=sys.stderr, flush=True)
+
+    # ---- build L layer caches (bulk quantize-append, timed with HIP events)
+    layers, tables, newk, newv, slots_new, qs = [], [], [], [], [], []
+    append_ms, append_bytes = [], []
+    chunk = max(1, (1 << 27) // (H * 128))  # tokens per generated chunk (~128M values)
+    for l in range(L):
+        bt_np, pool = synth.page_tables([ctx] * B, num_pages, seed=1000 + l)
+        bt = torch.from_numpy(bt_np).to(dev)
+        # calibration pass: amax of this layer's K and V (generated chunk by chunk)
+        amax = [0.0, 0.0]
+        n_fill = ctx - 1
+        total = B * n_fill
+        for which in (0, 1):
+            for c0 in range(0, total, chunk):
+                n = min(chunk, total - c0)
+                x = synth.kv_values(n, H, wl.dist, wl.outlier_frac, which, wl.in_dtype, dev, 2, l, c0)
+                amax[which] = max(amax[which], float(x.float().abs().max()))
+        g_k = 1.0 if wl.global_one else synth.global_scale(amax[0])
+        g_v = 1.0 if wl.global_one else synth.global_scale(amax[1])
+        layer = nk.KVCacheLayer.allocate(num_pages, H, g_k, g_v, dev)
+        tok = np.arange(n_fill, dtype=np.int64)
+        for c0 in range(0, total, chunk):
+            n = min(chunk, total - c0)
+            k = synth.kv_values(n, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, dev, 2, l, c0)
+            v = synth.kv_values(n, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, dev, 2, l, c0)
+            idx = np.arange(c0, c0 + n, dtype=np.int64)
+            b_of, t_of = idx // n_fill, idx % n_fill
+            sl = (bt_np[b_of, t_of // 16].astype(np.int64) * 16 + t_of % 16).astype(np.int32)
+            sl_d = torch.from_numpy(sl).to(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            nk.quantize_append(layer, k, v, sl_d)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            append_ms.append(e0.elapsed_time(e1))
+            append_bytes.append(n * H * (2 * 128 * k.element_size() + 144) + 4 * n)
+            del k, v
+        del tok
+        layers.append(layer)
+        tables.append(bt)
+        newk.append(synth.kv_values(B, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, dev, 3, l))
+        newv.append(synth.kv_values(B, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, dev, 3, l))
+        slots_new.append(torch.from_numpy(
+            (bt_np[:, (ctx - 1) // 16].astype(np.int64) * 16 + (ctx - 1) % 16).astype(np.int32)).to(dev))
+        qs.append(synth.queries(B, Hq, wl.in_dtype, dev, 4, l))
+        print(f"[bench] layer {l} filled (g_k={g_k:.3e} g_v={g_v:.3e})", file=sys.stderr, flush=True)
+
+    seq_lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    sm = 1 / math.sqrt(128)
+    ws_bytes = nk.decode_workspace_bytes(B, Hq, H, ctx)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    in_b = newk[0].element_size()
+    bytes_append_step = B * H * (2 * 128 * in_b + 144) + 4 * B
+    bytes_decode = B * ctx * H * 144 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
+    bytes_step = bytes_append_step + bytes_decode
+
+    def step(l, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nk.quantize_append(layers[l], newk[l], newv[l], slots_new[l])
+        if ev is not None:
+            ev[1].record(stream)
+        nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i % L)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, wall clock
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % L)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- same steps again with HIP events on the launch stream (per-call durations)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i % L, evs[i])
+    torch.cuda.synchronize()
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    dec_avg_s = float(dec_ms.mean()) / 1e3
+    achieved = bytes_decode / dec_avg_s / 1e9
+
+    # ---- FP8 workspace dequant on the same cache: 8 sequences' full prefixes (extend path)
+    n_ext = min(8, B)
+    prefix = torch.full((n_ext,), ctx, dtype=torch.int32, device=dev)
+    offs = torch.arange(0, (n_ext + 1) * ctx, ctx, dtype=torch.int32, device=dev)
+    ws_k = torch.empty((n_ext * ctx, H, 128), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty_like(ws_k)
+    ws_ms = []
+    for i in range(max(5, min(args.steps, 20))):
+        l = i % L
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nk.dequant_to_fp8_workspace(layers[l], tables[l][:n_ext].contiguous(), prefix, offs, ctx,
+                                    6 * layers[l].k_global, 6 * layers[l].v_global, ws_k, ws_v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ws_ms.append(e0.elapsed_time(e1))
+    ws_bytes_alg = n_ext * ctx * H * (144 + 256) + n_ext * pages_per_seq * 4
+    ws_gbs = ws_bytes_alg / (float(np.median(ws_ms)) / 1e3) / 1e9
+
+    app_total_b = float(sum(append_bytes))
+    app_total_s = float(sum(append_ms)) / 1e3
+    kernel_file = os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", "decode_attn.hip")
+    traffic = read_traffic(kernel_file, wl.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(bytes_step / (wall / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 cache; bf16 in; f16 MFMA, fp32 accumulate" if wl.in_dtype == torch.bfloat16
+                 else "nvfp4 cache; f32 in; f16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded torch generators)",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
+                   "context": ctx, "page_size": 16, "layers_rotated": L,
+                   "step": "append 1 token/seq + decode attention, one layer"},
+        "pct_of_peak": round(100 * bytes_step / (wall / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
+        "decode_attn_gbs_events": round(achieved, 2),
+        "decode_attn_us": round(dec_avg_s * 1e6, 3),
+        "append_step_us": round(float(app_ms.mean()) * 1e3, 3),
+        "quantize_append_bulk_gbs": round(app_total_b / app_total_s / 1e9, 2),
+        "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),
+        "fp8_workspace_gbs": round(ws_gbs, 2),
+        "fp8_workspace_tokens": int(n_ext * ctx),
+        "bytes_per_step": int(bytes_step),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "nvfp4_paged_decode_attn (decode_split_kernel + decode_combine_kernel)",
+                     "algorithmic_bytes_per_call": int(bytes_decode)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,6 +29,9 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the
+    # (rarely taken) softmax rescale in the decode loop
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -107,7 +107,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   p.seq_lens = seq_lens;
   const int64_t G = num_q_heads / layer->num_kv_heads;
   const int64_t units = (int64_t)batch * layer->num_kv_heads * geo.num_splits * G;
-  p.part_o = static_cast<float*>(workspace);
+  p.part_o = geo.workspace_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
   p.part_ml = geo.workspace_bytes > 0 ? static_cast<float*>(workspace) + units * kHeadDim : nullptr;
   p.out = out;
   p.num_pages = layer->num_pages;
@@ -121,7 +121,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   p.num_splits = geo.num_splits;
   p.qk_scale_log2 = (float)qk;
   p.v_global = layer->v_global;
-  return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_decode(p, q_dtype, geo.needs_combine, static_cast<hipStream_t>(stream)));
 }
 
 NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* layer, const int32_t* block_table,

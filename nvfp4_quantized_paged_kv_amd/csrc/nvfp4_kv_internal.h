@@ -43,7 +43,7 @@ struct DecodeParams {
   const void* q;           // [B][Hq][128]
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* part_o;           // [B][H][S][G][128] unnormalised split outputs
+  float* part_o;           // [B][H][S][G][128] unnormalised split outputs (S > 1 only)
   float* part_ml;          // [B][H][S][G][2]   (running max in log2 units, sum of weights)
   float* out;              // [B][Hq][128]
   int32_t num_pages;
@@ -63,11 +63,12 @@ struct DecodeParams {
 struct DecodeGeometry {
   int32_t pages_per_split;
   int32_t num_splits;
-  size_t workspace_bytes;
+  size_t workspace_bytes;  // split partials; 0 when no sequence can need more than one split
+  bool needs_combine;      // some sequence may span more than one split
 };
 DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len);
 
-hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, bool needs_combine, hipStream_t stream);
 
 struct DequantWsParams {
   const uint8_t* codes[2];
