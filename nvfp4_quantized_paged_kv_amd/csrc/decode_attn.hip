@@ -39,14 +39,18 @@ namespace nvfp4kv {
 namespace {
 
 #ifndef NVFP4_DECODE_WAVES
-#define NVFP4_DECODE_WAVES 8
+#define NVFP4_DECODE_WAVES 16
 #endif
 #ifndef NVFP4_DECODE_TARGET_GROUPS
-#define NVFP4_DECODE_TARGET_GROUPS 512
+#define NVFP4_DECODE_TARGET_GROUPS 256
 #endif
-constexpr int kWaves = NVFP4_DECODE_WAVES;              // waves per workgroup
+// One 16-wave workgroup fills a CU (4 waves per SIMD at <= 128 VGPRs), and
+// about one workgroup per CU covers the call, so a batch with at least as many
+// (sequence, kv head) units as CUs runs without splitting a sequence.
+constexpr int kWaves = NVFP4_DECODE_WAVES;                     // waves per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int64_t kTargetGroups = NVFP4_DECODE_TARGET_GROUPS;  // workgroups per call (2 per CU at 8 waves)
+constexpr int64_t kTargetGroups = NVFP4_DECODE_TARGET_GROUPS;  // workgroups per call
+constexpr int kMaxPagesPerWave = 128;                          // page indices a wave keeps in 2 lane registers
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max must move
 
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
@@ -190,11 +194,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- this wave's pages: pg_j = p_begin + wave + kWaves*j, j < n_mine <= 64
-  // (the host keeps pages_per_split <= 64*kWaves); their indices sit one per lane.
+  // ---- this wave's pages: pg_j = p_begin + wave + kWaves*j, j < n_mine <= 128
+  // (the host keeps pages_per_split <= 128*kWaves); their indices sit in two
+  // lane registers (pages j and j + 64 in lane j).
   const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
   const int n_mine = p_end - p_begin > wave ? (p_end - p_begin - wave + kWaves - 1) / kWaves : 0;
-  const int pidx = lane < n_mine ? bt_row[p_begin + wave + kWaves * lane] : 0;
+  const int pidx0 = lane < n_mine ? bt_row[p_begin + wave + kWaves * lane] : 0;
+  const int pidx1 = lane + 64 < n_mine ? bt_row[p_begin + wave + kWaves * (lane + 64)] : 0;
   auto process = [&](const PageRegs& cur) {
     const int valid = cur.valid;
 
@@ -215,14 +221,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[c], S, 0, 0, 0);
     }
 
-    // ---- online softmax (log2 domain)
+    // ---- online softmax (log2 domain).  Raw v_exp_f32: weights below 2^-126
+    // of the running max flush to 0, which the f16 weights could not hold anyway.
     float t[4];
+    if (valid == kPageSize) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = (4 * q4 + i < valid) ? S[i] * tscale : -__builtin_inff();
+      for (int i = 0; i < 4; ++i) t[i] = S[i] * tscale;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = (4 * q4 + i < valid) ? S[i] * tscale : -__builtin_inff();
+    }
     const float pm = max_over_groups(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
     if (__any(pm > m_run + kLazyMax)) {
       const float m_new = fmaxf(m_run, pm);
-      const float f = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - m_new);
+      const float f = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= f;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -232,15 +244,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       }
       m_run = m_new;
     }
+    // m_run is -inf only while every token seen so far was masked (t = -inf too)
+    const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = t[i] == -__builtin_inff() ? 0.0f : exp2f(t[i] - m_run);
+    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - m_use);
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const half4_t pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 
     // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3)
     uint32_t vsw = cur.vsw;
-    {
+    if (valid != kPageSize) {
       const int nv = min(max(valid - 4 * q4, 0), 4);
       vsw &= nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);  // zero the scales of tokens past the end
     }
@@ -268,7 +282,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const LaneOffsets lo{r * 64 + q4 * 16, r * 8 + q4 * 2, lane * 16, (r >> 1) * 16 + q4 * 4};
   auto load_mine = [&](int j) {
     const int jc = min(j, n_mine - 1);
-    return load_page(p, __builtin_amdgcn_readlane(pidx, jc), p_begin + wave + kWaves * jc, seq_len, h, lo);
+    const int page = jc < 64 ? __builtin_amdgcn_readlane(pidx0, jc) : __builtin_amdgcn_readlane(pidx1, jc - 64);
+    return load_page(p, page, p_begin + wave + kWaves * jc, seq_len, h, lo);
   };
   // Two register sets, unrolled by two: each set is loaded one page ahead of
   // its use and refilled right after, so no register copy waits on a load in
@@ -376,7 +391,7 @@ DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_k
   int64_t pps = ((int64_t)batch * num_kv_heads * max_pages + kTargetGroups - 1) / kTargetGroups;
   pps = (pps + kWaves - 1) / kWaves * kWaves;
   if (pps < kWaves) pps = kWaves;
-  if (pps > 64 * kWaves) pps = 64 * kWaves;  // a wave keeps the page indices of its pages in its 64 lanes
+  if (pps > kMaxPagesPerWave * kWaves) pps = kMaxPagesPerWave * kWaves;  // page indices held in lanes
   const int64_t max_pps = (max_pages + kWaves - 1) / kWaves * kWaves;
   if (pps > max_pps) pps = max_pps;
   geo.pages_per_split = (int32_t)pps;
