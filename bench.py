@@ -142,55 +142,28 @@ def main():
     L = args.layers or wl.layers
     B, Hq, H, ctx = wl.batch, wl.q_heads, wl.kv_heads, wl.ctx
     pages_per_seq = (ctx + 15) // 16
-    num_pages = B * pages_per_seq
     stream = torch.cuda.current_stream()
     print(f"[bench] workload {wl.name}: B={B} Hq={Hq} H={H} ctx={ctx} layers={L}", file=sys.stderr, flush=True)
 
-    # ---- build L layer caches (bulk quantize-append, timed with HIP events)
+    # ---- build L layer caches (bulk quantize-append of ctx-1 tokens per sequence, timed)
+    from nvfp4_quantized_paged_kv_amd.workloads import build_layer
+
     layers, tables, newk, newv, slots_new, qs = [], [], [], [], [], []
     append_ms, append_bytes = [], []
-    chunk = max(1, (1 << 27) // (H * 128))  # tokens per generated chunk (~128M values)
     for l in range(L):
-        bt_np, pool = synth.page_tables([ctx] * B, num_pages, seed=1000 + l)
-        bt = torch.from_numpy(bt_np).to(dev)
-        # calibration pass: amax of this layer's K and V (generated chunk by chunk)
-        amax = [0.0, 0.0]
-        n_fill = ctx - 1
-        total = B * n_fill
-        for which in (0, 1):
-            for c0 in range(0, total, chunk):
-                n = min(chunk, total - c0)
-                x = synth.kv_values(n, H, wl.dist, wl.outlier_frac, which, wl.in_dtype, dev, 2, l, c0)
-                amax[which] = max(amax[which], float(x.float().abs().max()))
-        g_k = 1.0 if wl.global_one else synth.global_scale(amax[0])
-        g_v = 1.0 if wl.global_one else synth.global_scale(amax[1])
-        layer = nk.KVCacheLayer.allocate(num_pages, H, g_k, g_v, dev)
-        tok = np.arange(n_fill, dtype=np.int64)
-        for c0 in range(0, total, chunk):
-            n = min(chunk, total - c0)
-            k = synth.kv_values(n, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, dev, 2, l, c0)
-            v = synth.kv_values(n, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, dev, 2, l, c0)
-            idx = np.arange(c0, c0 + n, dtype=np.int64)
-            b_of, t_of = idx // n_fill, idx % n_fill
-            sl = (bt_np[b_of, t_of // 16].astype(np.int64) * 16 + t_of % 16).astype(np.int32)
-            sl_d = torch.from_numpy(sl).to(dev)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            nk.quantize_append(layer, k, v, sl_d)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            append_ms.append(e0.elapsed_time(e1))
-            append_bytes.append(n * H * (2 * 128 * k.element_size() + 144) + 4 * n)
-            del k, v
-        del tok
-        layers.append(layer)
-        tables.append(bt)
+        fl = build_layer(wl, [ctx - 1] * B, [ctx] * B, l, dev, timed=True)
+        append_ms += fl.append_ms
+        append_bytes += fl.append_bytes
+        layers.append(fl.layer)
+        tables.append(fl.block_table_dev)
+        bt_np = fl.block_table
         newk.append(synth.kv_values(B, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, dev, 3, l))
         newv.append(synth.kv_values(B, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, dev, 3, l))
         slots_new.append(torch.from_numpy(
             (bt_np[:, (ctx - 1) // 16].astype(np.int64) * 16 + (ctx - 1) % 16).astype(np.int32)).to(dev))
         qs.append(synth.queries(B, Hq, wl.in_dtype, dev, 4, l))
-        print(f"[bench] layer {l} filled (g_k={g_k:.3e} g_v={g_v:.3e})", file=sys.stderr, flush=True)
+        print(f"[bench] layer {l} filled (g_k={fl.layer.k_global:.3e} g_v={fl.layer.v_global:.3e})",
+              file=sys.stderr, flush=True)
 
     seq_lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
     sm = 1 / math.sqrt(128)

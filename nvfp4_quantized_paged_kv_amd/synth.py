@@ -49,6 +49,44 @@ WORKLOADS = {
 }
 
 
+def chunk_tokens(H: int) -> int:
+    """Tokens per generated chunk (about 2^27 values, 256 MiB of bf16)."""
+    return max(1, (1 << 27) // (H * HEAD_DIM))
+
+
+def layer_token_chunks(wl: Workload, lens, layer: int, device):
+    """Yield (first_index, n, k, v) over the tokens of one layer's fill, in
+    (sequence, position) order: index i is token i % n_fill... of the flattened
+    list of every sequence's tokens.  k, v: [n, H, 128] in wl.in_dtype."""
+    total = int(sum(lens))
+    step = chunk_tokens(wl.kv_heads)
+    for c0 in range(0, total, step):
+        n = min(step, total - c0)
+        k = kv_values(n, wl.kv_heads, wl.dist, wl.outlier_frac, 0, wl.in_dtype, device, 2, layer, c0)
+        v = kv_values(n, wl.kv_heads, wl.dist, wl.outlier_frac, 1, wl.in_dtype, device, 2, layer, c0)
+        yield c0, n, k, v
+
+
+def token_positions(lens):
+    """(sequence index, position) of every token of the flattened fill order."""
+    lens = np.asarray(lens, np.int64)
+    seq = np.repeat(np.arange(lens.size), lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    pos = np.arange(int(lens.sum()), dtype=np.int64) - np.repeat(starts, lens)
+    return seq, pos
+
+
+def layer_global_scales(wl: Workload, lens, layer: int, device):
+    """Calibrated (g_k, g_v) = amax/(6*448) over the layer's K and V (1.0 if wl.global_one)."""
+    if wl.global_one:
+        return 1.0, 1.0
+    amax = [0.0, 0.0]
+    for _, _, k, v in layer_token_chunks(wl, lens, layer, device):
+        amax[0] = max(amax[0], float(k.float().abs().max()))
+        amax[1] = max(amax[1], float(v.float().abs().max()))
+    return global_scale(amax[0]), global_scale(amax[1])
+
+
 def mixed_lengths(n: int = 64, lo: int = 512, hi: int = 65536, seed: int = BASE_SEED + 5) -> list[int]:
     """Log-uniform ragged lengths for the mixed serving step."""
     rng = np.random.default_rng(seed)

@@ -215,6 +215,7 @@ static double plane_value(const uint8_t* code_plane, const uint8_t* scale_plane,
  * layout tests. */
 void nvfp4o_gather_rows(const uint8_t* code_plane, const uint8_t* scale_plane, int64_t n_tokens, int H,
                         const int32_t* slot_mapping, int is_v, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < n_tokens; ++t) {
     int64_t s = slot_mapping[t];
     int64_t p = s / 16;

@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+public header declares, and every argument check returns its status before
+any HIP call (so these run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_kv.h")
+
+
+def _lib():
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    return nk
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]+?\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    fns = _declared_functions()
+    for f in ("nvfp4_kv_quantize_append", "nvfp4_paged_decode_attn", "nvfp4_dequant_to_fp8_workspace"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    nk = _lib()
+    raw = ctypes.CDLL(nk.LIB_PATH)
+    for f in _declared_functions():
+        assert hasattr(raw, f), f
+    assert set(_declared_functions()) == set(nk.EXPORTED_SYMBOLS)
+
+
+def test_status_strings():
+    nk = _lib()
+    for s in range(5):
+        assert nk.status_string(s) and nk.status_string(s) != "unknown status"
+    assert nk.status_string(99) == "unknown status"
+
+
+# A fake layer with plausible (never dereferenced) aligned addresses.
+FAKE = 0x7F0000000000
+
+
+def _layer(nk, **kw):
+    d = dict(k_codes=FAKE, k_scales=FAKE + 0x100000, v_codes=FAKE + 0x200000, v_scales=FAKE + 0x300000,
+             num_pages=10, num_kv_heads=8, head_dim=128, page_size=16, k_global=0.01, v_global=0.02)
+    d.update(kw)
+    return nk.CKVLayer(**d)
+
+
+def _append(nk, layer, k=FAKE, v=FAKE, dtype=1, T=4, stride=1024, slots=FAKE):
+    return nk.lib.nvfp4_kv_quantize_append(ctypes.byref(layer) if layer is not None else None,
+                                           ctypes.c_void_p(k), ctypes.c_void_p(v), dtype, T, stride,
+                                           ctypes.c_void_p(slots), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 2), (dict(page_size=32), 2), (dict(k_codes=0), 1), (dict(num_pages=0), 1),
+    (dict(num_kv_heads=0), 1), (dict(k_global=0.0), 1), (dict(v_global=float("inf")), 1),
+    (dict(k_global=float("nan")), 1), (dict(k_global=1e-35), 1), (dict(k_codes=FAKE + 8), 2),
+    (dict(v_scales=FAKE + 2), 2), (dict(num_pages=1 << 28), 2),
+])
+def test_layer_checks(kw, status):
+    nk = _lib()
+    assert _append(nk, _layer(nk, **kw)) == status
+
+
+def test_append_checks():
+    nk = _lib()
+    L = _layer(nk)
+    assert nk.lib.nvfp4_kv_quantize_append(None, None, None, 1, 1, 1024, None, None) == 1
+    assert _append(nk, L, T=0, k=0, v=0, slots=0) == 0  # empty append is a no-op
+    assert _append(nk, L, T=-1) == 1
+    assert _append(nk, L, dtype=7) == 1
+    assert _append(nk, L, k=0) == 1
+    assert _append(nk, L, slots=0) == 1
+    assert _append(nk, L, stride=1023) == 1  # < H*128
+    assert _append(nk, L, k=FAKE + 4) == 2  # misaligned input
+    assert _append(nk, L, stride=1028, dtype=1) == 2  # token stride not a multiple of 16 bytes
+
+
+def _decode(nk, layer, q=FAKE, qdt=1, B=2, Hq=64, bt=FAKE, bts=4, sl=FAKE, msl=64, sm=0.088, out=FAKE,
+            ws=FAKE, wsb=1 << 30):
+    return nk.lib.nvfp4_paged_decode_attn(ctypes.byref(layer), ctypes.c_void_p(q), qdt, B, Hq, ctypes.c_void_p(bt),
+                                          bts, ctypes.c_void_p(sl), msl, sm, ctypes.c_void_p(out),
+                                          ctypes.c_void_p(ws), wsb, None)
+
+
+def test_decode_checks():
+    nk = _lib()
+    L = _layer(nk)
+    assert _decode(nk, L, Hq=60) == 1          # not a multiple of num_kv_heads
+    assert _decode(nk, L, Hq=8 * 17) == 2      # more than 16 q heads per kv head
+    assert _decode(nk, L, qdt=3) == 1
+    assert _decode(nk, L, B=-1) == 1
+    assert _decode(nk, L, B=0, q=0, bt=0, sl=0, out=0) == 0  # empty batch
+    assert _decode(nk, L, q=0) == 1
+    assert _decode(nk, L, out=0) == 1
+    assert _decode(nk, L, bts=3) == 1          # 3*16 < max_seq_len 64
+    assert _decode(nk, L, sm=float("inf")) == 1
+    assert _decode(nk, L, q=FAKE + 2) == 2
+    # workspace: too small, or missing when needed
+    need = nk.decode_workspace_bytes(1, 64, 8, 1 << 20)
+    assert need > 0
+    assert _decode(nk, L, B=1, msl=1 << 20, bts=1 << 16, wsb=need - 1) == 3
+    assert _decode(nk, L, B=1, msl=1 << 20, bts=1 << 16, ws=0, wsb=need) == 1
+
+
+def test_decode_workspace_size_rules():
+    nk = _lib()
+    assert nk.decode_workspace_bytes(0, 64, 8, 8192) == 0
+    assert nk.decode_workspace_bytes(32, 64, 8, 0) == 0
+    assert nk.decode_workspace_bytes(32, 60, 8, 8192) == 0          # invalid grouping
+    assert nk.decode_workspace_bytes(1, 96, 8, 2_000_000) > 0        # a long context needs split partials
+    # monotone in the context bound for a fixed batch
+    sizes = [nk.decode_workspace_bytes(4, 32, 8, n) for n in (1 << 14, 1 << 16, 1 << 18, 1 << 20)]
+    assert sizes == sorted(sizes)
+
+
+def _ws(nk, layer, bt=FAKE, bts=8, n=2, pl=FAKE, wo=FAKE, mpl=100, ks=1.0, vs=1.0, wk=FAKE, wv=FAKE, cap=1000):
+    return nk.lib.nvfp4_dequant_to_fp8_workspace(ctypes.byref(layer), ctypes.c_void_p(bt), bts, n,
+                                                 ctypes.c_void_p(pl), ctypes.c_void_p(wo), mpl, ks, vs,
+                                                 ctypes.c_void_p(wk), ctypes.c_void_p(wv), cap, None)
+
+
+def test_workspace_dequant_checks():
+    nk = _lib()
+    L = _layer(nk)
+    assert _ws(nk, L, n=-1) == 1
+    assert _ws(nk, L, mpl=-1) == 1
+    assert _ws(nk, L, cap=-1) == 1
+    assert _ws(nk, L, ks=0.0) == 1
+    assert _ws(nk, L, vs=float("nan")) == 1
+    assert _ws(nk, L, n=0, bt=0, pl=0, wo=0, wk=0, wv=0) == 0  # nothing to do
+    assert _ws(nk, L, wk=0) == 1
+    assert _ws(nk, L, bts=6) == 1                              # 6*16 < 100
+    assert _ws(nk, L, wv=FAKE + 4) == 2
