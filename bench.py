@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa70b_b32_8k",
-                    choices=["gqa70b_b32_8k", "long_b8_128k", "agentic_b1_2m", "tiny"])
+                    choices=["gqa70b_b32_8k", "long_b8_128k", "agentic_b1_2m", "mixed_64", "tiny"])
     ap.add_argument("--layers", type=int, default=0, help="override the number of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -122,6 +122,104 @@ def cpu_baseline(wl, target_s: float):
     }
 
 
+def bench_mixed(args, wl, dev):
+    """Mixed serving step per layer: quantize-append every new token (16 per
+    decoding sequence, 2048 per extended sequence), dequantize the extended
+    sequences' cached prefixes into the one FP8 workspace pair every layer
+    reuses, then decode attention for the 56 decoding sequences."""
+    import numpy as np
+    import torch
+
+    import nvfp4_quantized_paged_kv_amd as nk
+    from nvfp4_quantized_paged_kv_amd.workloads import build_mixed_step
+
+    L = args.layers or wl.layers
+    stream = torch.cuda.current_stream()
+    steps = []
+    append_ms, append_bytes = [], []
+    for l in range(L):
+        st = build_mixed_step(wl, l, dev, timed=True)
+        append_ms += st.filled.append_ms
+        append_bytes += st.filled.append_bytes
+        steps.append(st)
+        print(f"[bench] layer {l} filled", file=sys.stderr, flush=True)
+    s0 = steps[0]
+    H, Hq = wl.kv_heads, wl.q_heads
+    n_dec, n_ext = s0.decode.size, s0.extend.size
+    ws_cap = int(s0.ext_offsets[-1].item())
+    ws_k = torch.empty((ws_cap, H, 128), dtype=torch.uint8, device=dev)  # one pair for every layer
+    ws_v = torch.empty_like(ws_k)
+    out = torch.empty((n_dec, Hq, 128), dtype=torch.float32, device=dev)
+    wsb = nk.decode_workspace_bytes(n_dec, Hq, H, s0.max_dec_len)
+    dws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    in_b = s0.new_k.element_size()
+    t_new = s0.new_slots.numel()
+    dec_tokens = int(s0.dec_lens.sum().item())
+    dec_pages = int(((s0.dec_lens + 15) // 16).sum().item())
+    ext_pages = int(((s0.ext_prefix + 15) // 16).sum().item())
+    b_app = t_new * H * (2 * 128 * in_b + 144) + 4 * t_new
+    b_ws = ws_cap * H * (144 + 256) + ext_pages * 4
+    b_dec = dec_tokens * H * 144 + dec_pages * 4 + n_dec * Hq * 128 * (in_b + 4)
+    sm = 1 / math.sqrt(128)
+
+    def step(l, ev=None):
+        st = steps[l]
+        if ev is not None:
+            ev[0].record(stream)
+        nk.quantize_append(st.filled.layer, st.new_k, st.new_v, st.new_slots)
+        if ev is not None:
+            ev[1].record(stream)
+        nk.dequant_to_fp8_workspace(st.filled.layer, st.ext_table, st.ext_prefix, st.ext_offsets, st.max_prefix,
+                                    6 * st.filled.layer.k_global, 6 * st.filled.layer.v_global, ws_k, ws_v)
+        if ev is not None:
+            ev[2].record(stream)
+        nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
+                             workspace=dws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i % L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % L)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i % L, evs[i])
+    torch.cuda.synchronize()
+    app = np.array([e[0].elapsed_time(e[1]) for e in evs]) / 1e3
+    wsd = np.array([e[1].elapsed_time(e[2]) for e in evs]) / 1e3
+    dec = np.array([e[2].elapsed_time(e[3]) for e in evs]) / 1e3
+    b_step = b_app + b_ws + b_dec
+    achieved = b_dec / dec.mean() / 1e9
+    kernel_file = os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", "decode_attn.hip")
+    return {
+        "value": round(b_step / (wall / args.steps) / 1e9, 2),
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "config": {"workload": wl.name, "sequences": len(s0.lens), "decode_sequences": int(n_dec),
+                   "extend_sequences": int(n_ext), "q_heads": Hq, "kv_heads": H, "head_dim": 128, "page_size": 16,
+                   "layers_rotated": L, "new_tokens": int(t_new), "decode_tokens": dec_tokens,
+                   "workspace_tokens": ws_cap,
+                   "step": "append 16/2048 tokens + FP8 workspace dequant of 8 prefixes + decode of 56, one layer"},
+        "pct_of_peak": round(100 * b_step / (wall / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
+        "decode_attn_gbs_events": round(achieved, 2),
+        "decode_attn_us": round(dec.mean() * 1e6, 3),
+        "append_step_gbs": round(b_app / app.mean() / 1e9, 2),
+        "append_step_us": round(app.mean() * 1e6, 3),
+        "fp8_workspace_gbs": round(b_ws / wsd.mean() / 1e9, 2),
+        "fp8_workspace_us": round(wsd.mean() * 1e6, 3),
+        "quantize_append_bulk_gbs": round(sum(append_bytes) / (sum(append_ms) / 1e3) / 1e9, 2),
+        "bytes_per_step": int(b_step),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(kernel_file, wl.name),
+                     "kernel": "nvfp4_paged_decode_attn", "algorithmic_bytes_per_call": int(b_dec)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -139,6 +237,18 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = synth.WORKLOADS[args.workload]
+    if wl.lens:
+        res = bench_mixed(args, wl, dev)
+        result = {"metric": METRIC, "value": res.pop("value"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                  "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+                  "scaling": "weak", "vs_baseline": None,
+                  "dtype": "nvfp4 cache; bf16 in; f16 MFMA, fp32 accumulate",
+                  "data": "synthetic (seeded torch generators)"}
+        result.update(res)
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return
     L = args.layers or wl.layers
     B, Hq, H, ctx = wl.batch, wl.q_heads, wl.kv_heads, wl.ctx
     pages_per_seq = (ctx + 15) // 16

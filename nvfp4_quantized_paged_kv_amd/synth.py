@@ -49,6 +49,22 @@ WORKLOADS = {
 }
 
 
+# Mixed serving step: 64 ragged sequences (log-uniform 512..65536 tokens);
+# 8 of them are extended by a 2048-token chunk (their cached prefix goes
+# through the FP8 workspace), the other 56 append 16 tokens and decode.
+MIXED_N_EXTEND = 8
+MIXED_EXTEND_NEW = 2048
+MIXED_DECODE_NEW = 16
+
+
+def mixed_roles(n: int = 64, n_extend: int = MIXED_N_EXTEND, seed: int = BASE_SEED + 6):
+    """(extend sequence indices, decode sequence indices), both sorted."""
+    rng = np.random.default_rng(seed)
+    ext = np.sort(rng.choice(n, n_extend, replace=False)).astype(np.int64)
+    dec = np.setdiff1d(np.arange(n), ext).astype(np.int64)
+    return ext, dec
+
+
 def chunk_tokens(H: int) -> int:
     """Tokens per generated chunk (about 2^27 values, 256 MiB of bf16)."""
     return max(1, (1 << 27) // (H * HEAD_DIM))
@@ -91,6 +107,10 @@ def mixed_lengths(n: int = 64, lo: int = 512, hi: int = 65536, seed: int = BASE_
     """Log-uniform ragged lengths for the mixed serving step."""
     rng = np.random.default_rng(seed)
     return [int(x) for x in np.exp(rng.uniform(math.log(lo), math.log(hi), n)).astype(np.int64)]
+
+
+WORKLOADS["mixed_64"] = Workload("mixed_64", 64, 64, 8, 65536, 4, torch.bfloat16, "chan50",
+                                 lens=tuple(mixed_lengths()))
 
 
 def seed_of(*parts: int) -> int:

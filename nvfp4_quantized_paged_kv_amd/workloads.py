@@ -52,3 +52,54 @@ def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device
             on_chunk(c0, n, k, v, seq, pos)
         del k, v
     return FilledLayer(layer, bt, torch.from_numpy(bt).to(device), ms, by)
+
+
+@dataclass
+class MixedStep:
+    """One layer of the mixed serving step, ready to run."""
+    filled: FilledLayer
+    lens: list                  # cached tokens per sequence before the step
+    extend: np.ndarray          # indices of the extended sequences
+    decode: np.ndarray          # indices of the decoding sequences
+    new_k: torch.Tensor         # [T_new, H, 128] all new tokens of the step
+    new_v: torch.Tensor
+    new_slots: torch.Tensor     # [T_new] int32
+    new_seq: np.ndarray         # sequence of each new token
+    new_pos: np.ndarray         # position of each new token
+    dec_table: torch.Tensor     # [56, width] block-table rows of the decoding sequences
+    dec_lens: torch.Tensor      # [56] lengths after the append (L + 16)
+    dec_q: torch.Tensor         # [56, Hq, 128]
+    ext_table: torch.Tensor     # [8, width] block-table rows of the extended sequences
+    ext_prefix: torch.Tensor    # [8] cached prefix lengths (L)
+    ext_offsets: torch.Tensor   # [9] workspace token offsets
+    max_dec_len: int
+    max_prefix: int
+
+
+def build_mixed_step(wl: synth.Workload, layer_idx: int, device="cuda", on_chunk=None, timed=False) -> MixedStep:
+    lens = list(wl.lens)
+    ext, dec = synth.mixed_roles(len(lens))
+    grow = np.full(len(lens), synth.MIXED_DECODE_NEW, np.int64)
+    grow[ext] = synth.MIXED_EXTEND_NEW
+    pool_lens = (np.asarray(lens) + grow).tolist()
+    fl = build_layer(wl, lens, pool_lens, layer_idx, device, on_chunk=on_chunk, timed=timed)
+    bt = fl.block_table
+    new_seq = np.repeat(np.arange(len(lens)), grow)
+    new_pos = np.concatenate([np.arange(lens[b], lens[b] + grow[b]) for b in range(len(lens))])
+    T_new = new_seq.size
+    new_k = synth.kv_values(T_new, wl.kv_heads, wl.dist, wl.outlier_frac, 0, wl.in_dtype, device, 3, layer_idx)
+    new_v = synth.kv_values(T_new, wl.kv_heads, wl.dist, wl.outlier_frac, 1, wl.in_dtype, device, 3, layer_idx)
+    slots = (bt[new_seq, new_pos // synth.PAGE].astype(np.int64) * synth.PAGE + new_pos % synth.PAGE).astype(np.int32)
+    dec_lens = np.asarray(lens)[dec] + synth.MIXED_DECODE_NEW
+    prefix = np.asarray(lens)[ext]
+    offs = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32)
+    return MixedStep(
+        filled=fl, lens=lens, extend=ext, decode=dec, new_k=new_k, new_v=new_v,
+        new_slots=torch.from_numpy(slots).to(device), new_seq=new_seq, new_pos=new_pos,
+        dec_table=torch.from_numpy(np.ascontiguousarray(bt[dec])).to(device),
+        dec_lens=torch.from_numpy(dec_lens.astype(np.int32)).to(device),
+        dec_q=synth.queries(dec.size, wl.q_heads, wl.in_dtype, device, 4, layer_idx),
+        ext_table=torch.from_numpy(np.ascontiguousarray(bt[ext])).to(device),
+        ext_prefix=torch.from_numpy(prefix.astype(np.int32)).to(device),
+        ext_offsets=torch.from_numpy(offs).to(device),
+        max_dec_len=int(dec_lens.max()), max_prefix=int(prefix.max()))
