@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the number of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after the timed region, run a 1 GiB float32 elementwise add (reads 1 GiB, writes "
+                         "1 GiB) so hardware byte counters can be scaled against a kernel of known size")
     return ap.parse_args()
 
 
@@ -220,6 +223,17 @@ def bench_mixed(args, wl, dev):
     }
 
 
+def calibration_kernel():
+    """A plain elementwise kernel of known traffic: y = x + 1 over 2^28 float32."""
+    import torch
+
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.add(x, 1.0, out=y)
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +259,8 @@ def main():
                   "dtype": "nvfp4 cache; bf16 in; f16 MFMA, fp32 accumulate",
                   "data": "synthetic (seeded torch generators)"}
         result.update(res)
+        if args.calibrate:
+            calibration_kernel()
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
         print(json.dumps(result), flush=True)
@@ -376,6 +392,8 @@ def main():
                      "kernel": "nvfp4_paged_decode_attn (decode_split_kernel + decode_combine_kernel)",
                      "algorithmic_bytes_per_call": int(bytes_decode)},
     }
+    if args.calibrate:
+        calibration_kernel()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
