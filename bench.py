@@ -153,8 +153,7 @@ def bench_mixed(args, wl, dev):
     ws_k = torch.empty((ws_cap, H, 128), dtype=torch.uint8, device=dev)  # one pair for every layer
     ws_v = torch.empty_like(ws_k)
     out = torch.empty((n_dec, Hq, 128), dtype=torch.float32, device=dev)
-    wsb = nk.decode_workspace_bytes(n_dec, Hq, H, s0.max_dec_len)
-    dws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    dws = nk.decode_workspace(n_dec, Hq, H, s0.max_dec_len, dev)
     in_b = s0.new_k.element_size()
     t_new = s0.new_slots.numel()
     dec_tokens = int(s0.dec_lens.sum().item())
@@ -293,8 +292,7 @@ def main():
 
     seq_lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
     sm = 1 / math.sqrt(128)
-    ws_bytes = nk.decode_workspace_bytes(B, Hq, H, ctx)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    workspace = nk.decode_workspace(B, Hq, H, ctx, dev)
     out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
 
     in_b = newk[0].element_size()

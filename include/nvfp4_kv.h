@@ -105,7 +105,7 @@ NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer,
                                                   const int32_t* slot_mapping, void* stream);
 
 /* Bytes of device workspace nvfp4_paged_decode_attn needs for these (host)
- * sizes; 0 when batch or max_seq_len is 0.  Returns 0 for invalid sizes too. */
+ * sizes (never 0 for batch > 0); 0 for batch 0 or sizes the call rejects. */
 NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                                     int32_t max_seq_len);
 
@@ -125,10 +125,14 @@ NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q
  *   max_seq_len  : host bound used to size the launch; block_table_stride must
  *                  be >= ceil(max_seq_len/16).
  *   out          : [batch][num_q_heads][128] float32.
- *   workspace    : >= nvfp4_paged_decode_workspace_bytes(...) bytes, 16-byte
- *                  aligned; holds split-K partial results; contents on entry are
- *                  ignored.  Calls that share a workspace must be ordered on
- *                  one stream. */
+ *   workspace    : >= nvfp4_paged_decode_workspace_bytes(...) bytes, 256-byte
+ *                  aligned.  It holds one arrival counter per (sequence,
+ *                  kv head) and the partial results of the (sequence, kv head)
+ *                  pairs whose pages are shared by several workgroups.  It must be zero-filled once before its
+ *                  first use; every call leaves the counters at zero again.
+ *                  Calls that share a workspace must be ordered on one stream.
+ *   Supported: batch <= 4096 and
+ *              batch * num_kv_heads * ceil(max_seq_len/16) <= 2^30. */
 NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
                                                  int32_t batch, int32_t num_q_heads, const int32_t* block_table,
                                                  int32_t block_table_stride, const int32_t* seq_lens,

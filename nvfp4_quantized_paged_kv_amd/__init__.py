@@ -180,6 +180,12 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_
     return int(lib.nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
 
 
+def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int, device="cuda") -> torch.Tensor:
+    """A zero-filled decode workspace (the library keeps it zeroed between calls)."""
+    need = max(decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len), 256)
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
 def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                       max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
@@ -197,7 +203,7 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
         raise ValueError("out must be a contiguous float32 [B, Hq, 128] tensor")
     need = decode_workspace_bytes(B, Hq, layer.num_kv_heads, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(B, Hq, layer.num_kv_heads, max_seq_len, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = layer.c_struct()
     st = lib.nvfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), B, Hq, _ptr(block_table),

@@ -69,10 +69,16 @@ NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer,
   return from_hip(launch_quantize_append(p, dtype, static_cast<hipStream_t>(stream)));
 }
 
+// The decode kernel indexes the (sequence, kv head, page) work of a call in 32 bits.
+static bool decode_size_ok(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+  return (int64_t)batch * num_kv_heads * (((int64_t)max_seq_len + kPageSize - 1) / kPageSize) <= (int64_t)1 << 30;
+}
+
 NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                                     int32_t max_seq_len) {
-  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (batch < 0 || batch > kMaxDecodeBatch || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
   if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return 0;
+  if (!decode_size_ok(batch, num_kv_heads, max_seq_len)) return 0;
   return decode_geometry(batch, num_q_heads, num_kv_heads, max_seq_len).workspace_bytes;
 }
 
@@ -85,8 +91,9 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(q_dtype) || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return NVFP4_ERR_INVALID_ARGUMENT;
   if (num_q_heads % layer->num_kv_heads != 0) return NVFP4_ERR_INVALID_ARGUMENT;
-  if (num_q_heads / layer->num_kv_heads > kMaxGroup) return NVFP4_ERR_UNSUPPORTED;
+  if (num_q_heads / layer->num_kv_heads > kMaxGroup || batch > kMaxDecodeBatch) return NVFP4_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!decode_size_ok(batch, layer->num_kv_heads, max_seq_len)) return NVFP4_ERR_UNSUPPORTED;
   if (batch == 0) return NVFP4_OK;
   if (!q || !block_table || !seq_lens || !out) return NVFP4_ERR_INVALID_ARGUMENT;
   if ((int64_t)block_table_stride * kPageSize < (int64_t)max_seq_len || block_table_stride < 0)
@@ -94,7 +101,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   if (!aligned(q, 16)) return NVFP4_ERR_UNSUPPORTED;
   const DecodeGeometry geo = decode_geometry(batch, num_q_heads, layer->num_kv_heads, max_seq_len);
   if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
-  if (geo.workspace_bytes > 0 && (!workspace || !aligned(workspace, 16))) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARGUMENT;
   const double qk = (double)sm_scale * (double)layer->k_global * 1.4426950408889634;  // log2(e)
   if (!std::isfinite(qk)) return NVFP4_ERR_INVALID_ARGUMENT;
   DecodeParams p;
@@ -106,9 +113,8 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   const int64_t G = num_q_heads / layer->num_kv_heads;
-  const int64_t units = (int64_t)batch * layer->num_kv_heads * geo.num_splits * G;
-  p.part_o = geo.workspace_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
-  p.part_ml = geo.workspace_bytes > 0 ? static_cast<float*>(workspace) + units * kHeadDim : nullptr;
+  p.counters = static_cast<int32_t*>(workspace);
+  p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + geo.counters_bytes);
   p.out = out;
   p.num_pages = layer->num_pages;
   p.H = layer->num_kv_heads;
@@ -117,11 +123,10 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   p.batch = batch;
   p.bt_stride = block_table_stride;
   p.max_seq_len = max_seq_len;
-  p.pages_per_split = geo.pages_per_split > 0 ? geo.pages_per_split : 4;
-  p.num_splits = geo.num_splits;
+  p.num_groups = geo.num_groups;
   p.qk_scale_log2 = (float)qk;
   p.v_global = layer->v_global;
-  return from_hip(launch_decode(p, q_dtype, geo.needs_combine, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
 }
 
 NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* layer, const int32_t* block_table,

@@ -43,8 +43,8 @@ struct DecodeParams {
   const void* q;           // [B][Hq][128]
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* part_o;           // [B][H][S][G][128] unnormalised split outputs (S > 1 only)
-  float* part_ml;          // [B][H][S][G][2]   (running max in log2 units, sum of weights)
+  float* part;             // [B*H + num_groups][G][128 + 2]: unnormalised O, running max (log2), sum
+  int32_t* counters;       // [B*H] arrival counters of split sequences; zero between calls
   float* out;              // [B][Hq][128]
   int32_t num_pages;
   int32_t H;
@@ -53,22 +53,24 @@ struct DecodeParams {
   int32_t batch;
   int32_t bt_stride;
   int32_t max_seq_len;
-  int32_t pages_per_split;
-  int32_t num_splits;
+  int32_t num_groups;      // workgroups of the launch
   float qk_scale_log2;     // sm_scale * k_global * log2(e)
   float v_global;
 };
 
-// Split-K geometry for a decode call (shared by the workspace query and the launch).
+constexpr int kMaxDecodeBatch = 4096;  // sequences per decode call (prefix sums kept in LDS)
+
+// Launch geometry and workspace of a decode call (shared by the workspace
+// query and the launch).  Workspace = counters (B*H int32, padded to 256 B)
+// followed by the split partials.
 struct DecodeGeometry {
-  int32_t pages_per_split;
-  int32_t num_splits;
-  size_t workspace_bytes;  // split partials; 0 when no sequence can need more than one split
-  bool needs_combine;      // some sequence may span more than one split
+  int32_t num_groups;
+  size_t counters_bytes;
+  size_t workspace_bytes;
 };
 DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len);
 
-hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, bool needs_combine, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
 
 struct DequantWsParams {
   const uint8_t* codes[2];

@@ -105,6 +105,9 @@ def test_decode_checks():
     assert _decode(nk, L, bts=3) == 1          # 3*16 < max_seq_len 64
     assert _decode(nk, L, sm=float("inf")) == 1
     assert _decode(nk, L, q=FAKE + 2) == 2
+    assert _decode(nk, L, B=4097, bts=4) == 2  # more sequences than one launch handles
+    assert _decode(nk, L, B=4096, msl=1 << 20, bts=1 << 16) == 2  # 2^31 (sequence, head, page) items
+    assert _decode(nk, L, ws=FAKE + 16) == 1   # workspace must be 256-byte aligned
     # workspace: too small, or missing when needed
     need = nk.decode_workspace_bytes(1, 64, 8, 1 << 20)
     assert need > 0
@@ -115,8 +118,11 @@ def test_decode_checks():
 def test_decode_workspace_size_rules():
     nk = _lib()
     assert nk.decode_workspace_bytes(0, 64, 8, 8192) == 0
-    assert nk.decode_workspace_bytes(32, 64, 8, 0) == 0
+    assert nk.decode_workspace_bytes(32, 64, 8, 0) > 0               # counters even for an empty context
     assert nk.decode_workspace_bytes(32, 60, 8, 8192) == 0          # invalid grouping
+    assert nk.decode_workspace_bytes(4097, 64, 8, 8192) == 0        # batch limit
+    assert nk.decode_workspace_bytes(4096, 64, 8, 1 << 20) == 0     # 2^31 work items
+    assert nk.decode_workspace_bytes(2048, 64, 8, 1 << 20) > 0      # 2^30 work items
     assert nk.decode_workspace_bytes(1, 96, 8, 2_000_000) > 0        # a long context needs split partials
     # monotone in the context bound for a fixed batch
     sizes = [nk.decode_workspace_bytes(4, 32, 8, n) for n in (1 << 14, 1 << 16, 1 << 18, 1 << 20)]

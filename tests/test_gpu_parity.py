@@ -187,6 +187,31 @@ def test_decode_split_count_invariance():
     assert row_rel_err(a, b).max() <= ATTN_TOL
 
 
+def test_decode_workspace_reuse_and_counters():
+    """Sequences shared by many workgroups: repeated calls on one workspace give the
+    same result and leave every arrival counter at zero."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: decode workspace reuse (shared sequences)")
+    c = build_cache([20000, 3, 16000], 2, torch.bfloat16, "sparse6", 0.003, False, seed=41)
+    B, Hq = 3, 2 * 8
+    q = synth.queries(B, Hq, torch.bfloat16, "cpu", 41, 1).cuda()
+    bt = torch.from_numpy(c.bt).cuda()
+    sl = torch.tensor(c.lens, dtype=torch.int32, device="cuda")
+    ws = nk.decode_workspace(B, Hq, 2, 20000)
+    outs = []
+    for _ in range(3):
+        outs.append(nk.paged_decode_attn(c.layer, q, bt, sl, 20000, 1 / math.sqrt(128), workspace=ws).clone())
+    torch.cuda.synchronize()
+    n_units = B * 2
+    assert not ws[: 4 * n_units].any(), "arrival counters not reset"
+    ref = oracle.decode_attention(c.planes, c.g_k, c.g_v, host_f32(q), c.bt, np.array(c.lens, np.int32),
+                                  float(np.float32(1 / math.sqrt(128))))
+    for o in outs:
+        assert row_rel_err(o.cpu().numpy().reshape(-1, 128), ref).max() <= ATTN_TOL
+        assert torch.equal(o, outs[0])
+
+
 # ------------------------------------------------------- FP8 workspace dequant
 
 
