@@ -64,6 +64,17 @@ __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
 // query head) with the gfx950 row/half swaps: with both operands equal,
 // permlane16_swap returns (row 2k, row 2k+1) values and permlane32_swap the
 // (low half, high half) values.
+// IEEE maximum (v_maximum3_f32 on gfx950): NaN-propagating, so the compiler
+// adds no quieting copies around it as it does for fmaxf; the operands here
+// are finite scores or -inf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+__device__ __forceinline__ float vmax_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float max_over_groups(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -124,7 +135,6 @@ struct PageRegs {
   uint32_t ksw;  // K scales: token r, blocks 2*q4, 2*q4+1
   uint4 vw;      // V codes: tokens 4*q4 .. 4*q4+3, dims 8*r .. 8*r+7
   uint32_t vsw;  // V scales: block r/2, tokens 4*q4 .. 4*q4+3
-  int valid;
 };
 
 // Raw buffer loads from a per-page descriptor: the page's base address lives
@@ -141,23 +151,51 @@ struct LaneOffsets {
   int kc, ks, vc, vs;
 };
 
-__device__ __forceinline__ PageRegs load_page(const DecodeParams& p, int page, int pg, int seq_len, int h,
-                                              const LaneOffsets& lo) {
-  const bool ok = (unsigned)page < (unsigned)p.num_pages;
-  const int64_t tile = (int64_t)(ok ? page : 0) * p.H + h;
-  const auto kc = tile_rsrc(p.k_codes, tile * kTileCodeBytes, kTileCodeBytes);
-  const auto ks = tile_rsrc(p.k_scales, tile * kTileScaleBytes, kTileScaleBytes);
-  const auto vc = tile_rsrc(p.v_codes, tile * kTileCodeBytes, kTileCodeBytes);
-  const auto vs = tile_rsrc(p.v_scales, tile * kTileScaleBytes, kTileScaleBytes);
-  PageRegs d;
-  d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, lo.kc, 0, 0));
-  d.ksw = __builtin_amdgcn_raw_buffer_load_b16(ks, lo.ks, 0, 0);
-  d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, lo.vc, 0, 0));
-  d.vsw = __builtin_amdgcn_raw_buffer_load_b32(vs, lo.vs, 0, 0);
-  d.valid = ok ? min(kPageSize, seq_len - pg * kPageSize) : 0;
-  return d;
+// The four planes' descriptors.  kPlane: one descriptor per plane for the
+// whole call and the tile's offset in an SGPR (planes below 4 GiB); otherwise
+// a descriptor per tile.
+struct PlaneRsrc {
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+};
+
+template <bool kPlane>
+__device__ __forceinline__ PlaneRsrc plane_rsrc(const DecodeParams& p) {
+  PlaneRsrc r;
+  if (kPlane) {
+    const int64_t tiles = (int64_t)p.num_pages * p.H;
+    r.kc = tile_rsrc(p.k_codes, 0, (int)(uint32_t)(tiles * kTileCodeBytes));
+    r.ks = tile_rsrc(p.k_scales, 0, (int)(uint32_t)(tiles * kTileScaleBytes));
+    r.vc = tile_rsrc(p.v_codes, 0, (int)(uint32_t)(tiles * kTileCodeBytes));
+    r.vs = tile_rsrc(p.v_scales, 0, (int)(uint32_t)(tiles * kTileScaleBytes));
+  }
+  return r;
 }
 
+template <bool kPlane>
+__device__ __forceinline__ PageRegs load_page(const DecodeParams& p, const PlaneRsrc& pr, int page, int h,
+                                              const LaneOffsets& lo) {
+  const bool ok = (unsigned)page < (unsigned)p.num_pages;
+  PageRegs d;
+  if (kPlane) {
+    const uint32_t tile = (uint32_t)(ok ? page : 0) * (uint32_t)p.H + (uint32_t)h;
+    const int so_c = (int)(tile * kTileCodeBytes), so_s = (int)(tile * kTileScaleBytes);
+    d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.kc, lo.kc, so_c, 0));
+    d.ksw = __builtin_amdgcn_raw_buffer_load_b16(pr.ks, lo.ks, so_s, 0);
+    d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.vc, lo.vc, so_c, 0));
+    d.vsw = __builtin_amdgcn_raw_buffer_load_b32(pr.vs, lo.vs, so_s, 0);
+  } else {
+    const int64_t tile = (int64_t)(ok ? page : 0) * p.H + h;
+    const auto kc = tile_rsrc(p.k_codes, tile * kTileCodeBytes, kTileCodeBytes);
+    const auto ks = tile_rsrc(p.k_scales, tile * kTileScaleBytes, kTileScaleBytes);
+    const auto vc = tile_rsrc(p.v_codes, tile * kTileCodeBytes, kTileCodeBytes);
+    const auto vs = tile_rsrc(p.v_scales, tile * kTileScaleBytes, kTileScaleBytes);
+    d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, lo.kc, 0, 0));
+    d.ksw = __builtin_amdgcn_raw_buffer_load_b16(ks, lo.ks, 0, 0);
+    d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, lo.vc, 0, 0));
+    d.vsw = __builtin_amdgcn_raw_buffer_load_b32(vs, lo.vs, 0, 0);
+  }
+  return d;
+}
 
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -170,7 +208,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // A value every lane of the wave holds (read from LDS): keep it in an SGPR.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <bool QF32>
+template <bool QF32, bool kPlane>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ int s_pref[kMaxDecodeBatch + 1];  // exclusive prefix of pages per sequence
   __shared__ int s_wsum[kWaves];
@@ -183,8 +221,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets the page loop run on SGPRs
   const int lane = tid & 63;
-  const int r = lane & 15, q4 = lane >> 4;
+  const int q4 = lane >> 4;
   const int B = p.batch, H = p.H, G = p.G;
+  const PlaneRsrc planes = plane_rsrc<kPlane>(p);
 
   // ---- pages of every sequence and their exclusive prefix sums (4 sequences per thread)
   int pg[4];
@@ -292,7 +331,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #undef NVFP4_SWZ
     int qe = 0;
     (void)__builtin_frexpf(qmax, &qe);                                          // qmax < 2^qe
-    const float qscale = qmax > 0.0f ? __builtin_ldexpf(1.0f, 15 - qe) : 1.0f;  // exact power of two
+    // exact power of two, with the sign of the logit scale so that tscale >= 0
+    // (then the page maximum can be taken on the raw scores)
+    const float qscale = __builtin_copysignf(qmax > 0.0f ? __builtin_ldexpf(1.0f, 15 - qe) : 1.0f, p.qk_scale_log2);
     half8_t qa[4];
     half8_t ql[4];
 #pragma unroll
@@ -303,17 +344,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         qa[c][j] = (_Float16)xq;
         if (QF32) ql[c][j] = (_Float16)(xq - (float)qa[c][j]);
       }
-    const float tscale = p.qk_scale_log2 / qscale;
+    // > 0: a zero logit scale becomes FLT_MIN (uniform weights to fp32
+    // precision), so masked scores (-inf) always give weight exactly 0
+    const float tscale = fmaxf(p.qk_scale_log2 / qscale, __FLT_MIN__);
     const int seq_len = min(uni(len_v), p.max_seq_len);
 
-    float m_run = -__builtin_inff();
+    // running max; -FLT_MAX stands for "none yet" (exp2 of anything minus it is 0)
+    float m_run = -__FLT_MAX__;
+    float m_lim = -__FLT_MAX__;  // m_run + kLazyMax: the max moves only above this
     float l_run = 0.0f;
     float4_t acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto process = [&](const PageRegs& cur) {
-      const int valid = cur.valid;
+    auto process = [&](const PageRegs& cur, int valid) {
 
       // ---- S^T = K . Q^T over the page; lane (q head r, tokens 4*q4 .. 4*q4+3)
       const half2_t ks0 = e4m3_pair_to_f16_scaled(cur.ksw & 0xFFu, cur.ksw & 0xFFu);
@@ -331,21 +375,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qa[c], S, 0, 0, 0);
         if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[c], S, 0, 0, 0);
       }
+      // The MFMA result is read next, possibly across the partial-page branch;
+      // the compiler's wait-state insertion missed that path (the first read
+      // came a few cycles after the MFMA), so wait explicitly: 20 wait states
+      // cover the write-to-VALU-read latency of MFMAs up to 16 passes.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(S));
 
-      // ---- online softmax (log2 domain).  Raw v_exp_f32: weights below 2^-126
-      // of the running max flush to 0, which the f16 weights could not hold anyway.
-      float t[4];
-      if (valid == kPageSize) {
+      // ---- online softmax (log2 domain) on t = S * tscale (tscale >= 0, so the
+      // maximum of t is the maximum of S times tscale).  Raw v_exp_f32: weights
+      // below 2^-126 of the running max flush to 0, which f16 could not hold.
+      if (valid != kPageSize) {  // tokens past the sequence end (or a bad page index)
   #pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = S[i] * tscale;
-      } else {
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = (4 * q4 + i < valid) ? S[i] * tscale : -__builtin_inff();
+        for (int i = 0; i < 4; ++i)
+          if (4 * q4 + i >= valid) S[i] = -__builtin_inff();
       }
-      const float pm = max_over_groups(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
-      if (__any(pm > m_run + kLazyMax)) {
+      const float pm = vmax_over_groups(vmax(vmax3(S[0], S[1], S[2]), S[3])) * tscale;  // -inf: all masked
+      if (__any(pm > m_lim)) {
         const float m_new = fmaxf(m_run, pm);
-        const float f = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float f = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= f;
   #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -354,12 +401,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           for (int i = 0; i < 8; ++i) acc[i][jj] *= fj;
         }
         m_run = m_new;
+        m_lim = m_new + kLazyMax;
       }
-      // m_run is -inf only while every token seen so far was masked (t = -inf too)
-      const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
       float pr[4];
   #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - m_use);
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], tscale, -m_run));
       l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       const half4_t pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 
@@ -369,8 +415,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int nv = min(max(valid - 4 * q4, 0), 4);
         vsw &= nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);  // zero the scales of tokens past the end
       }
-      const half2_t vs01 = e4m3_pair_to_f16_scaled(vsw & 0xFFu, (vsw >> 8) & 0xFFu);
-      const half2_t vs23 = e4m3_pair_to_f16_scaled((vsw >> 16) & 0xFFu, vsw >> 24);
+      // scale bytes (s0, s1) -> f16 pair (s0 << 7, s1 << 7): bytes moved to 0 and 2, then one shift
+      const half2_t vs01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, vsw, 0x0C010C00u) << 7);
+      const half2_t vs23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, vsw, 0x0C030C02u) << 7);
       const uint32_t E01 = bfi(0x0F0F0F0Fu, cur.vw.x, cur.vw.y << 4), O01 = bfi(0x0F0F0F0Fu, cur.vw.x >> 4, cur.vw.y);
       const uint32_t E23 = bfi(0x0F0F0F0Fu, cur.vw.z, cur.vw.w << 4), O23 = bfi(0x0F0F0F0Fu, cur.vw.z >> 4, cur.vw.w);
   #define NVFP4_PV_STEP(C)                                                                   \
@@ -393,10 +440,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
     const LaneOffsets lo{er * 64 + eq * 16, er * 8 + eq * 2, el * 16, (er >> 1) * 16 + eq * 4};
     while (true) {
-      auto load_mine = [&](int j) {
-        const int jc = min(j, n_mine - 1);
-        const int page = jc < 64 ? __builtin_amdgcn_readlane(pidx0, jc) : __builtin_amdgcn_readlane(pidx1, jc - 64);
-        return load_page(p, page, c0 + wave + kWaves * jc, seq_len, h, lo);
+      auto page_of = [&](int j) {
+        return j < 64 ? __builtin_amdgcn_readlane(pidx0, j) : __builtin_amdgcn_readlane(pidx1, j - 64);
+      };
+      auto load_mine = [&](int j) { return load_page<kPlane>(p, planes, page_of(min(j, n_mine - 1)), h, lo); };
+      // valid tokens of page j (0 for a page index outside the cache): uniform
+      auto valid_of = [&](int j) {
+        return (unsigned)page_of(j) < (unsigned)p.num_pages ? min(kPageSize, seq_len - (c0 + wave + kWaves * j) * kPageSize)
+                                                            : 0;
       };
       // Two register sets, unrolled by two: each set is loaded one page ahead of
       // its use and refilled right after, so no register copy waits on a load in
@@ -406,11 +457,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int j = 0; j < n_mine; j += 2) {
           const PageRegs Bp = load_mine(j + 1);
           __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any work on the current page
-          process(A);
+          process(A, valid_of(j));
           if (j + 1 >= n_mine) break;
           A = load_mine(j + 2);
           __builtin_amdgcn_sched_barrier(0);
-          process(Bp);
+          process(Bp, valid_of(j + 1));
         }
       }
       // next chunk of the segment (only units of more than kChunkPages pages)
@@ -450,13 +501,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
       float O = 0.0f, L = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_m[w][g];
-        if (mw != -__builtin_inff()) {
-          const float f = exp2f(mw - M);
-          O += s_o[w][g][d] * f;
-          L += s_l[w][g] * f;
-        }
+      for (int w = 0; w < kWaves; ++w) {  // a wave without tokens has m = -FLT_MAX, O = L = 0
+        const float f = exp2f(s_m[w][g] - M);
+        O += s_o[w][g][d] * f;
+        L += s_l[w][g] * f;
       }
       if (whole) {
         p.out[((int64_t)b * p.Hq + (int64_t)h * G + g) * kHeadDim + d] = L > 0.0f ? O / L * p.v_global : 0.0f;
@@ -486,15 +534,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           for (int w2 = w_first; w2 <= w_last; ++w2)
             M = fmaxf(M, load_coherent(p.part + (((int64_t)u + w2) * G + g) * kPartStride + kHeadDim));
           float O = 0.0f, L = 0.0f;
-          if (M != -__builtin_inff()) {
-            for (int w2 = w_first; w2 <= w_last; ++w2) {
-              const float* ps = p.part + (((int64_t)u + w2) * G + g) * kPartStride;
-              const float ms = load_coherent(ps + kHeadDim);
-              if (ms == -__builtin_inff()) continue;
-              const float f = exp2f(ms - M);
-              O += load_coherent(ps + d) * f;
-              L += load_coherent(ps + kHeadDim + 1) * f;
-            }
+          for (int w2 = w_first; w2 <= w_last; ++w2) {
+            const float* ps = p.part + (((int64_t)u + w2) * G + g) * kPartStride;
+            const float f = exp2f(load_coherent(ps + kHeadDim) - M);
+            O += load_coherent(ps + d) * f;
+            L += load_coherent(ps + kHeadDim + 1) * f;
           }
           p.out[((int64_t)b * p.Hq + (int64_t)h * G + g) * kHeadDim + d] = L > 0.0f ? O / L * p.v_global : 0.0f;
         }
@@ -537,10 +581,17 @@ DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_k
 hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
   const dim3 grid((unsigned)p.num_groups);
-  if (q_dtype == NVFP4_DTYPE_F32)
-    hipLaunchKernelGGL(decode_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+  // one descriptor per plane when every tile offset fits the 32-bit buffer offset
+  const bool plane = (int64_t)p.num_pages * p.H * kTileCodeBytes <= (int64_t)UINT32_MAX;
+  const bool f32 = q_dtype == NVFP4_DTYPE_F32;
+  if (f32 && plane)
+    hipLaunchKernelGGL((decode_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
+  else if (f32)
+    hipLaunchKernelGGL((decode_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+  else if (plane)
+    hipLaunchKernelGGL((decode_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(decode_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
