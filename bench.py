@@ -387,7 +387,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "nvfp4_paged_decode_attn (decode_split_kernel + decode_combine_kernel)",
+                     "kernel": "nvfp4_paged_decode_attn (decode_kernel)",
                      "algorithmic_bytes_per_call": int(bytes_decode)},
     }
     if args.calibrate:

@@ -69,9 +69,11 @@ NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer,
   return from_hip(launch_quantize_append(p, dtype, static_cast<hipStream_t>(stream)));
 }
 
-// The decode kernel indexes the (sequence, kv head, page) work of a call in 32 bits.
+// The decode kernel indexes the (sequence, kv head, page) work of a call, plus
+// kDecodeUnitCost slots per unit, in 32 bits.
 static bool decode_size_ok(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
-  return (int64_t)batch * num_kv_heads * (((int64_t)max_seq_len + kPageSize - 1) / kPageSize) <= (int64_t)1 << 30;
+  const int64_t slots = ((int64_t)max_seq_len + kPageSize - 1) / kPageSize + kDecodeUnitCost;
+  return (int64_t)batch * num_kv_heads * slots <= (int64_t)1 << 30;
 }
 
 NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * tid + i;
     const int len = b < B ? min(p.seq_lens[b], p.max_seq_len) : 0;
-    pg[i] = len > 0 ? (len + kPageSize - 1) / kPageSize : 0;
+    pg[i] = len > 0 ? (len + kPageSize - 1) / kPageSize + kDecodeUnitCost : 0;  // slots of one unit
     local += pg[i];
   }
   int incl = local;
@@ -243,12 +243,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  int wave_off = 0, total_pages = 0;
+  int wave_off = 0, total_slots = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
     const int v = uni(s_wsum[i]);
     wave_off += i < wave ? v : 0;
-    total_pages += v;
+    total_slots += v;
   }
   {
     int excl = wave_off + incl - local;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       if (b < B) s_pref[b] = excl;
       excl += pg[i];
     }
-    if (tid == 0) s_pref[B] = total_pages;
+    if (tid == 0) s_pref[B] = total_slots;
   }
   __syncthreads();
 
@@ -268,12 +268,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       for (int e = tid; e < p.Hq * kHeadDim; e += kThreads) p.out[(int64_t)b * p.Hq * kHeadDim + e] = 0.0f;
   }
 
-  // ---- this workgroup's share [x0, x1) of the flattened (unit, page) work
-  // (the host keeps H * total pages <= 2^30, so this index space fits in 32 bits)
-  const uint32_t T = (uint32_t)(H * total_pages);
+  // ---- this workgroup's share [x0, x1) of the flattened work.  Unit u = b*H+h
+  // occupies kDecodeUnitCost + pages_b slots from S_u: the first slots stand
+  // for the fixed cost of a unit segment (Q, pipeline fill, merges), page k is
+  // slot S_u + kDecodeUnitCost + k, so shares balance cost, not just pages.
+  // (The host keeps this index space below 2^30.)
+  const uint32_t T = (uint32_t)(H * total_slots);
   if (T == 0) return;
-  uint32_t W = (T + p.num_groups - 1) / (uint32_t)p.num_groups;
-  W = (W + kWaves - 1) / kWaves * kWaves;
+  const uint32_t W = (T + p.num_groups - 1) / (uint32_t)p.num_groups;
   const uint32_t x0 = (uint32_t)wg * W;
   if (x0 >= T) return;
   const uint32_t x1 = min(x0 + W, T);
@@ -286,19 +288,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   int b = lo_b;
   int pref_b = uni(s_pref[b]);
-  int pages_b = uni(s_pref[b + 1]) - pref_b;
-  int h = (int)((x0 - (uint32_t)(H * pref_b)) / (uint32_t)pages_b);
+  int slots_b = uni(s_pref[b + 1]) - pref_b;
+  int h = (int)((x0 - (uint32_t)(H * pref_b)) / (uint32_t)slots_b);
   uint32_t x = x0;
-  while (true) {
+  for (;; x = (uint32_t)(H * pref_b + h * slots_b) + slots_b) {  // x: first slot of the next unit
+    if (x >= x1) break;
+    if (x > x0) {  // move to the unit that starts at x
+      if (++h == H) {
+        h = 0;
+        do {
+          ++b;
+          pref_b = uni(s_pref[b]);
+          slots_b = uni(s_pref[b + 1]) - pref_b;
+        } while (slots_b == 0);
+      }
+    }
+    const int pages_b = slots_b - kDecodeUnitCost;
+    const uint32_t S_u = (uint32_t)(H * pref_b + h * slots_b) + kDecodeUnitCost;  // slot of page 0
+    const int seg_begin = x > S_u ? (int)(x - S_u) : 0;
+    const int seg_end = x1 > S_u ? (int)min((uint32_t)pages_b, x1 - S_u) : 0;
+    if (seg_end <= seg_begin) continue;  // the share holds only this unit's overhead slots
+
     // Lane indices pass through an empty asm at every segment, so addresses
     // derived from them are recomputed here instead of being hoisted out of
     // the segment loop and spilled across the page loop.
     int et = tid;
     asm volatile("" : "+v"(et));
     const int el = et & 63, er = et & 15, eq = (et >> 4) & 3;
-    const uint32_t S_u = (uint32_t)(H * pref_b + h * pages_b);  // unit start in the flat order
-    const int seg_begin = (int)(x - S_u);
-    const int seg_end = (int)min((uint32_t)pages_b, x1 - S_u);
 
     // The segment's independent loads go out together: Q, the first chunk's
     // page indices and the sequence length.
@@ -320,6 +336,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int len_v = __builtin_amdgcn_raw_buffer_load_b32(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p.seq_lens), 0, 4 * B, kBufferFlags), 4 * b, 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // all of them in flight before Q is used
+
+    const LaneOffsets lo{er * 64 + eq * 16, er * 8 + eq * 2, el * 16, (er >> 1) * 16 + eq * 4};
+    auto page_of = [&](int j) {
+      return j < 64 ? __builtin_amdgcn_readlane(pidx0, j) : __builtin_amdgcn_readlane(pidx1, j - 64);
+    };
+    auto load_mine = [&](int j) { return load_page<kPlane>(p, planes, page_of(min(j, n_mine - 1)), h, lo); };
+    // the first page's loads go out before the Q conversion below
+    PageRegs A;
+    if (n_mine > 0) A = load_mine(0);
+    __builtin_amdgcn_sched_barrier(0);
+
     float qv[32];
     widen_q<QF32>(q_raw, qv);
     float qmax = 0.0f;
@@ -438,12 +465,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   #undef NVFP4_PV_STEP
     };
 
-    const LaneOffsets lo{er * 64 + eq * 16, er * 8 + eq * 2, el * 16, (er >> 1) * 16 + eq * 4};
     while (true) {
-      auto page_of = [&](int j) {
-        return j < 64 ? __builtin_amdgcn_readlane(pidx0, j) : __builtin_amdgcn_readlane(pidx1, j - 64);
-      };
-      auto load_mine = [&](int j) { return load_page<kPlane>(p, planes, page_of(min(j, n_mine - 1)), h, lo); };
       // valid tokens of page j (0 for a page index outside the cache): uniform
       auto valid_of = [&](int j) {
         return (unsigned)page_of(j) < (unsigned)p.num_pages ? min(kPageSize, seq_len - (c0 + wave + kWaves * j) * kPageSize)
@@ -453,7 +475,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // its use and refilled right after, so no register copy waits on a load in
       // flight (loads past the last page re-read that page).
       if (n_mine > 0) {
-        PageRegs A = load_mine(0);
         for (int j = 0; j < n_mine; j += 2) {
           const PageRegs Bp = load_mine(j + 1);
           __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any work on the current page
@@ -472,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       rs_bt = chunk_rsrc(c1);
       pidx0 = __builtin_amdgcn_raw_buffer_load_b32(rs_bt, 4 * (c0 + wave + kWaves * el), 0, 0);
       pidx1 = __builtin_amdgcn_raw_buffer_load_b32(rs_bt, 4 * (c0 + wave + kWaves * (el + 64)), 0, 0);
+      if (n_mine > 0) A = load_mine(0);
     }
 
     // ---- per-wave totals: the sum over the 4 token groups
@@ -547,17 +569,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     __syncthreads();  // LDS is reused by the next segment
 
-    // ---- next unit of the share
-    x = S_u + seg_end;
-    if (x >= x1) break;
-    if (++h == H) {
-      h = 0;
-      do {
-        ++b;
-        pref_b = uni(s_pref[b]);
-        pages_b = uni(s_pref[b + 1]) - pref_b;
-      } while (pages_b == 0);
-    }
   }
 }
 

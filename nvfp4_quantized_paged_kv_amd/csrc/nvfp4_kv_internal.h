@@ -59,6 +59,10 @@ struct DecodeParams {
 };
 
 constexpr int kMaxDecodeBatch = 4096;  // sequences per decode call (prefix sums kept in LDS)
+// Decode work balancing: each (sequence, kv head) unit counts as this many
+// extra pages, the fixed cost of processing a unit piece (Q setup, pipeline
+// fill, merges), so a share of many short units holds fewer pages.
+constexpr int kDecodeUnitCost = 48;
 
 // Launch geometry and workspace of a decode call (shared by the workspace
 // query and the launch).  Workspace = counters (B*H int32, padded to 256 B)

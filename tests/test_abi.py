@@ -121,8 +121,8 @@ def test_decode_workspace_size_rules():
     assert nk.decode_workspace_bytes(32, 64, 8, 0) > 0               # counters even for an empty context
     assert nk.decode_workspace_bytes(32, 60, 8, 8192) == 0          # invalid grouping
     assert nk.decode_workspace_bytes(4097, 64, 8, 8192) == 0        # batch limit
-    assert nk.decode_workspace_bytes(4096, 64, 8, 1 << 20) == 0     # 2^31 work items
-    assert nk.decode_workspace_bytes(2048, 64, 8, 1 << 20) > 0      # 2^30 work items
+    assert nk.decode_workspace_bytes(4096, 64, 8, 1 << 20) == 0     # over 2^30 work slots
+    assert nk.decode_workspace_bytes(2000, 64, 8, 1 << 20) > 0      # just under 2^30 work slots
     assert nk.decode_workspace_bytes(1, 96, 8, 2_000_000) > 0        # a long context needs split partials
     # monotone in the context bound for a fixed batch
     sizes = [nk.decode_workspace_bytes(4, 32, 8, n) for n in (1 << 14, 1 << 16, 1 << 18, 1 << 20)]
