@@ -99,7 +99,8 @@ typedef struct nvfp4_kv_layer {
  *                  16-byte aligned base and token stride.  Values must be finite.
  *   slot_mapping : [num_tokens] int32.
  * Slots that appear twice in one call are written by both tokens in an
- * unspecified order.  num_tokens == 0 is a no-op. */
+ * unspecified order.  num_tokens == 0 is a no-op.
+ *   Supported: ceil(num_tokens/16) * num_kv_heads < 2^31. */
 NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
                                                   nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
                                                   const int32_t* slot_mapping, void* stream);

@@ -56,6 +56,8 @@ NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer,
   if (num_tokens == 0) return NVFP4_OK;
   if (!k_new || !v_new || !slot_mapping) return NVFP4_ERR_INVALID_ARGUMENT;
   if (token_stride_elems < (int64_t)layer->num_kv_heads * kHeadDim) return NVFP4_ERR_INVALID_ARGUMENT;
+  // the kernel indexes (group of 16 tokens, kv head) pairs in 31 bits
+  if (((int64_t)num_tokens + 15) / 16 * layer->num_kv_heads >= ((int64_t)1 << 31)) return NVFP4_ERR_UNSUPPORTED;
   const int64_t esize = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || (token_stride_elems * esize) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
   AppendParams p;

@@ -8,9 +8,11 @@
 //
 // One thread owns one 16-value block of one (token, kv head): it reads the 16
 // inputs (32 B bf16 / 64 B f32), so the block's amax needs no cross-lane work,
-// and writes 8 code bytes plus 1 scale byte.  Consecutive threads own
-// consecutive blocks, so both the loads and the stores of a wave are
-// contiguous.
+// and writes 8 code bytes plus 1 scale byte.  Lane order, fastest first: token
+// within a group of 4, block, group of 4 within 16 consecutive tokens, kv head,
+// group of 16 tokens.  Sixteen consecutive tokens usually fill one page, so a
+// 256-lane workgroup writes whole (page, kv head) tiles of two heads: its K and
+// V code runs and its 128-B scale rows are complete lines written by one CU.
 //
 // Exact rounding.  bs = E4M3 nearest to amax/(6g): the float64 quotient of the
 // float32 amax and the exact float64 6g is correctly rounded, and no float64
@@ -27,6 +29,17 @@
 // (global scales are restricted to [2^-100, 2^100], which keeps a_k*g in the
 // float32 normal range).  The magnitude then follows from three comparisons
 // (binary search over the 7 thresholds).
+//
+// Fast path.  The hardware conversion v_cvt_scalef32_pk_fp4_f32 rounds a
+// float32 to the nearest E2M1 code, ties to the even code, saturating at 6.
+// With c_lo < 1/(bs*g) < c_hi (float64 reciprocal scaled by 1 -/+ 2^-21, then
+// rounded to float32), the float32 products satisfy |x|*c_lo < |x|/(bs*g) <
+// |x|*c_hi even after their own rounding.  The code is a nondecreasing step
+// function of the magnitude, so if both products give the same code, that is
+// the code of the exact |x|/(bs*g).  An exact tie lies strictly between the
+// two products and makes their codes differ.  A block where any of the 16
+// pairs differ takes the threshold path above instead (rare: a value within
+// about 2^-21 of a rounding boundary).
 #include "nvfp4_device.h"
 #include "nvfp4_kv_internal.h"
 
@@ -39,6 +52,15 @@ __device__ __forceinline__ float threshold_f32(float a, float g, bool odd) {
   const float pred = __int_as_float(__float_as_int(hi) - 1);
   const bool down = odd ? (lo <= 0.0f) : (lo < 0.0f);
   return down ? pred : hi;
+}
+
+// Values 2Q and 2Q+1, times c_lo and times c_hi, to E2M1 codes in byte Q%4 of
+// word Q/4 of lo and hi (low nibble = value 2Q).
+template <int Q>
+__device__ __forceinline__ void cvt_pair(uint32_t (&lo)[2], uint32_t (&hi)[2], const float (&x)[16], float c_lo,
+                                         float c_hi) {
+  lo[Q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[Q >> 2], x[2 * Q] * c_lo, x[2 * Q + 1] * c_lo, 1.0f, Q & 3);
+  hi[Q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[Q >> 2], x[2 * Q] * c_hi, x[2 * Q + 1] * c_hi, 1.0f, Q & 3);
 }
 
 template <typename InT>
@@ -73,12 +95,11 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p) {
   const int which = blockIdx.y;  // 0 = K, 1 = V
   const AppendTensor& T = p.t[which];
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n_blocks = (int64_t)p.num_tokens * p.H * 8;
-  if (i >= n_blocks) return;
-  const int b = (int)(i & 7);
-  const int64_t row = i >> 3;
-  const int h = (int)(row % p.H);
-  const int64_t t = row / p.H;
+  const int tq = (int)(i & 3), b = (int)((i >> 2) & 7), tg = (int)((i >> 5) & 3);
+  const uint32_t gh = (uint32_t)(i >> 7);  // group of 16 tokens * H + kv head (< 2^31, checked by the host)
+  const int h = (int)(gh % (uint32_t)p.H);
+  const int64_t t = 16 * (int64_t)(gh / (uint32_t)p.H) + 4 * tg + tq;
+  if (t >= p.num_tokens) return;
   const int32_t slot = p.slots[t];
   if (slot < 0 || (int64_t)slot >= (int64_t)p.num_pages * kPageSize) return;
 
@@ -93,26 +114,43 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p) {
   const uint32_t sb = e4m3_encode_rne_sat((double)amax / (6.0 * (double)g));
   const float bs = e4m3_value(sb);
 
-  float u[7];
-  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-#pragma unroll
-  for (int k = 0; k < 7; ++k) u[k] = bs == 0.0f ? __builtin_inff() : threshold_f32(mids[k] * bs, g, (k & 1) != 0);
-
   uint32_t packed[2] = {0u, 0u};
+  bool exact_path = bs == 0.0f;  // zero scale: every code is its sign (threshold path, thresholds +inf)
+  if (!exact_path) {
+    const double rcp = 1.0 / ((double)bs * (double)g);  // bs*g exact in float64
+    const float c_lo = (float)(rcp * (1.0 - 0x1p-21)), c_hi = (float)(rcp * (1.0 + 0x1p-21));
+    uint32_t hi[2] = {0u, 0u};
+    cvt_pair<0>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<1>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<2>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<3>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<4>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<5>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<6>(packed, hi, x, c_lo, c_hi);
+    cvt_pair<7>(packed, hi, x, c_lo, c_hi);
+    exact_path = (packed[0] != hi[0]) | (packed[1] != hi[1]);
+  }
+  if (exact_path) {
+    float u[7];
+    const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float ax = fabsf(x[k]);
-    const bool c2 = ax > u[3];
-    const bool c1 = ax > (c2 ? u[5] : u[1]);
-    const float t0 = c2 ? (c1 ? u[6] : u[4]) : (c1 ? u[2] : u[0]);
-    const bool c0 = ax > t0;
-    const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
-    const uint32_t code = mag | ((__float_as_uint(x[k]) >> 28) & 8u);
-    packed[k >> 3] |= code << (4 * (k & 7));
+    for (int k = 0; k < 7; ++k) u[k] = bs == 0.0f ? __builtin_inff() : threshold_f32(mids[k] * bs, g, (k & 1) != 0);
+    packed[0] = packed[1] = 0u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float ax = fabsf(x[k]);
+      const bool c2 = ax > u[3];
+      const bool c1 = ax > (c2 ? u[5] : u[1]);
+      const float t0 = c2 ? (c1 ? u[6] : u[4]) : (c1 ? u[2] : u[0]);
+      const bool c0 = ax > t0;
+      const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
+      const uint32_t code = mag | ((__float_as_uint(x[k]) >> 28) & 8u);
+      packed[k >> 3] |= code << (4 * (k & 7));
+    }
   }
 
-  const int64_t page = slot / kPageSize;
-  const int o = slot % kPageSize;
+  const int64_t page = (uint32_t)slot / kPageSize;  // slot >= 0 here
+  const int o = (int)((uint32_t)slot % kPageSize);
   const int64_t tile = page * p.H + h;
   if (which == 0) {
     *reinterpret_cast<uint2*>(T.codes + tile * kTileCodeBytes + o * 64 + 8 * b) = make_uint2(packed[0], packed[1]);
@@ -128,7 +166,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p) {
 }  // namespace
 
 hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream) {
-  const int64_t n_blocks = (int64_t)p.num_tokens * p.H * 8;
+  const int64_t n_blocks = (int64_t)((p.num_tokens + 15) / 16) * 16 * p.H * 8;  // tokens rounded up to groups of 16
   if (n_blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_blocks + 255) / 256), 2, 1);
   if (dtype == NVFP4_DTYPE_BF16)
