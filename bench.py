@@ -30,6 +30,9 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s) + quantize-append GB/s"
+# GPU spin (torch.cuda._sleep, clock cycles, about 0.5 ms) queued ahead of a
+# per-kernel event pair: the host-side call is hidden behind it
+SLEEP_CYCLES = 1 << 20
 
 
 def parse():
@@ -187,20 +190,27 @@ def bench_mixed(args, wl, dev):
     sm = 1 / math.sqrt(128)
 
     def step(l, ev=None):
+        # with ev: each kernel sits between its own event pair, preceded by a GPU
+        # sleep that covers the host-side call, so the pair brackets only the kernel
         st = steps[l]
         if ev is not None:
+            torch.cuda._sleep(SLEEP_CYCLES)
             ev[0].record(stream)
         nk.quantize_append(st.filled.layer, st.new_k, st.new_v, st.new_slots)
         if ev is not None:
             ev[1].record(stream)
+            torch.cuda._sleep(SLEEP_CYCLES)
+            ev[2].record(stream)
         nk.dequant_to_fp8_workspace(st.filled.layer, st.ext_table, st.ext_prefix, st.ext_offsets, st.max_prefix,
                                     6 * st.filled.layer.k_global, 6 * st.filled.layer.v_global, ws_k, ws_v)
         if ev is not None:
-            ev[2].record(stream)
+            ev[3].record(stream)
+            torch.cuda._sleep(SLEEP_CYCLES)
+            ev[4].record(stream)
         nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
                              workspace=dws)
         if ev is not None:
-            ev[3].record(stream)
+            ev[5].record(stream)
 
     for i in range(args.warmup):
         step(i % L)
@@ -210,14 +220,14 @@ def bench_mixed(args, wl, dev):
         step(i % L)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i % L, evs[i])
     torch.cuda.synchronize()
     app = np.array([e[0].elapsed_time(e[1]) for e in evs]) / 1e3
-    wsd = np.array([e[1].elapsed_time(e[2]) for e in evs]) / 1e3
-    dec = np.array([e[2].elapsed_time(e[3]) for e in evs]) / 1e3
+    wsd = np.array([e[2].elapsed_time(e[3]) for e in evs]) / 1e3
+    dec = np.array([e[4].elapsed_time(e[5]) for e in evs]) / 1e3
     b_step = b_app + b_ws + b_dec
     achieved = b_dec / dec.mean() / 1e9
     kernel_file = os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", "decode_attn.hip")
@@ -324,14 +334,19 @@ def main():
     bytes_step = bytes_append_step + bytes_decode
 
     def step(l, ev=None):
+        # with ev: each kernel sits between its own event pair, preceded by a GPU
+        # sleep that covers the host-side call, so the pair brackets only the kernel
         if ev is not None:
+            torch.cuda._sleep(SLEEP_CYCLES)
             ev[0].record(stream)
         nk.quantize_append(layers[l], newk[l], newv[l], slots_new[l])
         if ev is not None:
             ev[1].record(stream)
+            torch.cuda._sleep(SLEEP_CYCLES)
+            ev[2].record(stream)
         nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
         if ev is not None:
-            ev[2].record(stream)
+            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i % L)
@@ -347,13 +362,13 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     # ---- same steps again with HIP events on the launch stream (per-call durations)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i % L, evs[i])
     torch.cuda.synchronize()
     app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     dec_avg_s = float(dec_ms.mean()) / 1e3
     achieved = bytes_decode / dec_avg_s / 1e9
 
@@ -367,8 +382,10 @@ def main():
     for i in range(max(5, min(args.steps, 20))):
         l = i % L
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tab = tables[l][:n_ext].contiguous()
+        torch.cuda._sleep(SLEEP_CYCLES)
         e0.record(stream)
-        nk.dequant_to_fp8_workspace(layers[l], tables[l][:n_ext].contiguous(), prefix, offs, ctx,
+        nk.dequant_to_fp8_workspace(layers[l], tab, prefix, offs, ctx,
                                     6 * layers[l].k_global, 6 * layers[l].v_global, ws_k, ws_v)
         e1.record(stream)
         torch.cuda.synchronize()

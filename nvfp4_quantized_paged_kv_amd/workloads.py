@@ -40,6 +40,9 @@ def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device
         slots = (bt[seq, pos // synth.PAGE].astype(np.int64) * synth.PAGE + pos % synth.PAGE).astype(np.int32)
         sl = torch.from_numpy(slots).to(device)
         if timed:
+            # keep the GPU busy while the host prepares the launch, so the
+            # events bracket the kernel and not the host-side call overhead
+            torch.cuda._sleep(1 << 20)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         quantize_append(layer, k, v, sl)
