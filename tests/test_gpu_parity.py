@@ -212,6 +212,27 @@ def test_decode_workspace_reuse_and_counters():
         assert torch.equal(o, outs[0])
 
 
+@pytest.mark.parametrize("seed", [7, 8])
+def test_decode_ragged_many_units(seed):
+    """A ragged batch whose work shares start and end everywhere: empty and
+    one-token sequences between long ones, lengths on and off page boundaries,
+    units much shorter than a share (many per workgroup) and units split over
+    several workgroups; the output is checked row by row against the oracle."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.choice([0, 1, 15, 16, 17, 33, 250, 511, 1024, 3000, 9000], size=40)]
+    lens[0], lens[-1] = 0, 1
+    H, G = 4, 6
+    _say(f"case: decode ragged many units seed={seed} lens={lens}")
+    c = build_cache(lens, H, torch.bfloat16, "sparse6", 0.003, False, seed=seed)
+    got, ref = decode_both(c, H * G, torch.bfloat16, seed=seed)
+    err = row_rel_err(got, ref)
+    assert err.max() <= ATTN_TOL, (err.max(), np.argmax(err))
+    # empty sequences give zeros
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert not got.reshape(len(lens), H * G, 128)[b].any()
+
+
 # ------------------------------------------------------- FP8 workspace dequant
 
 
