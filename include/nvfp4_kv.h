@@ -133,7 +133,7 @@ NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q
  *                  first use; every call leaves the counters at zero again.
  *                  Calls that share a workspace must be ordered on one stream.
  *   Supported: batch <= 4096 and
- *              batch * num_kv_heads * (ceil(max_seq_len/16) + 48) <= 2^30. */
+ *              batch * num_kv_heads * (ceil(max_seq_len/16) + 96) <= 2^30. */
 NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
                                                  int32_t batch, int32_t num_q_heads, const int32_t* block_table,
                                                  int32_t block_table_stride, const int32_t* seq_lens,

@@ -62,7 +62,10 @@ constexpr int kMaxDecodeBatch = 4096;  // sequences per decode call (prefix sums
 // Decode work balancing: each (sequence, kv head) unit counts as this many
 // extra pages, the fixed cost of processing a unit piece (Q setup, pipeline
 // fill, merges), so a share of many short units holds fewer pages.
-constexpr int kDecodeUnitCost = 48;
+#ifndef NVFP4_DECODE_UNIT_COST
+#define NVFP4_DECODE_UNIT_COST 96
+#endif
+constexpr int kDecodeUnitCost = NVFP4_DECODE_UNIT_COST;
 
 // Launch geometry and workspace of a decode call (shared by the workspace
 // query and the launch).  Workspace = counters (B*H int32, padded to 256 B)
