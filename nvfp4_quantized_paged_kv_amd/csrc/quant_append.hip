@@ -90,22 +90,9 @@ __device__ __forceinline__ void load_block<float>(const float* src, float (&x)[1
   }
 }
 
-template <typename InT>
-__global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p) {
-  const int which = blockIdx.y;  // 0 = K, 1 = V
-  const AppendTensor& T = p.t[which];
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int tq = (int)(i & 3), b = (int)((i >> 2) & 7), tg = (int)((i >> 5) & 3);
-  const uint32_t gh = (uint32_t)(i >> 7);  // group of 16 tokens * H + kv head (< 2^31, checked by the host)
-  const int h = (int)(gh % (uint32_t)p.H);
-  const int64_t t = 16 * (int64_t)(gh / (uint32_t)p.H) + 4 * tg + tq;
-  if (t >= p.num_tokens) return;
-  const int32_t slot = p.slots[t];
-  if (slot < 0 || (int64_t)slot >= (int64_t)p.num_pages * kPageSize) return;
-
-  float x[16];
-  load_block<InT>(reinterpret_cast<const InT*>(T.x) + t * p.token_stride + (int64_t)h * kHeadDim + 16 * b, x);
-
+// Quantize one 16-value block x and store its codes and scale byte at `slot`.
+__device__ __forceinline__ void quantize_store(const float (&x)[16], const AppendTensor& T, const AppendParams& p,
+                                               int which, int32_t slot, int h, int b) {
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
@@ -163,16 +150,68 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p) {
   }
 }
 
+// Block index i of the flattened work -> (token t, kv head h, block b); t < 0 if past the end.
+__device__ __forceinline__ void block_coords(int64_t i, const AppendParams& p, int64_t& t, int& h, int& b) {
+  const int tq = (int)(i & 3), tg = (int)((i >> 5) & 3);
+  b = (int)((i >> 2) & 7);
+  const uint32_t gh = (uint32_t)(i >> 7);  // group of 16 tokens * H + kv head (< 2^31, checked by the host)
+  h = (int)(gh % (uint32_t)p.H);
+  t = 16 * (int64_t)(gh / (uint32_t)p.H) + 4 * tg + tq;
+  if (t >= p.num_tokens) t = -1;
+}
+
+// Each thread takes R blocks, n_threads apart in the flattened order (so every
+// pass keeps the page-tile lane pattern); all of their loads are issued before
+// any of them is quantized.  R = 2 for bulk appends (more bytes in flight per
+// wave), R = 1 for small ones, where the per-thread chain is the latency.
+template <typename InT, int R>
+__global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p, int64_t n_threads) {
+  const int which = blockIdx.y;  // 0 = K, 1 = V
+  const AppendTensor& T = p.t[which];
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i0 >= n_threads) return;
+  float x[R][16];
+  int32_t slot[R];
+  int h[R], b[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    int64_t t;
+    block_coords(i0 + k * n_threads, p, t, h[k], b[k]);
+    slot[k] = t >= 0 ? p.slots[t] : -1;
+    if (slot[k] < 0 || (int64_t)slot[k] >= (int64_t)p.num_pages * kPageSize) {
+      slot[k] = -1;
+      t = 0;  // load token 0 (in range) and skip the store
+    }
+    load_block<InT>(reinterpret_cast<const InT*>(T.x) + t * p.token_stride + (int64_t)h[k] * kHeadDim + 16 * b[k], x[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k)
+    if (slot[k] >= 0) quantize_store(x[k], T, p, which, slot[k], h[k], b[k]);
+}
+
+// blocks (16 values of one token and head) from which an append counts as bulk
+constexpr int64_t kAppendBulkBlocks = 1 << 18;
+
 }  // namespace
 
 hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream) {
   const int64_t n_blocks = (int64_t)((p.num_tokens + 15) / 16) * 16 * p.H * 8;  // tokens rounded up to groups of 16
   if (n_blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n_blocks + 255) / 256), 2, 1);
-  if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(quantize_append_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
+  // threads per pass, a multiple of 128 (one 16-token group of one head) so
+  // every pass starts on a group boundary
+  const bool bulk = n_blocks >= kAppendBulkBlocks;
+  const int r = bulk ? 2 : 1;
+  const int64_t n_threads = (n_blocks / 128 + r - 1) / r * 128;
+  const dim3 grid((unsigned)((n_threads + 255) / 256), 2, 1);
+  const bool bf16 = dtype == NVFP4_DTYPE_BF16;
+  if (bf16 && bulk)
+    hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 2>), grid, dim3(256), 0, stream, p, n_threads);
+  else if (bf16)
+    hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, p, n_threads);
+  else if (bulk)
+    hipLaunchKernelGGL((quantize_append_kernel<float, 2>), grid, dim3(256), 0, stream, p, n_threads);
   else
-    hipLaunchKernelGGL(quantize_append_kernel<float>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((quantize_append_kernel<float, 1>), grid, dim3(256), 0, stream, p, n_threads);
   return hipGetLastError();
 }
 
