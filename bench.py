@@ -30,9 +30,14 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s) + quantize-append GB/s"
-# GPU spin (torch.cuda._sleep, clock cycles, about 0.5 ms) queued ahead of a
-# per-kernel event pair: the host-side call is hidden behind it
-SLEEP_CYCLES = 1 << 20
+# GPU spin (torch.cuda._sleep, clock cycles, about 0.1 ms) queued ahead of a
+# per-kernel event pair: the host-side call (10-20 us) is hidden behind it.
+# Kept short: after a long near-idle spin the GPU runs the next kernels slower
+# while its clocks ramp back up.
+SLEEP_CYCLES = 1 << 18
+# Back-to-back windows: calls queued (untimed) ahead of each timed window, and windows per measurement
+LEAD_CALLS = 16
+WINDOWS = 3
 
 
 def parse():
@@ -51,12 +56,51 @@ def parse():
     return ap.parse_args()
 
 
-def src_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_file: str, workload: str):
+# The decode kernel's source: the kernel file and the two headers it includes.
+DECODE_SOURCES = [os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", n)
+                  for n in ("decode_attn.hip", "nvfp4_kv_internal.h", "nvfp4_device.h")]
+
+
+def back_to_back(stream, n, launch):
+    """Per-call GPU time of n calls queued back to back between one event pair
+    on `stream`: the median over WINDOWS windows.  Each window is led by
+    LEAD_CALLS untimed calls, so the GPU is already busy with the same work
+    (no idle gap, no clock ramp) when the first event is taken and the host
+    queues the timed calls while earlier ones run.  Warns on stderr if the host
+    took longer to queue a window than the GPU took to run it."""
+    import numpy as np
+    import torch
+    per_call = []
+    for w in range(WINDOWS):
+        torch.cuda.synchronize()
+        for i in range(LEAD_CALLS):
+            launch(i)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        t0 = time.perf_counter()
+        for i in range(n):
+            launch(LEAD_CALLS + i)
+        host_s = time.perf_counter() - t0
+        d1.record(stream)
+        torch.cuda.synchronize()
+        gpu_s = d0.elapsed_time(d1) / 1e3
+        if host_s > gpu_s:
+            print(f"[bench] warning: queueing {n} calls took {host_s * 1e3:.2f} ms, longer than their "
+                  f"{gpu_s * 1e3:.2f} ms on the GPU; the back-to-back time includes host gaps", file=sys.stderr)
+        per_call.append(gpu_s / n)
+    return float(np.median(per_call))
+
+
+def read_traffic(kernel_files, workload: str):
     """HBM traffic per decode call from a committed rocprofv3 PMC summary, if it
     was taken on the current kernel source; else None."""
     prof = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.txt")
@@ -68,7 +112,7 @@ def read_traffic(kernel_file: str, workload: str):
             if ":" in ln and not ln.startswith("#"):
                 k, v = ln.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != src_hash(kernel_file):
+    if vals.get("kernel_source_sha256_16") != src_hash(kernel_files):
         return None
     try:
         return float(vals["hbm_bytes_per_call"])
@@ -229,20 +273,13 @@ def bench_mixed(args, wl, dev):
     wsd = np.array([e[2].elapsed_time(e[3]) for e in evs]) / 1e3
     dec = np.array([e[4].elapsed_time(e[5]) for e in evs]) / 1e3
     # decode calls back to back between one event pair (the roofline's per-launch duration)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(SLEEP_CYCLES)
-    d0.record(stream)
-    for i in range(args.steps):
+    def dec_call(i):
         st = steps[i % L]
         nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
                              workspace=dws)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dec_b2b = d0.elapsed_time(d1) / 1e3 / args.steps
+    dec_b2b = back_to_back(stream, args.steps, dec_call)
     b_step = b_app + b_ws + b_dec
     achieved = b_dec / dec_b2b / 1e9
-    kernel_file = os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", "decode_attn.hip")
     return {
         "value": round(b_step / (wall / args.steps) / 1e9, 2),
         "ms_per_step": round(wall * 1e3 / args.steps, 5),
@@ -262,7 +299,7 @@ def bench_mixed(args, wl, dev):
         "quantize_append_bulk_gbs": round(sum(append_bytes) / (sum(append_ms) / 1e3) / 1e9, 2),
         "bytes_per_step": int(b_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(kernel_file, wl.name),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(DECODE_SOURCES, wl.name),
                      "kernel": "nvfp4_paged_decode_attn", "algorithmic_bytes_per_call": int(b_dec)},
     }
 
@@ -385,16 +422,10 @@ def main():
 
     # ---- decode calls back to back between one event pair (the roofline's
     # per-launch duration: no per-call event or dispatch overhead inside it)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(SLEEP_CYCLES)
-    d0.record(stream)
-    for i in range(args.steps):
+    def dec_call(i):
         l = i % L
         nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dec_avg_s = d0.elapsed_time(d1) / 1e3 / args.steps
+    dec_avg_s = back_to_back(stream, args.steps, dec_call)
     achieved = bytes_decode / dec_avg_s / 1e9
 
     # ---- FP8 workspace dequant on the same cache: 8 sequences' full prefixes (extend path)
@@ -420,8 +451,7 @@ def main():
 
     app_total_b = float(sum(append_bytes))
     app_total_s = float(sum(append_ms)) / 1e3
-    kernel_file = os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", "decode_attn.hip")
-    traffic = read_traffic(kernel_file, wl.name)
+    traffic = read_traffic(DECODE_SOURCES, wl.name)
 
     result = {
         "metric": METRIC,
