@@ -67,6 +67,11 @@ def lib():
     L.nvfp4o_decode_attention.restype = None
     L.nvfp4o_fp8_workspace.argtypes = [_u8p, _u8p, _int, _int, _flt, _i32p, _int, _int, _i32p, _i32p, _flt, _u8p]
     L.nvfp4o_fp8_workspace.restype = None
+    L.nvfp4o_fp8_quantize_rows.argtypes = [_f32p, _i64, _i64, _int, _i32p, _flt, _u8p]
+    L.nvfp4o_fp8_quantize_rows.restype = None
+    L.nvfp4o_extend_attention.argtypes = [_u8p, _u8p, _int, _flt, _flt, _f32p, _int, _int, _i32p, _i32p, _i32p, _flt,
+                                          _i64p, _i64, _f64p]
+    L.nvfp4o_extend_attention.restype = None
     L.nvfp4o_page_mode_dequant.argtypes = [_f64p, _i64, _i64, _f64p]
     L.nvfp4o_page_mode_dequant.restype = None
     L.nvfp4o_bytes_per_token_head.argtypes = []
@@ -183,6 +188,41 @@ def fp8_workspace(planes: Planes, is_v: bool, g: float, block_table, prefix_lens
     lib().nvfp4o_fp8_workspace(cp, sp, int(bool(is_v)), planes.H, float(np.float32(g)), bt, bt.shape[1], pl.size,
                                pl, wo, float(np.float32(ws_scale)), out)
     return out.reshape(int(total_tokens), planes.H, 128)
+
+
+def fp8_quantize_rows(x: np.ndarray, rows, ws_scale: float, ws: np.ndarray) -> None:
+    """Store x [T, H, 128] (float32 values) as E4M3 into ws [capacity, H, 128] uint8 at ws rows `rows` (in place)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T, H, D = x.shape
+    assert D == 128 and ws.dtype == np.uint8 and ws.flags.c_contiguous and ws.shape[1:] == (H, 128)
+    r = np.ascontiguousarray(rows, dtype=np.int32)
+    assert r.size == T and (r < ws.shape[0]).all()
+    lib().nvfp4o_fp8_quantize_rows(x, T, H * 128, H, r, float(np.float32(ws_scale)), ws.reshape(-1))
+
+
+def extend_attention(ws_k: np.ndarray, ws_v: np.ndarray, k_ws_scale: float, v_ws_scale: float, q: np.ndarray,
+                     q_offsets, ws_offsets, prefix_lens, sm_scale: float, rows=None) -> np.ndarray:
+    """q: float32 [Tq, Hq, 128]; ws_k/ws_v: uint8 [capacity, H, 128]; rows: flat indices qrow*Hq + qh.
+
+    Returns float64 [len(rows), 128]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    Tq, Hq, D = q.shape
+    H = ws_k.shape[1]
+    assert D == 128 and Hq % H == 0 and ws_k.shape == ws_v.shape
+    qo = np.ascontiguousarray(q_offsets, dtype=np.int32)
+    wo = np.ascontiguousarray(ws_offsets, dtype=np.int32)
+    pl = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+    n = pl.size
+    assert qo.size == n + 1 and wo.size >= n and qo[-1] == Tq
+    assert all(wo[i] + pl[i] + (qo[i + 1] - qo[i]) <= ws_k.shape[0] for i in range(n))
+    if rows is None:
+        rows = np.arange(Tq * Hq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, 128), np.float64)
+    lib().nvfp4o_extend_attention(np.ascontiguousarray(ws_k).reshape(-1), np.ascontiguousarray(ws_v).reshape(-1), H,
+                                  float(np.float32(k_ws_scale)), float(np.float32(v_ws_scale)), q, Hq, n, qo, wo, pl,
+                                  float(np.float32(sm_scale)), rows, rows.size, out)
+    return out
 
 
 # ------------------------------------------------------ the page experiment

@@ -306,6 +306,79 @@ void nvfp4o_fp8_workspace(const uint8_t* code_plane, const uint8_t* scale_plane,
   }
 }
 
+/* ------------------------------------------------ FP8 rows of a new chunk
+ * [MW] §3, first and second data flows: the K/V of the tokens being
+ * prefilled or extended take part in attention as FP8 (only the cached prefix
+ * goes through the NVFP4 -> FP8 workspace).  Reading: they are stored into
+ * workspace rows with the workspace's own per-tensor scale, by the same
+ * rounding as above (E4M3 nearest to |x| / ws_scale, ties to even, saturating
+ * at 448; sign bit of x).  x is n_tokens x stride floats, token t's head h
+ * at x[t*stride + h*128]; rows[t] < 0 skips token t. */
+void nvfp4o_fp8_quantize_rows(const float* x, int64_t n_tokens, int64_t stride, int Hkv, const int32_t* rows,
+                              float ws_scale, uint8_t* ws) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    if (rows[t] < 0) continue;
+    for (int h = 0; h < Hkv; ++h)
+      for (int d = 0; d < 128; ++d) {
+        double xv = (double)x[t * stride + h * 128 + d];
+        int byte = nvfp4o_e4m3_encode(fabs(xv) / (double)ws_scale);
+        if (signbit(xv)) byte |= 0x80;
+        ws[((int64_t)rows[t] * Hkv + h) * 128 + d] = (uint8_t)byte;
+      }
+  }
+}
+
+/* ------------------------------------------ extend attention over FP8 rows
+ * [MW] §3 second data flow (chunked prefill / extend): the chunk's queries
+ * attend over the cached prefix, read from the FP8 workspace, and over the
+ * chunk itself, causally as in prefill ([MW] §3 first data flow; the chunk's
+ * K/V are FP8 rows after the prefix, see nvfp4o_fp8_quantize_rows).
+ * Sequence i: prefix P_i = prefix_lens[i], chunk C_i = q_offsets[i+1] -
+ * q_offsets[i]; its K/V rows are ws_offsets[i] + t, t < P_i + C_i.  Query
+ * token j < C_i (row q_offsets[i] + j of q) sits at position P_i + j and sees
+ * keys t <= P_i + j.  For query head qh, kv head h = qh / (Hq/Hkv) ([MW] §1):
+ *   s_t = sm_scale * sum_d q[d] * E4M3(ws_k[row_t][h][d]) * k_ws_scale
+ *   o   = sum_t softmax(s)_t * E4M3(ws_v[row_t][h][d]) * v_ws_scale
+ * in float64.  rows[r] = (query row) * Hq + qh selects the outputs computed;
+ * out is n_rows x 128. */
+void nvfp4o_extend_attention(const uint8_t* ws_k, const uint8_t* ws_v, int Hkv, float k_ws_scale, float v_ws_scale,
+                             const float* q, int Hq, int num_seqs, const int32_t* q_offsets,
+                             const int32_t* ws_offsets, const int32_t* prefix_lens, float sm_scale,
+                             const int64_t* rows, int64_t n_rows, double* out) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t qrow = rows[r] / Hq;
+    const int qh = (int)(rows[r] % Hq), h = qh / G;
+    int i = 0;
+    while (i < num_seqs - 1 && q_offsets[i + 1] <= qrow) ++i; /* the sequence holding this query row */
+    const int64_t j = qrow - q_offsets[i];
+    const int64_t n = (int64_t)prefix_lens[i] + j + 1; /* keys 0 .. P_i + j */
+    const float* qv = q + rows[r] * 128;
+    double* o = out + r * 128;
+    double* s = (double*)malloc((size_t)n * sizeof(double));
+    double m = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+      const uint8_t* kr = ws_k + (((int64_t)ws_offsets[i] + t) * Hkv + h) * 128;
+      double acc = 0.0;
+      for (int d = 0; d < 128; ++d) acc += (double)qv[d] * (nvfp4o_e4m3_value(kr[d]) * (double)k_ws_scale);
+      s[t] = (double)sm_scale * acc;
+      if (s[t] > m) m = s[t];
+    }
+    for (int d = 0; d < 128; ++d) o[d] = 0.0;
+    double l = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+      const uint8_t* vr = ws_v + (((int64_t)ws_offsets[i] + t) * Hkv + h) * 128;
+      const double pt = exp(s[t] - m);
+      l += pt;
+      for (int d = 0; d < 128; ++d) o[d] += pt * (nvfp4o_e4m3_value(vr[d]) * (double)v_ws_scale);
+    }
+    free(s);
+    for (int d = 0; d < 128; ++d) o[d] /= l;
+  }
+}
+
 /* --------------------------------------------------- the page's experiment
  * [MW] §2 stdlib experiment, reproduced operation for operation: per block of
  * `block` values, scale = amax/6 (1.0 when amax <= 1e-12, no rounding, no
