@@ -8,10 +8,11 @@
  * scaling, and section 1 for the 9/16 byte accounting; cloud.tencent.com.cn
  * "NVFP4: breaking the memory wall of GPU inference", E2M1 encoding section).
  *
- * The three entry points are the three cache data flows of section 3 of the
- * same blog: quantize-on-write of new K/V, decode attention that dequantizes
- * inside the kernel, and extend-path dequantization into one FP8 workspace
- * that is reused across layers.
+ * The entry points follow the cache data flows of section 3 of the same blog:
+ * quantize-on-write of new K/V, decode attention that dequantizes inside the
+ * kernel, extend-path dequantization into one FP8 workspace that is reused
+ * across layers, and the FP8 attention of an extend / prefill chunk over that
+ * workspace (with the chunk's own K/V stored as FP8 rows).
  *
  * Conventions for every function
  *   - All array arguments are DEVICE pointers unless marked "host".  The caller
@@ -162,6 +163,60 @@ NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* 
                                                         int32_t max_prefix_len, float k_ws_scale, float v_ws_scale,
                                                         uint8_t* ws_k, uint8_t* ws_v, int32_t ws_capacity_tokens,
                                                         void* stream);
+
+/* FP8 rows of new tokens (blog section 3, first and second data flows: the
+ * K/V of the tokens being prefilled or extended take part in attention as FP8;
+ * only the cached prefix goes through the NVFP4 -> FP8 workspace).  Typical
+ * use: an extend chunk's K/V go into the workspace rows right after its
+ * prefix, with the workspace's own scales.  For token t < num_tokens with
+ * 0 <= ws_rows[t] < ws_capacity_tokens, KV head h and dim d:
+ *   ws_k[ws_rows[t]][h][d] = sign(x) | E4M3 nearest to |x| / k_ws_scale
+ *   (x = k_new[t][h][d]; ties to even, saturating at 448: the rounding of
+ *   nvfp4_dequant_to_fp8_workspace), and likewise ws_v from v_new.
+ *   k_new, v_new : [num_tokens][num_kv_heads][128] of dtype, token stride
+ *                  token_stride_elems >= num_kv_heads*128; 16-byte aligned
+ *                  pointers and token rows.
+ *   ws_rows      : [num_tokens] int32; other rows (< 0 or past the capacity)
+ *                  are skipped.
+ *   ws_k, ws_v   : [ws_capacity_tokens][num_kv_heads][128] uint8, 16-byte aligned.
+ *   Non-finite inputs give unspecified bytes (written in bounds). */
+NVFP4_API nvfp4_status_t nvfp4_fp8_rows_to_workspace(const void* k_new, const void* v_new, nvfp4_dtype_t dtype,
+                                                     int32_t num_tokens, int64_t token_stride_elems,
+                                                     int32_t num_kv_heads, const int32_t* ws_rows, float k_ws_scale,
+                                                     float v_ws_scale, uint8_t* ws_k, uint8_t* ws_v,
+                                                     int32_t ws_capacity_tokens, void* stream);
+
+/* Causal attention of extend (or prefill) chunks over FP8 workspace rows
+ * (blog section 3, second data flow: a chunked prefill / extend attends over
+ * its cached prefix from the FP8 workspace; first data flow: the new tokens'
+ * own K/V take part as FP8, causally as in prefill).  Sequence i < num_seqs
+ * has prefix P_i = prefix_lens[i] and chunk C_i = q_offsets[i+1] -
+ * q_offsets[i]; its K/V are workspace rows ws_offsets[i] + t, t < P_i + C_i
+ * (the prefix from nvfp4_dequant_to_fp8_workspace, the chunk from
+ * nvfp4_fp8_rows_to_workspace).  Query token j < C_i is row q_offsets[i] + j
+ * of q; for query head qh and kv head h = qh / (num_q_heads/num_kv_heads):
+ *   s_t = sm_scale * sum_d q[d] * E4M3(ws_k[row_t][h][d]) * k_ws_scale,  t <= P_i + j
+ *   out[q_offsets[i] + j][qh][d] = sum_t softmax(s)_t * E4M3(ws_v[row_t][h][d]) * v_ws_scale
+ * E4M3 values are widened exactly to f16 for f16 MFMA; softmax and
+ * accumulation are fp32.
+ *   q          : [num_q_tokens][num_q_heads][128] of q_dtype, 16-byte aligned.
+ *   q_offsets  : [num_seqs+1] int32, nondecreasing (values are clamped to
+ *                [0, num_q_tokens]); ws_offsets, prefix_lens: [num_seqs] int32.
+ *   max_chunk_len: host bound >= every C_i (sizes the launch); query tokens
+ *                of a chunk past it are not computed.
+ *   ws_k, ws_v : [ws_capacity_tokens][num_kv_heads][128] uint8, 16-byte aligned;
+ *                rows outside it read as zero bytes (memory-safe, results
+ *                then unspecified).
+ *   out        : [num_q_tokens][num_q_heads][128] float32; rows of tokens that
+ *                belong to no chunk are not written.
+ *   Supported: num_kv_heads <= 65535 and num_seqs <= 65535. */
+NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn(const void* q, nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                               int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                               const int32_t* q_offsets, const int32_t* ws_offsets,
+                                               const int32_t* prefix_lens, int32_t max_chunk_len,
+                                               const uint8_t* ws_k, const uint8_t* ws_v, int32_t ws_capacity_tokens,
+                                               float k_ws_scale, float v_ws_scale, float sm_scale, float* out,
+                                               void* stream);
 
 /* Static string for a status code. */
 NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);

@@ -39,6 +39,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_paged_decode_workspace_bytes",
     "nvfp4_paged_decode_attn",
     "nvfp4_dequant_to_fp8_workspace",
+    "nvfp4_fp8_rows_to_workspace",
+    "nvfp4_fp8_extend_attn",
     "nvfp4_status_string",
 )
 
@@ -81,6 +83,11 @@ def _load():
     L.nvfp4_paged_decode_attn.restype = ctypes.c_int
     L.nvfp4_dequant_to_fp8_workspace.argtypes = [lp, vp, i32, i32, vp, vp, i32, f32, f32, vp, vp, i32, vp]
     L.nvfp4_dequant_to_fp8_workspace.restype = ctypes.c_int
+    L.nvfp4_fp8_rows_to_workspace.argtypes = [vp, vp, ctypes.c_int, i32, i64, i32, vp, f32, f32, vp, vp, i32, vp]
+    L.nvfp4_fp8_rows_to_workspace.restype = ctypes.c_int
+    L.nvfp4_fp8_extend_attn.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, f32, f32,
+                                        f32, vp, vp]
+    L.nvfp4_fp8_extend_attn.restype = ctypes.c_int
     L.nvfp4_status_string.argtypes = [ctypes.c_int]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     return L
@@ -236,3 +243,58 @@ def dequant_to_fp8_workspace(layer: KVCacheLayer, block_table: torch.Tensor, pre
                                             float(k_ws_scale), float(v_ws_scale), _ptr(ws_k), _ptr(ws_v),
                                             ws_k.shape[0], _stream(stream))
     _check(st, "nvfp4_dequant_to_fp8_workspace")
+
+
+def _check_ws_pair(ws_k: torch.Tensor, ws_v: torch.Tensor):
+    for w in (ws_k, ws_v):
+        if w.dtype not in (torch.uint8, torch.float8_e4m3fn) or not w.is_contiguous():
+            raise ValueError("workspace must be contiguous uint8 / float8_e4m3fn")
+        if w.dim() != 3 or w.shape[2] != HEAD_DIM:
+            raise ValueError("workspace must be [capacity, H, 128]")
+    if ws_k.shape != ws_v.shape:
+        raise ValueError("ws_k and ws_v must have the same shape")
+
+
+def fp8_rows_to_workspace(k: torch.Tensor, v: torch.Tensor, ws_rows: torch.Tensor, k_ws_scale: float,
+                          v_ws_scale: float, ws_k: torch.Tensor, ws_v: torch.Tensor, stream=None) -> None:
+    """Store new tokens' k, v ([T, H, 128], bf16/f32, token-strided) as E4M3 rows ws_rows of ws_k, ws_v."""
+    if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape, dtype and strides")
+    _check_ws_pair(ws_k, ws_v)
+    _dev_i32(ws_rows, "ws_rows")
+    T = k.shape[0]
+    if k.dim() != 3 or k.shape[1:] != (ws_k.shape[1], HEAD_DIM) or k.stride(2) != 1 or \
+            (k.shape[1] > 1 and k.stride(1) != HEAD_DIM):
+        raise ValueError("k/v must be [T, H, 128] with contiguous heads, H matching the workspace")
+    if ws_rows.numel() != T:
+        raise ValueError("ws_rows must have one entry per token")
+    st = lib.nvfp4_fp8_rows_to_workspace(_ptr(k), _ptr(v), _dtype_code(k), T,
+                                         k.stride(0) if T > 0 else ws_k.shape[1] * HEAD_DIM, ws_k.shape[1],
+                                         _ptr(ws_rows), float(k_ws_scale), float(v_ws_scale), _ptr(ws_k), _ptr(ws_v),
+                                         ws_k.shape[0], _stream(stream))
+    _check(st, "nvfp4_fp8_rows_to_workspace")
+
+
+def fp8_extend_attn(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.Tensor, prefix_lens: torch.Tensor,
+                    max_chunk_len: int, ws_k: torch.Tensor, ws_v: torch.Tensor, k_ws_scale: float, v_ws_scale: float,
+                    sm_scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal attention of chunk queries q [Tq, Hq, 128] over FP8 workspace rows; returns f32 [Tq, Hq, 128]."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [Tq, Hq, 128] tensor")
+    _check_ws_pair(ws_k, ws_v)
+    for t, name in ((q_offsets, "q_offsets"), (ws_offsets, "ws_offsets"), (prefix_lens, "prefix_lens")):
+        _dev_i32(t, name)
+    n = prefix_lens.numel()
+    if q_offsets.numel() != n + 1 or ws_offsets.numel() != n:
+        raise ValueError("q_offsets [n+1], ws_offsets [n], prefix_lens [n]")
+    Tq, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((Tq, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (Tq, Hq, HEAD_DIM):
+        raise ValueError("out must be a contiguous float32 [Tq, Hq, 128] tensor")
+    st = lib.nvfp4_fp8_extend_attn(_ptr(q), _dtype_code(q), Tq, Hq, ws_k.shape[1], n, _ptr(q_offsets),
+                                   _ptr(ws_offsets), _ptr(prefix_lens), int(max_chunk_len), _ptr(ws_k), _ptr(ws_v),
+                                   ws_k.shape[0], float(k_ws_scale), float(v_ws_scale), float(sm_scale), _ptr(out),
+                                   _stream(stream))
+    _check(st, "nvfp4_fp8_extend_attn")
+    return out

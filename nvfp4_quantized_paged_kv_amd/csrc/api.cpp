@@ -171,4 +171,72 @@ NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* 
   return from_hip(launch_dequant_ws(p, static_cast<hipStream_t>(stream)));
 }
 
+NVFP4_API nvfp4_status_t nvfp4_fp8_rows_to_workspace(const void* k_new, const void* v_new, nvfp4_dtype_t dtype,
+                                                     int32_t num_tokens, int64_t token_stride_elems,
+                                                     int32_t num_kv_heads, const int32_t* ws_rows, float k_ws_scale,
+                                                     float v_ws_scale, uint8_t* ws_k, uint8_t* ws_v,
+                                                     int32_t ws_capacity_tokens, void* stream) {
+  if (!dtype_ok(dtype) || num_tokens < 0 || num_kv_heads <= 0 || ws_capacity_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!scale_ok(k_ws_scale) || !scale_ok(v_ws_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0 || ws_capacity_tokens == 0) return NVFP4_OK;
+  if (!k_new || !v_new || !ws_rows || !ws_k || !ws_v) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (token_stride_elems < (int64_t)num_kv_heads * kHeadDim) return NVFP4_ERR_INVALID_ARGUMENT;
+  const int64_t esize = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || (token_stride_elems * esize) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(ws_k, 16) || !aligned(ws_v, 16)) return NVFP4_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens * num_kv_heads * 8 / 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_UNSUPPORTED;  // grid size
+  Fp8RowsParams p;
+  p.x[0] = k_new;
+  p.x[1] = v_new;
+  p.ws[0] = ws_k;
+  p.ws[1] = ws_v;
+  p.ws_scale[0] = k_ws_scale;
+  p.ws_scale[1] = v_ws_scale;
+  p.rows = ws_rows;
+  p.token_stride = token_stride_elems;
+  p.num_tokens = num_tokens;
+  p.H = num_kv_heads;
+  p.ws_capacity = ws_capacity_tokens;
+  return from_hip(launch_fp8_rows(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn(const void* q, nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                               int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                               const int32_t* q_offsets, const int32_t* ws_offsets,
+                                               const int32_t* prefix_lens, int32_t max_chunk_len,
+                                               const uint8_t* ws_k, const uint8_t* ws_v, int32_t ws_capacity_tokens,
+                                               float k_ws_scale, float v_ws_scale, float sm_scale, float* out,
+                                               void* stream) {
+  if (!dtype_ok(q_dtype) || num_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_seqs < 0 ||
+      max_chunk_len < 0 || ws_capacity_tokens < 0)
+    return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_q_heads / num_kv_heads > kMaxGroup) return NVFP4_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || num_seqs > 65535) return NVFP4_ERR_UNSUPPORTED;  // grid dimensions
+  if (!scale_ok(k_ws_scale) || !scale_ok(v_ws_scale) || !std::isfinite(sm_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  const double qk = (double)sm_scale * (double)k_ws_scale * 1.4426950408889634;  // log2(e)
+  if (!std::isfinite(qk) || !std::isfinite((float)qk)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0 || max_chunk_len == 0 || num_q_tokens == 0) return NVFP4_OK;
+  if (!q || !q_offsets || !ws_offsets || !prefix_lens || !ws_k || !ws_v || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(ws_k, 16) || !aligned(ws_v, 16)) return NVFP4_ERR_UNSUPPORTED;
+  ExtendParams p;
+  p.q = q;
+  p.out = out;
+  p.ws_k = ws_k;
+  p.ws_v = ws_v;
+  p.q_offsets = q_offsets;
+  p.ws_offsets = ws_offsets;
+  p.prefix_lens = prefix_lens;
+  p.num_q_tokens = num_q_tokens;
+  p.Hq = num_q_heads;
+  p.H = num_kv_heads;
+  p.G = num_q_heads / num_kv_heads;
+  p.num_seqs = num_seqs;
+  p.max_chunk = max_chunk_len;
+  p.ws_capacity = ws_capacity_tokens;
+  p.qk_scale_log2 = (float)qk;
+  p.v_scale = v_ws_scale;
+  return from_hip(launch_extend(p, q_dtype, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,389 @@
+// FP8 rows of new tokens, and causal extend / prefill attention over FP8
+// workspace rows, for gfx950 (CDNA4, wave64, MFMA).
+//
+// grer.cn blog "NVFP4 KV cache and the memory wall", section 3: in chunked
+// prefill / extend the cached prefix is dequantized from NVFP4 into one FP8
+// workspace that every layer reuses (dequant_ws.hip), and the K/V of the
+// tokens being processed take part in attention as FP8, as in the first
+// prefill.  Here the chunk's K/V are stored as FP8 rows right after their
+// prefix (fp8_rows_kernel), and the chunk's queries attend causally over
+// [prefix | chunk] (extend_kernel).  The attention is compute-bound (about
+// 512 flops per query row and key for 256 bytes per key), so QK^T and PV run
+// on MFMA; the E4M3 bytes are widened exactly to f16 in registers.
+//
+// extend_kernel work split: one workgroup per (16 chunk tokens, kv head,
+// sequence); its rows are the 16 tokens of each of the G query heads of the
+// kv head.  Wave w owns heads 2w and 2w+1 (two 16-row blocks).  Keys stream
+// through LDS in tiles of 32: K rows as FP8 (padded), V transposed to
+// [dim][key] while it is written, so a lane's PV operand (4 keys of one dim)
+// is one 32-bit read.  Per tile and wave:
+//   S^T[key][token] = K . Q^T : 2 key blocks x 4 mfma_f32_16x16x32_f16 per
+//                     row block (lane: key 16kb + l%16, dims 32*(l/16)..+31;
+//                     Q in the same permuted dim order, so no shuffles)
+//   online softmax in fp32 (exp2 domain, lazy max as in the decode kernel)
+//   O[token][dim]  += P . V : 8 dim blocks x 2 key blocks x
+//                     mfma_f32_16x16x16_f16 (the S^T lane layout is the
+//                     PV A-operand layout)
+// The FP32 per-tensor workspace scales go on the logits (K) and on the output
+// (V); Q is converted to f16 after an exact power-of-two prescale (float32 Q
+// as an f16 hi + lo pair), as in the decode kernel.
+#include "nvfp4_device.h"
+#include "nvfp4_kv_internal.h"
+
+namespace nvfp4kv {
+namespace {
+
+// ------------------------------------------------------------------ FP8 rows
+// One thread per 16 consecutive values of one (token, kv head); blockIdx.y
+// picks K or V.  Byte = sign(x) | E4M3 nearest to |x| / ws_scale: the float64
+// quotient of a float32 dividend rounds like the exact real quotient (an E4M3
+// midpoint times the divisor has at most 29 significant bits, so a dividend
+// that is not on it lies at least 2^-30 away, relative).
+template <typename InT>
+__global__ __launch_bounds__(256) void fp8_rows_kernel(Fp8RowsParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tensor = blockIdx.y;
+  if (i >= (int64_t)p.num_tokens * p.H * 8) return;
+  const int grp = (int)(i & 7);
+  const int64_t th = i >> 3;
+  const int h = (int)(th % p.H);
+  const int64_t t = th / p.H;
+  const int row = p.rows[t];
+  if (row < 0 || row >= p.ws_capacity) return;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(p.x[tensor]) +
+                       (t * p.token_stride + (int64_t)h * kHeadDim + grp * 16) * (int64_t)sizeof(InT);
+  float v[16];
+  if (sizeof(InT) == 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint4 w = reinterpret_cast<const uint4*>(src)[k];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * k + 2 * j] = __uint_as_float(ww[j] << 16);
+        v[8 * k + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w = reinterpret_cast<const uint4*>(src)[k];
+      v[4 * k] = __uint_as_float(w.x);
+      v[4 * k + 1] = __uint_as_float(w.y);
+      v[4 * k + 2] = __uint_as_float(w.z);
+      v[4 * k + 3] = __uint_as_float(w.w);
+    }
+  }
+  const double s = (double)p.ws_scale[tensor];
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t mag = e4m3_encode_rne_sat((double)__builtin_fabsf(v[k]) / s);
+    const uint32_t byte = mag | ((__float_as_uint(v[k]) >> 24) & 0x80u);
+    w[k >> 2] |= byte << (8 * (k & 3));
+  }
+  *reinterpret_cast<uint4*>(p.ws[tensor] + ((int64_t)row * p.H + h) * kHeadDim + grp * 16) =
+      uint4{w[0], w[1], w[2], w[3]};
+}
+
+// ------------------------------------------------------------ extend attention
+constexpr int kExtTok = 16;                        // chunk tokens per workgroup
+constexpr int kExtKeys = 32;                       // keys per LDS tile
+constexpr int kKStride = 144;                      // LDS bytes per K row (128 + 16 pad)
+constexpr int kVStride = 36;                       // LDS bytes per transposed V row (32 keys + 4 pad)
+constexpr int kKTileBytes = kExtKeys * kKStride;
+constexpr int kVTileBytes = kHeadDim * kVStride;
+constexpr float kExtLazyMax = 8.0f;                // log2 headroom before the running max moves
+
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max / sum over lanes l, l^16, l^32, l^48 (the 4 key groups of one query row)
+__device__ __forceinline__ float vmax_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Two E4M3 bytes of word `w` (bytes 0-1, or 2-3 with HI) widened exactly to
+// an f16 pair, returned as its 32-bit pattern (scale operand 1.0).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+template <bool QF32>
+__global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kKTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kVTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int er = lane & 15, eq = lane >> 4;
+  const int seq = blockIdx.z, h = blockIdx.y;
+  const int tile = gridDim.x - 1 - blockIdx.x;  // the tiles with the most keys start first
+  const int G = p.G, H = p.H;
+
+  // ---- the sequence (device data is clamped, never trusted)
+  const int nq = p.num_q_tokens;
+  const int q0 = min(max(__builtin_amdgcn_readfirstlane(p.q_offsets[seq]), 0), nq);
+  const int q1 = min(max(__builtin_amdgcn_readfirstlane(p.q_offsets[seq + 1]), q0), nq);
+  const int C = min(q1 - q0, p.max_chunk);
+  const int t0 = tile * kExtTok;
+  if (t0 >= C) return;
+  const int ntok = min(kExtTok, C - t0);
+  const int P = min(max(__builtin_amdgcn_readfirstlane(p.prefix_lens[seq]), 0), p.ws_capacity);
+  const int64_t woff = __builtin_amdgcn_readfirstlane(p.ws_offsets[seq]);
+  const int n_keys = P + t0 + ntok;  // keys the tile's last token sees
+  const int n_all = P + t0 + 1;      // keys every token of the tile sees
+  const int n_kt = (n_keys + kExtKeys - 1) / kExtKeys;
+
+  // ---- tile loads: thread tid < 256 moves 16 K bytes (key tid/8, bytes 16*(tid%8))
+  // and a 4x4 block of V (keys 4*(tid/32)..+3, dims 4*(tid%32)..+3)
+  const bool loader = tid < 256;
+  const int kk = tid >> 3, kc = tid & 7;
+  const int vg = (tid >> 5) & 7, vd = tid & 31;
+  uint4 kreg = {0u, 0u, 0u, 0u};
+  uint32_t vreg[4] = {0u, 0u, 0u, 0u};
+  auto key_row = [&](int key) -> int64_t {  // workspace row of key, or -1 outside [0, n_keys) / the buffer
+    const int64_t r = woff + key;
+    return (key < n_keys && r >= 0 && r < p.ws_capacity) ? r : -1;
+  };
+  auto load_tile = [&](int kt) {
+    if (!loader) return;
+    const int64_t rk = key_row(kt * kExtKeys + kk);
+    kreg = rk >= 0 ? *reinterpret_cast<const uint4*>(p.ws_k + (rk * H + h) * kHeadDim + 16 * kc) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t rv = key_row(kt * kExtKeys + 4 * vg + j);
+      vreg[j] = rv >= 0 ? *reinterpret_cast<const uint32_t*>(p.ws_v + (rv * H + h) * kHeadDim + 4 * vd) : 0u;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if (!loader) return;
+    *reinterpret_cast<uint4*>(&s_k[buf][kk * kKStride + 16 * kc]) = kreg;
+    // 4x4 byte transpose: out[e] = dim 4*vd+e of keys 4*vg .. 4*vg+3
+    const uint32_t a_lo = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+    const uint32_t a_hi = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+    const uint32_t b_lo = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x05010400u);
+    const uint32_t b_hi = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x07030602u);
+    uint8_t* vt = &s_v[buf][(4 * vd) * kVStride + 4 * vg];
+    *reinterpret_cast<uint32_t*>(vt) = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(vt + kVStride) = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
+    *reinterpret_cast<uint32_t*>(vt + 2 * kVStride) = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(vt + 3 * kVStride) = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+  };
+  load_tile(0);
+
+  // ---- this wave's two row blocks: query heads 2*wave and 2*wave+1, tokens t0 .. t0+15
+  const bool active = 2 * wave < G;
+  half8_t qa[2][4], ql[2][4];
+  float tscale[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int g = 2 * wave + rb;
+    float qv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) qv[k] = 0.0f;
+    if (active && g < G && er < ntok) {
+      const int64_t qoff = ((int64_t)(q0 + t0 + er) * p.Hq + (int64_t)h * G + g) * kHeadDim + 32 * eq;
+      if (QF32) {
+        const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.q) + qoff);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint4 w = qp[k];
+          qv[4 * k] = __uint_as_float(w.x);
+          qv[4 * k + 1] = __uint_as_float(w.y);
+          qv[4 * k + 2] = __uint_as_float(w.z);
+          qv[4 * k + 3] = __uint_as_float(w.w);
+        }
+      } else {
+        const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) + qoff);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint4 w = qp[k];
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            qv[8 * k + 2 * j] = __uint_as_float(ww[j] << 16);
+            qv[8 * k + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+    float qmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, __builtin_fabsf(qv[k]));
+    qmax = wave_max(qmax);
+    int qe = 0;
+    (void)__builtin_frexpf(qmax, &qe);  // qmax < 2^qe
+    // exact power of two carrying the sign of the logit scale, so that tscale >= 0
+    const float qscale = __builtin_copysignf(qmax > 0.0f ? __builtin_ldexpf(1.0f, 15 - qe) : 1.0f, p.qk_scale_log2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float xq = qv[8 * c + j] * qscale;
+        qa[rb][c][j] = (_Float16)xq;
+        ql[rb][c][j] = QF32 ? (_Float16)(xq - (float)qa[rb][c][j]) : (_Float16)0.0f;
+      }
+    tscale[rb] = fmaxf(p.qk_scale_log2 / qscale, __FLT_MIN__);
+  }
+
+  float m_run[2] = {-__FLT_MAX__, -__FLT_MAX__};  // -FLT_MAX: no maximum yet
+  float m_lim[2] = {-__FLT_MAX__, -__FLT_MAX__};
+  float l_run[2] = {0.0f, 0.0f};
+  float4_t acc[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[rb][d] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(kt + 1);  // in flight while this tile is computed
+    if (!active) continue;
+
+    // ---- S^T = K . Q^T for the tile's two 16-key blocks
+    float4_t S[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint8_t* kp = &s_k[buf][(16 * kb + er) * kKStride + 32 * eq];
+      const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(kp + 16);
+      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      S[kb][0] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      S[kb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 hw = {fp8x2_to_f16x2<false>(kw[2 * c]), fp8x2_to_f16x2<true>(kw[2 * c]),
+                          fp8x2_to_f16x2<false>(kw[2 * c + 1]), fp8x2_to_f16x2<true>(kw[2 * c + 1])};
+        const half8_t a = __builtin_bit_cast(half8_t, hw);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          S[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qa[rb][c], S[kb][rb], 0, 0, 0);
+          if (QF32) S[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[rb][c], S[kb][rb], 0, 0, 0);
+        }
+      }
+    }
+    // explicit wait states between the MFMA results and their first VALU
+    // reads (20 cover MFMAs of up to 16 passes), as in the decode kernel
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[1][0]), "+v"(S[1][1]));
+
+    // ---- causal mask: only tiles reaching past the keys every token sees
+    const int kbase = kt * kExtKeys;
+    if (kbase + kExtKeys > n_all) {
+      const int lim = P + t0 + er;  // last key of this lane's token
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kbase + 16 * kb + 4 * eq + i > lim) {
+            S[kb][0][i] = -__builtin_inff();
+            S[kb][1][i] = -__builtin_inff();
+          }
+    }
+
+    // ---- online softmax per row block (exp2 domain, lazy max)
+    half4_t pa[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float pm =
+          vmax_over_groups(vmax(vmax(vmax(S[0][rb][0], S[0][rb][1]), vmax(S[0][rb][2], S[0][rb][3])),
+                                vmax(vmax(S[1][rb][0], S[1][rb][1]), vmax(S[1][rb][2], S[1][rb][3])))) *
+          tscale[rb];
+      if (__any(pm > m_lim[rb])) {
+        const float m_new = fmaxf(m_run[rb], pm);
+        const float f = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float fj = __shfl(f, 4 * eq + jj);
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[rb][d][jj] *= fj;
+        }
+        m_run[rb] = m_new;
+        m_lim[rb] = m_new + kExtLazyMax;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][rb][i], tscale[rb], -m_run[rb]));
+        l_run[rb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        pa[rb][kb] = half4_t{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+      }
+    }
+
+    // ---- O += P . V: lane (dim 16*db + er, keys 16*kb + 4*eq .. +3) from transposed V
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t vw = *reinterpret_cast<const uint32_t*>(&s_v[buf][(16 * db + er) * kVStride + 16 * kb + 4 * eq]);
+        const uint2 hv = {fp8x2_to_f16x2<false>(vw), fp8x2_to_f16x2<true>(vw)};
+        const half4_t b = __builtin_bit_cast(half4_t, hv);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[rb][kb], b, acc[rb][db], 0, 0, 0);
+      }
+  }
+  if (!active) return;
+
+  // ---- normalise and store: lane holds O[token 4*eq + i][dim 16*db + er]
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int g = 2 * wave + rb;
+    const float l_tot = sum_over_groups(l_run[rb]);  // lane er: the row sum of token er
+    if (g >= G) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * eq + i;
+      const float L = __shfl(l_tot, row);
+      if (row >= ntok) continue;
+      float* op = p.out + ((int64_t)(q0 + t0 + row) * p.Hq + (int64_t)h * G + g) * kHeadDim + er;
+      const float f = p.v_scale / L;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) op[16 * db] = acc[rb][db][i] * f;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_rows(const Fp8RowsParams& p, nvfp4_dtype_t dtype, hipStream_t stream) {
+  const int64_t n = (int64_t)p.num_tokens * p.H * 8;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256), 2);
+  if (dtype == NVFP4_DTYPE_F32)
+    hipLaunchKernelGGL(fp8_rows_kernel<float>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(fp8_rows_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_extend(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream) {
+  if (p.num_seqs == 0 || p.max_chunk == 0 || p.num_q_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.max_chunk + kExtTok - 1) / kExtTok), (unsigned)p.H, (unsigned)p.num_seqs);
+  const dim3 block(p.G <= 8 ? 256 : 512);  // at least 256 threads: the tile loaders
+  if (q_dtype == NVFP4_DTYPE_F32)
+    hipLaunchKernelGGL(extend_kernel<true>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(extend_kernel<false>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

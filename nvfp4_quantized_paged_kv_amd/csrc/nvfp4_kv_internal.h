@@ -98,4 +98,40 @@ struct DequantWsParams {
 
 hipError_t launch_dequant_ws(const DequantWsParams& p, hipStream_t stream);
 
+// FP8 rows of new tokens (K and V) into a workspace pair.
+struct Fp8RowsParams {
+  const void* x[2];      // K, V: [num_tokens][H][128], token stride `token_stride` elements
+  uint8_t* ws[2];        // [ws_capacity][H][128]
+  float ws_scale[2];
+  const int32_t* rows;   // [num_tokens] workspace row per token (< 0: skip)
+  int64_t token_stride;
+  int32_t num_tokens;
+  int32_t H;
+  int32_t ws_capacity;
+};
+
+hipError_t launch_fp8_rows(const Fp8RowsParams& p, nvfp4_dtype_t dtype, hipStream_t stream);
+
+// Causal attention of extend / prefill chunks over FP8 workspace rows.
+struct ExtendParams {
+  const void* q;               // [num_q_tokens][Hq][128]
+  float* out;                  // [num_q_tokens][Hq][128]
+  const uint8_t* ws_k;         // [ws_capacity][H][128] E4M3
+  const uint8_t* ws_v;
+  const int32_t* q_offsets;    // [num_seqs + 1]
+  const int32_t* ws_offsets;   // [num_seqs]
+  const int32_t* prefix_lens;  // [num_seqs]
+  int32_t num_q_tokens;
+  int32_t Hq;
+  int32_t H;
+  int32_t G;
+  int32_t num_seqs;
+  int32_t max_chunk;
+  int32_t ws_capacity;
+  float qk_scale_log2;         // sm_scale * k_ws_scale * log2(e)
+  float v_scale;               // v_ws_scale
+};
+
+hipError_t launch_extend(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
+
 }  // namespace nvfp4kv

@@ -147,3 +147,53 @@ def test_workspace_dequant_checks():
     assert _ws(nk, L, wk=0) == 1
     assert _ws(nk, L, bts=6) == 1                              # 6*16 < 100
     assert _ws(nk, L, wv=FAKE + 4) == 2
+
+
+def _rows(nk, k=FAKE, v=FAKE, dtype=1, T=4, stride=1024, H=8, rows=FAKE, ks=1.0, vs=1.0, wk=FAKE, wv=FAKE, cap=100):
+    return nk.lib.nvfp4_fp8_rows_to_workspace(ctypes.c_void_p(k), ctypes.c_void_p(v), dtype, T, stride, H,
+                                              ctypes.c_void_p(rows), ks, vs, ctypes.c_void_p(wk), ctypes.c_void_p(wv),
+                                              cap, None)
+
+
+def test_fp8_rows_checks():
+    nk = _lib()
+    assert _rows(nk, dtype=7) == 1
+    assert _rows(nk, T=-1) == 1
+    assert _rows(nk, H=0) == 1
+    assert _rows(nk, cap=-1) == 1
+    assert _rows(nk, ks=float("inf")) == 1
+    assert _rows(nk, vs=-1.0) == 1
+    assert _rows(nk, T=0, k=0, v=0, rows=0, wk=0, wv=0) == 0    # nothing to do
+    assert _rows(nk, cap=0, k=0, v=0, rows=0, wk=0, wv=0) == 0  # nothing can be written
+    assert _rows(nk, rows=0) == 1
+    assert _rows(nk, stride=1000) == 1                           # < H*128
+    assert _rows(nk, k=FAKE + 8) == 2
+    assert _rows(nk, stride=1028) == 2                           # rows not 16-byte aligned
+    assert _rows(nk, wv=FAKE + 2) == 2
+
+
+def _ext(nk, q=FAKE, dt=1, nq=64, hq=64, h=8, n=2, qo=FAKE, wo=FAKE, pl=FAKE, mc=32, wk=FAKE, wv=FAKE, cap=1000,
+         ks=1.0, vs=1.0, sm=0.088, out=FAKE):
+    return nk.lib.nvfp4_fp8_extend_attn(ctypes.c_void_p(q), dt, nq, hq, h, n, ctypes.c_void_p(qo), ctypes.c_void_p(wo),
+                                        ctypes.c_void_p(pl), mc, ctypes.c_void_p(wk), ctypes.c_void_p(wv), cap, ks, vs,
+                                        sm, ctypes.c_void_p(out), None)
+
+
+def test_fp8_extend_checks():
+    nk = _lib()
+    assert _ext(nk, dt=3) == 1
+    assert _ext(nk, hq=60) == 1                 # not a multiple of the kv heads
+    assert _ext(nk, hq=8 * 17) == 2             # more than 16 query heads per kv head
+    assert _ext(nk, h=70000, hq=70000) == 2     # grid limit
+    assert _ext(nk, n=70000) == 2
+    assert _ext(nk, n=-1) == 1
+    assert _ext(nk, mc=-1) == 1
+    assert _ext(nk, ks=0.0) == 1
+    assert _ext(nk, sm=float("nan")) == 1
+    assert _ext(nk, sm=3e38, ks=1e30) == 1      # logit scale overflows float32
+    assert _ext(nk, n=0, q=0, qo=0, wo=0, pl=0, wk=0, wv=0, out=0) == 0
+    assert _ext(nk, mc=0, q=0, out=0) == 0
+    assert _ext(nk, out=0) == 1
+    assert _ext(nk, pl=0) == 1
+    assert _ext(nk, q=FAKE + 4) == 2
+    assert _ext(nk, wk=FAKE + 8) == 2

@@ -1,0 +1,216 @@
+"""GPU parity of the extend path: FP8 rows of new tokens (bit-exact against the
+oracle) and causal extend / prefill attention over FP8 workspace rows (within
+the 1e-3 row-normalised bound of the decode attention), through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from nvfp4_quantized_paged_kv_amd import synth
+from tests.gpu_cases import ATTN_TOL, build_cache, host_f32, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_quantized_paged_kv_amd as nk  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def _kv_values(rng, T, H, chan50=True):
+    """K/V-like float32 values: N(0, 0.02), K with 2 channels x50 (the 70B-class recipe)."""
+    k = rng.normal(0, 0.02, (T, H, 128)).astype(np.float32)
+    v = rng.normal(0, 0.02, (T, H, 128)).astype(np.float32)
+    if chan50:
+        k[:, :, [5, 77]] *= 50
+    return k, v
+
+
+# ------------------------------------------------------------------- FP8 rows
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fp8_rows_bitexact(dtype):
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say(f"case: fp8 rows dtype={dtype}")
+    rng = np.random.default_rng(51)
+    T, H, cap = 333, 4, 400
+    k, v = _kv_values(rng, T, H)
+    # exact E4M3 midpoints (times the scale) in a few rows: ties go to the even byte
+    ks, vs = float(np.abs(k).max() / 448), float(np.abs(v).max() / 448)
+    e4 = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    mids = (e4[:-1] + e4[1:]) / 2
+    k[:4].reshape(-1)[: 4 * H * 128] = np.resize(mids * 1.0, 4 * H * 128).astype(np.float32)
+    if dtype == torch.float32:
+        ks = 1.0  # the midpoints above are exact quotients only for a unit scale
+    kt = torch.from_numpy(k).to(dtype)
+    vt = torch.from_numpy(v).to(dtype)
+    if dtype == torch.float32:  # token-strided input: rows of a wider buffer
+        def strided(x):
+            wide = torch.zeros((T, H * 128 + 64), dtype=dtype)
+            wide[:, : H * 128] = x.reshape(T, -1)
+            return wide.cuda()[:, : H * 128].reshape(T, H, 128)
+        kd, vd = strided(kt), strided(vt)
+        assert kd.stride(0) == H * 128 + 64
+    else:
+        kd, vd = kt.cuda(), vt.cuda()
+    rows = rng.permutation(cap)[:T].astype(np.int32)
+    rows[::17] = -1                   # skipped
+    rows[5] = cap + 3                 # past the capacity: skipped
+    ws_k = torch.full((cap, H, 128), 0x5A, dtype=torch.uint8, device="cuda")
+    ws_v = torch.full_like(ws_k, 0x5A)
+    nk.fp8_rows_to_workspace(kd, vd, torch.from_numpy(rows).cuda(), ks, vs, ws_k, ws_v)
+    torch.cuda.synchronize()
+    ref_k = np.full((cap, H, 128), 0x5A, np.uint8)
+    ref_v = np.full_like(ref_k, 0x5A)
+    oracle.fp8_quantize_rows(host_f32(kt), np.where(rows < cap, rows, -1), ks, ref_k)
+    oracle.fp8_quantize_rows(host_f32(vt), np.where(rows < cap, rows, -1), vs, ref_v)
+    assert np.array_equal(ws_k.cpu().numpy(), ref_k)
+    assert np.array_equal(ws_v.cpu().numpy(), ref_v)
+
+
+# ----------------------------------------------------------- extend attention
+def _case(rng, prefixes, chunks, H, gap=5):
+    """Workspace rows [prefix | chunk] per sequence (gaps between), FP8 bytes from the oracle."""
+    offs, at = [], 0
+    for p, c in zip(prefixes, chunks):
+        offs.append(at)
+        at += p + c + gap
+    cap = at
+    k, v = _kv_values(rng, cap, H)
+    ks, vs = float(np.abs(k).max() / 448), float(np.abs(v).max() / 448)
+    ws_k = np.zeros((cap, H, 128), np.uint8)
+    ws_v = np.zeros_like(ws_k)
+    oracle.fp8_quantize_rows(k, np.arange(cap), ks, ws_k)
+    oracle.fp8_quantize_rows(v, np.arange(cap), vs, ws_v)
+    qo = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return ws_k, ws_v, ks, vs, np.array(offs, np.int32), qo
+
+
+def _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, qdt, seed, q_scale=1.0, sm=0.088, rows=None,
+                 max_chunk=None, extra_q_rows=0):
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    Tq = int(qo[-1]) + extra_q_rows
+    q = synth.queries(Tq, Hq, qdt, "cpu", seed, 7)
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(qdt)
+    pl = np.asarray(prefixes, np.int32)
+    mc = int(np.diff(qo).max()) if max_chunk is None else max_chunk
+    out = torch.full((Tq, Hq, 128), 12345.0, dtype=torch.float32, device="cuda")
+    nk.fp8_extend_attn(q.cuda(), torch.from_numpy(qo).cuda(), torch.from_numpy(offs).cuda(),
+                       torch.from_numpy(pl).cuda(), mc, torch.from_numpy(ws_k).cuda(), torch.from_numpy(ws_v).cuda(),
+                       ks, vs, sm, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(Tq * Hq, 128)
+    qf = host_f32(q)[: int(qo[-1])]
+    if rows is None:
+        rows = np.arange(int(qo[-1]) * Hq, dtype=np.int64)
+    ref = oracle.extend_attention(ws_k, ws_v, ks, vs, qf, qo, offs, pl, sm, rows=rows)
+    return got, rows, ref
+
+
+@pytest.mark.parametrize("prefixes,chunks,H,G,qdt", [
+    ([0], [100], 2, 4, torch.bfloat16),                 # prefill: the chunk only
+    ([0, 37, 300], [1, 50, 33], 2, 8, torch.bfloat16),  # ragged extends, single-token chunk
+    ([200], [40], 1, 16, torch.float32),                # 512-thread workgroups, float32 Q
+    ([70, 5], [17, 64], 3, 3, torch.bfloat16),          # odd group: a half-empty wave
+    ([31, 32, 33], [15, 16, 17], 1, 1, torch.float32),  # tile and page boundaries, one head
+])
+def test_extend_matches_oracle(prefixes, chunks, H, G, qdt):
+    _say(f"case: extend prefixes={prefixes} chunks={chunks} H={H} G={G} q={qdt}")
+    rng = np.random.default_rng(sum(prefixes) + sum(chunks) + G)
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, H)
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, H * G, qdt, seed=G)
+    err = row_rel_err(got[rows], ref)
+    assert err.max() <= ATTN_TOL, (err.max(), int(np.argmax(err)))
+
+
+@pytest.mark.parametrize("q_scale", [30.0, 300.0])
+def test_extend_peaked_softmax(q_scale):
+    _say(f"case: extend peaked q_scale={q_scale}")
+    rng = np.random.default_rng(61)
+    prefixes, chunks = [150, 9], [40, 70]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, 16, torch.bfloat16, seed=3,
+                                  q_scale=q_scale)
+    err = row_rel_err(got[rows], ref)
+    assert err.max() <= ATTN_TOL, err.max()
+
+
+def test_extend_rows_outside_chunks_are_untouched():
+    """Tokens past max_chunk_len and query rows after the last chunk are not written."""
+    _say("case: extend untouched rows")
+    rng = np.random.default_rng(62)
+    prefixes, chunks = [20, 40], [30, 12]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, 8, torch.bfloat16, seed=4, max_chunk=16,
+                                  extra_q_rows=5)
+    Hq = 8
+    got = got.reshape(-1, Hq, 128)
+    ref = ref.reshape(-1, Hq, 128)
+    computed = [t for i in range(2) for t in range(qo[i], qo[i] + min(16, chunks[i]))]
+    assert row_rel_err(got[computed], ref[computed]).max() <= ATTN_TOL
+    skipped = [t for t in range(got.shape[0]) if t not in computed]
+    assert np.all(got[skipped] == 12345.0)
+
+
+def test_extend_after_nvfp4_workspace_and_fp8_rows():
+    """The whole extend flow: NVFP4 cache -> FP8 workspace prefix (dequant kernel),
+    chunk K/V -> FP8 rows, then attention; bytes bit-exact, attention to 1e-3."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: extend full flow")
+    H, G = 2, 8
+    prefixes, chunks = [200, 45, 0], [33, 64, 20]
+    c = build_cache(prefixes, H, torch.bfloat16, "chan50", 0.0, False, seed=71)
+    ks, vs = 6 * c.g_k, 6 * c.g_v
+    offs = np.concatenate([[0], np.cumsum(np.array(prefixes) + np.array(chunks))])[:-1].astype(np.int32)
+    cap = int(sum(prefixes) + sum(chunks))
+    ws_k = torch.zeros((cap, H, 128), dtype=torch.uint8, device="cuda")
+    ws_v = torch.zeros_like(ws_k)
+    pl = np.array(prefixes, np.int32)
+    nk.dequant_to_fp8_workspace(c.layer, torch.from_numpy(c.bt).cuda(), torch.from_numpy(pl).cuda(),
+                                torch.from_numpy(np.append(offs, cap).astype(np.int32)).cuda(), int(pl.max()), ks, vs,
+                                ws_k, ws_v)
+    rng = np.random.default_rng(72)
+    T = int(sum(chunks))
+    kn, vn = _kv_values(rng, T, H)
+    knt, vnt = torch.from_numpy(kn).to(torch.bfloat16), torch.from_numpy(vn).to(torch.bfloat16)
+    rows = np.concatenate([offs[i] + prefixes[i] + np.arange(chunks[i]) for i in range(3)]).astype(np.int32)
+    nk.fp8_rows_to_workspace(knt.cuda(), vnt.cuda(), torch.from_numpy(rows).cuda(), ks, vs, ws_k, ws_v)
+    torch.cuda.synchronize()
+    wk = oracle.fp8_workspace(c.planes, False, c.g_k, c.bt, pl, np.append(offs, cap), ks, cap)
+    wv = oracle.fp8_workspace(c.planes, True, c.g_v, c.bt, pl, np.append(offs, cap), vs, cap)
+    oracle.fp8_quantize_rows(host_f32(knt), rows, ks, wk)
+    oracle.fp8_quantize_rows(host_f32(vnt), rows, vs, wv)
+    assert np.array_equal(ws_k.cpu().numpy(), wk)
+    assert np.array_equal(ws_v.cpu().numpy(), wv)
+    qo = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    got, r, ref = _extend_both(wk, wv, ks, vs, offs, qo, prefixes, H * G, torch.bfloat16, seed=5)
+    assert row_rel_err(got[r], ref).max() <= ATTN_TOL
+
+
+def test_extend_mixed_step_shape_sampled():
+    """The mixed serving step's extend shape (64 q / 8 kv heads, 2048-token chunks over
+    long prefixes), checked on a sample of output rows the oracle computes one by one."""
+    _say("case: extend mixed-step shape, sampled rows")
+    rng = np.random.default_rng(81)
+    prefixes, chunks = [9000, 700], [2048, 2048]
+    H, Hq = 8, 64
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, H, gap=0)
+    Tq = int(qo[-1])
+    rows = np.unique(np.concatenate([
+        rng.integers(0, Tq * Hq, 150),
+        [0, Hq - 1, 2047 * Hq, 2048 * Hq, Tq * Hq - 1],  # first / last tokens of each chunk
+    ])).astype(np.int64)
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, torch.bfloat16, seed=6, rows=rows)
+    err = row_rel_err(got[rows], ref)
+    assert err.max() <= ATTN_TOL, err.max()
