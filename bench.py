@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0  # dense f16 / bf16 MFMA
 METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s) + quantize-append GB/s"
 # GPU spin (torch.cuda._sleep, clock cycles, about 0.1 ms) queued ahead of a
 # per-kernel event pair: the host-side call (10-20 us) is hidden behind it.
@@ -190,6 +191,12 @@ def warm_kernels(wl, dev):
     ws = torch.zeros((4, H, 128), dtype=torch.uint8, device=dev)
     nk.dequant_to_fp8_workspace(layer, bt, sl, torch.tensor([0, 4], dtype=torch.int32, device=dev), 4, 1.0, 1.0,
                                 ws, ws.clone())
+    rows = torch.arange(4, dtype=torch.int32, device=dev)
+    nk.fp8_rows_to_workspace(x, x, rows, 1.0, 1.0, ws, ws.clone())
+    qx = torch.zeros((4, wl.q_heads, 128), dtype=wl.in_dtype, device=dev)
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    nk.fp8_extend_attn(qx, torch.tensor([0, 4], dtype=torch.int32, device=dev), zero, zero, 4, ws, ws.clone(), 1.0,
+                       1.0, 0.088)
     torch.cuda.synchronize()
 
 
@@ -197,7 +204,10 @@ def bench_mixed(args, wl, dev):
     """Mixed serving step per layer: quantize-append every new token (16 per
     decoding sequence, 2048 per extended sequence), dequantize the extended
     sequences' cached prefixes into the one FP8 workspace pair every layer
-    reuses, then decode attention for the 56 decoding sequences."""
+    reuses, then decode attention for the 56 decoding sequences.  The extend
+    chunks' attention (compute-bound, on MFMA) and the FP8 rows of their K/V
+    are timed beside the step and reported with their own roofline; the
+    step's GB/s value covers the memory-bound kernels above."""
     import numpy as np
     import torch
 
@@ -218,7 +228,8 @@ def bench_mixed(args, wl, dev):
     s0 = steps[0]
     H, Hq = wl.kv_heads, wl.q_heads
     n_dec, n_ext = s0.decode.size, s0.extend.size
-    ws_cap = int(s0.ext_offsets[-1].item())
+    ws_cap = int(s0.ext_offsets[-1].item())  # prefix and chunk rows of the 8 extended sequences
+    ws_prefix = int(s0.ext_prefix.sum().item())
     ws_k = torch.empty((ws_cap, H, 128), dtype=torch.uint8, device=dev)  # one pair for every layer
     ws_v = torch.empty_like(ws_k)
     out = torch.empty((n_dec, Hq, 128), dtype=torch.float32, device=dev)
@@ -229,7 +240,7 @@ def bench_mixed(args, wl, dev):
     dec_pages = int(((s0.dec_lens + 15) // 16).sum().item())
     ext_pages = int(((s0.ext_prefix + 15) // 16).sum().item())
     b_app = t_new * H * (2 * 128 * in_b + 144) + 4 * t_new
-    b_ws = ws_cap * H * (144 + 256) + ext_pages * 4
+    b_ws = ws_prefix * H * (144 + 256) + ext_pages * 4
     b_dec = dec_tokens * H * 144 + dec_pages * 4 + n_dec * Hq * 128 * (in_b + 4)
     sm = 1 / math.sqrt(128)
 
@@ -278,6 +289,34 @@ def bench_mixed(args, wl, dev):
         nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
                              workspace=dws)
     dec_b2b = back_to_back(stream, args.steps, dec_call)
+
+    # ---- extend chunks: their K/V as FP8 rows after each prefix, then causal
+    # attention of the chunk queries over [prefix | chunk] in the workspace
+    ext_out = torch.empty((s0.ext_q.shape[0], Hq, 128), dtype=torch.float32, device=dev)
+    scales = lambda st: (6 * st.filled.layer.k_global, 6 * st.filled.layer.v_global)
+    rows_ms = []
+    for i in range(max(5, min(args.steps, 20))):
+        st = steps[i % L]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SLEEP_CYCLES)
+        e0.record(stream)
+        nk.fp8_rows_to_workspace(st.new_k, st.new_v, st.ext_rows, *scales(st), ws_k, ws_v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rows_ms.append(e0.elapsed_time(e1))
+    t_ext = int(s0.ext_q.shape[0])
+    b_rows = t_ext * H * 128 * (2 * in_b + 2) + 4 * t_new
+
+    def ext_call(i):
+        st = steps[i % L]
+        nk.fp8_extend_attn(st.ext_q, st.ext_q_offsets, st.ext_offsets[:-1], st.ext_prefix, st.ext_chunk, ws_k, ws_v,
+                           *scales(st), sm, out=ext_out)
+    ext_s = back_to_back(stream, max(4, args.steps // 10), ext_call)
+    C = s0.ext_chunk
+    pairs = sum(C * int(p) + C * (C + 1) // 2 for p in s0.ext_prefix.cpu().numpy())  # (query token, key) pairs
+    ext_flops = pairs * Hq * 4 * 128  # QK^T and PV: 2 x 128 multiply-adds per (query row, key)
+    ext_tf = ext_flops / ext_s / 1e12
+
     b_step = b_app + b_ws + b_dec
     achieved = b_dec / dec_b2b / 1e9
     return {
@@ -286,7 +325,7 @@ def bench_mixed(args, wl, dev):
         "config": {"workload": wl.name, "sequences": len(s0.lens), "decode_sequences": int(n_dec),
                    "extend_sequences": int(n_ext), "q_heads": Hq, "kv_heads": H, "head_dim": 128, "page_size": 16,
                    "layers_rotated": L, "new_tokens": int(t_new), "decode_tokens": dec_tokens,
-                   "workspace_tokens": ws_cap,
+                   "workspace_tokens": ws_prefix, "workspace_rows": ws_cap,
                    "step": "append 16/2048 tokens + FP8 workspace dequant of 8 prefixes + decode of 56, one layer"},
         "pct_of_peak": round(100 * b_step / (wall / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
         "decode_attn_gbs_events": round(achieved, 2),
@@ -296,6 +335,14 @@ def bench_mixed(args, wl, dev):
         "append_step_us": round(app.mean() * 1e6, 3),
         "fp8_workspace_gbs": round(b_ws / wsd.mean() / 1e9, 2),
         "fp8_workspace_us": round(wsd.mean() * 1e6, 3),
+        "fp8_rows_us": round(float(np.median(rows_ms)) * 1e3, 3),
+        "fp8_rows_gbs": round(b_rows / (float(np.median(rows_ms)) / 1e3) / 1e9, 2),
+        "extend_attn_us": round(ext_s * 1e6, 2),
+        "extend_attn_tflops": round(ext_tf, 2),
+        "extend_roofline": {"bound": "mfma", "achieved": round(ext_tf, 2), "peak": PEAK_F16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(ext_tf / PEAK_F16_TFLOPS, 4),
+                            "kernel": "nvfp4_fp8_extend_attn (extend_kernel)", "flops_per_call": int(ext_flops),
+                            "query_tokens": t_ext, "key_pairs": int(pairs)},
         "quantize_append_bulk_gbs": round(sum(append_bytes) / (sum(append_ms) / 1e3) / 1e9, 2),
         "bytes_per_step": int(b_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",

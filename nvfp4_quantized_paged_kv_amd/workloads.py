@@ -74,9 +74,13 @@ class MixedStep:
     dec_q: torch.Tensor         # [56, Hq, 128]
     ext_table: torch.Tensor     # [8, width] block-table rows of the extended sequences
     ext_prefix: torch.Tensor    # [8] cached prefix lengths (L)
-    ext_offsets: torch.Tensor   # [9] workspace token offsets
+    ext_offsets: torch.Tensor   # [9] workspace token offsets: sequence i's rows [prefix | 2048-token chunk]
+    ext_rows: torch.Tensor      # [T_new] workspace row of each new token of an extended sequence, -1 otherwise
+    ext_q: torch.Tensor         # [8 * 2048, Hq, 128] queries of the extend chunks
+    ext_q_offsets: torch.Tensor  # [9] chunk query rows per extended sequence
     max_dec_len: int
     max_prefix: int
+    ext_chunk: int              # tokens per extend chunk
 
 
 def build_mixed_step(wl: synth.Workload, layer_idx: int, device="cuda", on_chunk=None, timed=False) -> MixedStep:
@@ -95,7 +99,12 @@ def build_mixed_step(wl: synth.Workload, layer_idx: int, device="cuda", on_chunk
     slots = (bt[new_seq, new_pos // synth.PAGE].astype(np.int64) * synth.PAGE + new_pos % synth.PAGE).astype(np.int32)
     dec_lens = np.asarray(lens)[dec] + synth.MIXED_DECODE_NEW
     prefix = np.asarray(lens)[ext]
-    offs = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32)
+    chunk = synth.MIXED_EXTEND_NEW
+    offs = np.concatenate([[0], np.cumsum(prefix + chunk)]).astype(np.int32)  # room for prefix and chunk
+    ext_rows = np.full(T_new, -1, np.int64)
+    for i, b in enumerate(ext):
+        mine = np.flatnonzero(new_seq == b)
+        ext_rows[mine] = offs[i] + new_pos[mine]  # new_pos runs lens[b] .. lens[b] + chunk - 1
     return MixedStep(
         filled=fl, lens=lens, extend=ext, decode=dec, new_k=new_k, new_v=new_v,
         new_slots=torch.from_numpy(slots).to(device), new_seq=new_seq, new_pos=new_pos,
@@ -105,4 +114,7 @@ def build_mixed_step(wl: synth.Workload, layer_idx: int, device="cuda", on_chunk
         ext_table=torch.from_numpy(np.ascontiguousarray(bt[ext])).to(device),
         ext_prefix=torch.from_numpy(prefix.astype(np.int32)).to(device),
         ext_offsets=torch.from_numpy(offs).to(device),
-        max_dec_len=int(dec_lens.max()), max_prefix=int(prefix.max()))
+        ext_rows=torch.from_numpy(ext_rows.astype(np.int32)).to(device),
+        ext_q=synth.queries(ext.size * chunk, wl.q_heads, wl.in_dtype, device, 5, layer_idx),
+        ext_q_offsets=torch.from_numpy((np.arange(ext.size + 1) * chunk).astype(np.int32)).to(device),
+        max_dec_len=int(dec_lens.max()), max_prefix=int(prefix.max()), ext_chunk=chunk)
