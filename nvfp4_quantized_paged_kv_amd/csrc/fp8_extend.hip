@@ -21,9 +21,9 @@
 //                     row block (lane: key 16kb + l%16, dims 32*(l/16)..+31;
 //                     Q in the same permuted dim order, so no shuffles)
 //   online softmax in fp32 (exp2 domain, lazy max as in the decode kernel)
-//   O[token][dim]  += P . V : 8 dim blocks x 2 key blocks x
-//                     mfma_f32_16x16x16_f16 (the S^T lane layout is the
-//                     PV A-operand layout)
+//   O[token][dim]  += P . V : 8 dim blocks x mfma_f32_16x16x32_f16 (the
+//                     weights stay where the S^T layout put them: the
+//                     contraction index is mapped onto the 32 keys to match)
 // The FP32 per-tensor workspace scales go on the logits (K) and on the output
 // (V); Q is converted to f16 after an exact power-of-two prescale (float32 Q
 // as an f16 hi + lo pair), as in the decode kernel.
@@ -329,17 +329,25 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
       }
     }
 
-    // ---- O += P . V: lane (dim 16*db + er, keys 16*kb + 4*eq .. +3) from transposed V
+    // ---- O += P . V, one 16x16x32 MFMA per dim block: its contraction index
+    // k = 8*eq + j stands for key 4*eq + j (j < 4) of key block 0 and key
+    // 16 + 4*eq + j - 4 of key block 1, which is how the S^T layout left the
+    // weights in this lane; V is read from the transposed tile in the same order.
+    half8_t pw[2];
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int rb = 0; rb < 2; ++rb)
+      pw[rb] = __builtin_shufflevector(pa[rb][0], pa[rb][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(&s_v[buf][(16 * db + er) * kVStride + 16 * kb + 4 * eq]);
-        const uint2 hv = {fp8x2_to_f16x2<false>(vw), fp8x2_to_f16x2<true>(vw)};
-        const half4_t b = __builtin_bit_cast(half4_t, hv);
+    for (int db = 0; db < 8; ++db) {
+      const uint8_t* vp = &s_v[buf][(16 * db + er) * kVStride + 4 * eq];
+      const uint32_t v0 = *reinterpret_cast<const uint32_t*>(vp);       // keys 4*eq .. +3
+      const uint32_t v1 = *reinterpret_cast<const uint32_t*>(vp + 16);  // keys 16 + 4*eq .. +3
+      const uint4 hv = {fp8x2_to_f16x2<false>(v0), fp8x2_to_f16x2<true>(v0), fp8x2_to_f16x2<false>(v1),
+                        fp8x2_to_f16x2<true>(v1)};
+      const half8_t b = __builtin_bit_cast(half8_t, hv);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[rb][kb], b, acc[rb][db], 0, 0, 0);
-      }
+      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rb], b, acc[rb][db], 0, 0, 0);
+    }
   }
   if (!active) return;
 
