@@ -14,9 +14,9 @@
 // extend_kernel work split: one workgroup per (16 chunk tokens, kv head,
 // sequence); its rows are the 16 tokens of each of the G query heads of the
 // kv head.  Wave w owns heads 2w and 2w+1 (two 16-row blocks).  Keys stream
-// through LDS in tiles of 32: K rows as FP8 (padded), V transposed to
-// [dim][key] while it is written, so a lane's PV operand (4 keys of one dim)
-// is one 32-bit read.  Per tile and wave:
+// through LDS in tiles of 32, widened to f16 while they are staged (once per
+// workgroup): K rows (padded), V transposed to [dim][key] so that a lane's PV
+// operand (4 + 4 keys of one dim) is two 64-bit reads.  Per tile and wave:
 //   S^T[key][token] = K . Q^T : 2 key blocks x 4 mfma_f32_16x16x32_f16 per
 //                     row block (lane: key 16kb + l%16, dims 32*(l/16)..+31;
 //                     Q in the same permuted dim order, so no shuffles)
@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(Fp8RowsParams p) {
 // ------------------------------------------------------------ extend attention
 constexpr int kExtTok = 16;                        // chunk tokens per workgroup
 constexpr int kExtKeys = 32;                       // keys per LDS tile
-constexpr int kKStride = 144;                      // LDS bytes per K row (128 + 16 pad)
-constexpr int kVStride = 36;                       // LDS bytes per transposed V row (32 keys + 4 pad)
+constexpr int kKStride = 272;                      // LDS bytes per K row: 128 f16 + 16 pad
+constexpr int kVStride = 80;                       // LDS bytes per transposed V row: 32 f16 keys + 16 pad
+constexpr int kBufferFlags = 0x00020000;           // gfx9 buffer resource word 3 for raw dword access
 constexpr int kKTileBytes = kExtKeys * kKStride;
 constexpr int kVTileBytes = kHeadDim * kVStride;
 constexpr float kExtLazyMax = 8.0f;                // log2 headroom before the running max moves
@@ -150,40 +151,55 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
   const int n_all = P + t0 + 1;      // keys every token of the tile sees
   const int n_kt = (n_keys + kExtKeys - 1) / kExtKeys;
 
-  // ---- tile loads: thread tid < 256 moves 16 K bytes (key tid/8, bytes 16*(tid%8))
-  // and a 4x4 block of V (keys 4*(tid/32)..+3, dims 4*(tid%32)..+3)
+  // ---- tile loads: thread tid < 256 moves 16 K bytes (key tid/8, dims 16*(tid%8)..+15)
+  // and a 4x4 block of V (keys 4*(tid%8)..+3, dims 4*(tid/8)..+3: consecutive lanes
+  // take consecutive key groups, so their transposed LDS stores hit distinct banks).  Raw buffer
+  // loads through a per-tile descriptor over the sequence's valid rows: rows past
+  // them (or past the workspace) read as 0, and a thread's offsets never change.
   const bool loader = tid < 256;
   const int kk = tid >> 3, kc = tid & 7;
-  const int vg = (tid >> 5) & 7, vd = tid & 31;
+  const int vg = tid & 7, vd = (tid >> 3) & 31;
+  const int row_bytes = H * kHeadDim;
+  const int64_t valid_rows = (woff >= 0 && woff < p.ws_capacity) ? min((int64_t)n_keys, (int64_t)p.ws_capacity - woff) : 0;
+  const int ko = (kk * H + h) * kHeadDim + 16 * kc;
+  int vo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vo[j] = ((4 * vg + j) * H + h) * kHeadDim + 4 * vd;
+  auto tile_rsrc = [&](const uint8_t* base, int kt) {
+    const int64_t r0 = (int64_t)kt * kExtKeys;
+    const int64_t rows = max((int64_t)0, min((int64_t)kExtKeys, valid_rows - r0));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base) + (woff + r0) * row_bytes, 0,
+                                             (int)(rows * row_bytes), kBufferFlags);
+  };
   uint4 kreg = {0u, 0u, 0u, 0u};
   uint32_t vreg[4] = {0u, 0u, 0u, 0u};
-  auto key_row = [&](int key) -> int64_t {  // workspace row of key, or -1 outside [0, n_keys) / the buffer
-    const int64_t r = woff + key;
-    return (key < n_keys && r >= 0 && r < p.ws_capacity) ? r : -1;
-  };
   auto load_tile = [&](int kt) {
     if (!loader) return;
-    const int64_t rk = key_row(kt * kExtKeys + kk);
-    kreg = rk >= 0 ? *reinterpret_cast<const uint4*>(p.ws_k + (rk * H + h) * kHeadDim + 16 * kc) : uint4{0u, 0u, 0u, 0u};
+    const auto rk = tile_rsrc(p.ws_k, kt);
+    const auto rv = tile_rsrc(p.ws_v, kt);
+    kreg = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t rv = key_row(kt * kExtKeys + 4 * vg + j);
-      vreg[j] = rv >= 0 ? *reinterpret_cast<const uint32_t*>(p.ws_v + (rv * H + h) * kHeadDim + 4 * vd) : 0u;
-    }
+    for (int j = 0; j < 4; ++j) vreg[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo[j], 0, 0);
   };
+  // The tile goes into LDS already widened to f16 (once per workgroup, not per wave).
   auto store_tile = [&](int buf) {
     if (!loader) return;
-    *reinterpret_cast<uint4*>(&s_k[buf][kk * kKStride + 16 * kc]) = kreg;
-    // 4x4 byte transpose: out[e] = dim 4*vd+e of keys 4*vg .. 4*vg+3
+    uint8_t* kp = &s_k[buf][kk * kKStride + 32 * kc];
+    *reinterpret_cast<uint4*>(kp) = uint4{fp8x2_to_f16x2<false>(kreg.x), fp8x2_to_f16x2<true>(kreg.x),
+                                          fp8x2_to_f16x2<false>(kreg.y), fp8x2_to_f16x2<true>(kreg.y)};
+    *reinterpret_cast<uint4*>(kp + 16) = uint4{fp8x2_to_f16x2<false>(kreg.z), fp8x2_to_f16x2<true>(kreg.z),
+                                               fp8x2_to_f16x2<false>(kreg.w), fp8x2_to_f16x2<true>(kreg.w)};
+    // 4x4 byte transpose: t[e] = dim 4*vd+e of keys 4*vg .. 4*vg+3
     const uint32_t a_lo = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
     const uint32_t a_hi = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
     const uint32_t b_lo = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x05010400u);
     const uint32_t b_hi = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x07030602u);
-    uint8_t* vt = &s_v[buf][(4 * vd) * kVStride + 4 * vg];
-    *reinterpret_cast<uint32_t*>(vt) = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);
-    *reinterpret_cast<uint32_t*>(vt + kVStride) = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
-    *reinterpret_cast<uint32_t*>(vt + 2 * kVStride) = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
-    *reinterpret_cast<uint32_t*>(vt + 3 * kVStride) = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+    const uint32_t t[4] = {__builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u), __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u),
+                           __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u), __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u)};
+    uint8_t* vt = &s_v[buf][(4 * vd) * kVStride + 8 * vg];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<uint2*>(vt + e * kVStride) = uint2{fp8x2_to_f16x2<false>(t[e]), fp8x2_to_f16x2<true>(t[e])};
   };
   load_tile(0);
 
@@ -262,17 +278,12 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
     float4_t S[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* kp = &s_k[buf][(16 * kb + er) * kKStride + 32 * eq];
-      const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(kp + 16);
-      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const uint8_t* kp = &s_k[buf][(16 * kb + er) * kKStride + 64 * eq];  // f16 dims 32*eq .. +31
       S[kb][0] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
       S[kb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 hw = {fp8x2_to_f16x2<false>(kw[2 * c]), fp8x2_to_f16x2<true>(kw[2 * c]),
-                          fp8x2_to_f16x2<false>(kw[2 * c + 1]), fp8x2_to_f16x2<true>(kw[2 * c + 1])};
-        const half8_t a = __builtin_bit_cast(half8_t, hw);
+        const half8_t a = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(kp + 16 * c));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           S[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qa[rb][c], S[kb][rb], 0, 0, 0);
@@ -339,12 +350,10 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
       pw[rb] = __builtin_shufflevector(pa[rb][0], pa[rb][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint8_t* vp = &s_v[buf][(16 * db + er) * kVStride + 4 * eq];
-      const uint32_t v0 = *reinterpret_cast<const uint32_t*>(vp);       // keys 4*eq .. +3
-      const uint32_t v1 = *reinterpret_cast<const uint32_t*>(vp + 16);  // keys 16 + 4*eq .. +3
-      const uint4 hv = {fp8x2_to_f16x2<false>(v0), fp8x2_to_f16x2<true>(v0), fp8x2_to_f16x2<false>(v1),
-                        fp8x2_to_f16x2<true>(v1)};
-      const half8_t b = __builtin_bit_cast(half8_t, hv);
+      const uint8_t* vp = &s_v[buf][(16 * db + er) * kVStride + 8 * eq];
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vp);       // f16 keys 4*eq .. +3
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 32);  // f16 keys 16 + 4*eq .. +3
+      const half8_t b = __builtin_bit_cast(half8_t, uint4{v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rb], b, acc[rb][db], 0, 0, 0);
     }
