@@ -473,6 +473,24 @@ def main():
         l = i % L
         nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
     dec_avg_s = back_to_back(stream, args.steps, dec_call)
+
+    # ---- multi-token decode: T = 16 / G new tokens per sequence (the last T of
+    # the context) fill the 16-row MFMA tile in the same pass over the cache
+    multi = None
+    T_m = 16 // (Hq // H)
+    if T_m >= 2:
+        q_m = [synth.queries(B * T_m, Hq, wl.in_dtype, dev, 6, l).reshape(B, T_m, Hq, 128) for l in range(L)]
+        out_m = torch.empty((B, T_m, Hq, 128), dtype=torch.float32, device=dev)
+        ws_m = torch.zeros(nk.decode_multi_workspace_bytes(B, T_m, Hq, H, ctx), dtype=torch.uint8, device=dev)
+
+        def multi_call(i):
+            l = i % L
+            nk.paged_decode_attn_multi(layers[l], q_m[l], tables[l], seq_lens, ctx, sm, out=out_m, workspace=ws_m)
+        multi_s = back_to_back(stream, args.steps, multi_call)
+        b_multi = B * ctx * H * 144 + B * pages_per_seq * 4 + B * T_m * Hq * 128 * (in_b + 4)
+        multi = {"q_per_seq": T_m, "us": round(multi_s * 1e6, 3), "gbs": round(b_multi / multi_s / 1e9, 2),
+                 "query_tokens_per_s": round(B * T_m / multi_s, 1),
+                 "time_vs_one_token": round(multi_s / dec_avg_s, 4)}
     achieved = bytes_decode / dec_avg_s / 1e9
 
     # ---- FP8 workspace dequant on the same cache: 8 sequences' full prefixes (extend path)
@@ -521,6 +539,7 @@ def main():
         "decode_attn_gbs_events": round(achieved, 2),
         "decode_attn_us": round(dec_avg_s * 1e6, 3),
         "decode_attn_us_per_call_events": round(float(dec_ms.mean()) * 1e3, 3),
+        "decode_multi_token": multi,
         "append_step_us": round(float(app_ms.mean()) * 1e3, 3),
         "quantize_append_bulk_gbs": round(app_total_b / app_total_s / 1e9, 2),
         "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),

@@ -141,6 +141,34 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
                                                  int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                                                  size_t workspace_bytes, void* stream);
 
+/* Decode of several new query tokens per sequence (multi-token or
+ * speculative decoding; the survey's next row after the three data flows).
+ * It is the decode data flow of blog section 3 with q_per_seq query tokens
+ * that share one pass over the cache: their G * q_per_seq query rows fill the
+ * 16-row MFMA tile that plain decode fills only to G.  The q_per_seq new
+ * tokens are already appended: query token i < q_per_seq of sequence b sits
+ * at position seq_lens[b] - q_per_seq + i and attends over tokens
+ * t <= that position (causal among the new tokens).
+ *   q   : [batch][q_per_seq][num_q_heads][128] of q_dtype (16-byte aligned).
+ *   out : [batch][q_per_seq][num_q_heads][128] float32.
+ *   workspace: >= nvfp4_paged_decode_multi_workspace_bytes(batch, q_per_seq,
+ *          num_q_heads, num_kv_heads, max_seq_len) bytes; the same contract as
+ *          nvfp4_paged_decode_attn's (zero-filled once, left zeroed, calls
+ *          that share it ordered on one stream).
+ *   Other arguments as nvfp4_paged_decode_attn; seq_lens[b] < q_per_seq
+ *   leaves the tokens with no key at zero output.
+ *   Supported: (num_q_heads / num_kv_heads) * q_per_seq <= 16,
+ *   q_per_seq * num_q_heads * 512 < 2^31, and the batch and size limits of
+ *   nvfp4_paged_decode_attn.  q_per_seq == 1 is nvfp4_paged_decode_attn. */
+NVFP4_API size_t nvfp4_paged_decode_multi_workspace_bytes(int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
+                                                          int32_t num_kv_heads, int32_t max_seq_len);
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* layer, const void* q,
+                                                       nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq,
+                                                       int32_t num_q_heads, const int32_t* block_table,
+                                                       int32_t block_table_stride, const int32_t* seq_lens,
+                                                       int32_t max_seq_len, float sm_scale, float* out,
+                                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Extend-path dequantization into one FP8 workspace pair (blog section 3,
  * second data flow: cached NVFP4 pages are dequantized into a single FP8
  * workspace that every layer reuses; nmedialink.com, Fig. 3: values are taken

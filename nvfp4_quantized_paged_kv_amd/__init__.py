@@ -38,6 +38,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_kv_quantize_append",
     "nvfp4_paged_decode_workspace_bytes",
     "nvfp4_paged_decode_attn",
+    "nvfp4_paged_decode_multi_workspace_bytes",
+    "nvfp4_paged_decode_attn_multi",
     "nvfp4_dequant_to_fp8_workspace",
     "nvfp4_fp8_rows_to_workspace",
     "nvfp4_fp8_extend_attn",
@@ -81,6 +83,11 @@ def _load():
     L.nvfp4_paged_decode_workspace_bytes.restype = sz
     L.nvfp4_paged_decode_attn.argtypes = [lp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
     L.nvfp4_paged_decode_attn.restype = ctypes.c_int
+    L.nvfp4_paged_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.nvfp4_paged_decode_multi_workspace_bytes.restype = sz
+    L.nvfp4_paged_decode_attn_multi.argtypes = [lp, vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz,
+                                                vp]
+    L.nvfp4_paged_decode_attn_multi.restype = ctypes.c_int
     L.nvfp4_dequant_to_fp8_workspace.argtypes = [lp, vp, i32, i32, vp, vp, i32, f32, f32, vp, vp, i32, vp]
     L.nvfp4_dequant_to_fp8_workspace.restype = ctypes.c_int
     L.nvfp4_fp8_rows_to_workspace.argtypes = [vp, vp, ctypes.c_int, i32, i64, i32, vp, f32, f32, vp, vp, i32, vp]
@@ -217,6 +224,38 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
                                      block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(sm_scale),
                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "nvfp4_paged_decode_attn")
+    return out
+
+
+def decode_multi_workspace_bytes(batch: int, q_per_seq: int, num_q_heads: int, num_kv_heads: int,
+                                 max_seq_len: int) -> int:
+    return int(lib.nvfp4_paged_decode_multi_workspace_bytes(batch, q_per_seq, num_q_heads, num_kv_heads, max_seq_len))
+
+
+def paged_decode_attn_multi(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                            max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode of q [B, T, Hq, 128] (T new tokens per sequence, causal among them); returns f32 [B, T, Hq, 128]."""
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, T, Hq, 128] tensor")
+    B, T, Hq, _ = q.shape
+    _dev_i32(block_table, "block_table")
+    _dev_i32(seq_lens, "seq_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table must be [B, stride] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, T, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (B, T, Hq, HEAD_DIM):
+        raise ValueError("out must be a contiguous float32 [B, T, Hq, 128] tensor")
+    need = decode_multi_workspace_bytes(B, T, Hq, layer.num_kv_heads, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = layer.c_struct()
+    st = lib.nvfp4_paged_decode_attn_multi(ctypes.byref(c), _ptr(q), _dtype_code(q), B, T, Hq, _ptr(block_table),
+                                           block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+                                           _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_paged_decode_attn_multi")
     return out
 
 

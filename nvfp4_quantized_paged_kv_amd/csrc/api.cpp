@@ -80,22 +80,35 @@ static bool decode_size_ok(int32_t batch, int32_t num_kv_heads, int32_t max_seq_
 
 NVFP4_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                                     int32_t max_seq_len) {
-  if (batch < 0 || batch > kMaxDecodeBatch || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
-  if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return 0;
-  if (!decode_size_ok(batch, num_kv_heads, max_seq_len)) return 0;
-  return decode_geometry(batch, num_q_heads, num_kv_heads, max_seq_len).workspace_bytes;
+  return nvfp4_paged_decode_multi_workspace_bytes(batch, 1, num_q_heads, num_kv_heads, max_seq_len);
 }
 
-NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
-                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
-                                                 int32_t block_table_stride, const int32_t* seq_lens,
-                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
-                                                 size_t workspace_bytes, void* stream) {
+NVFP4_API size_t nvfp4_paged_decode_multi_workspace_bytes(int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
+                                                          int32_t num_kv_heads, int32_t max_seq_len) {
+  if (batch < 0 || batch > kMaxDecodeBatch || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (q_per_seq < 1 || num_q_heads % num_kv_heads != 0) return 0;
+  if ((int64_t)(num_q_heads / num_kv_heads) * q_per_seq > kMaxGroup) return 0;
+  if (!decode_size_ok(batch, num_kv_heads, max_seq_len)) return 0;
+  return decode_geometry(batch, num_q_heads / num_kv_heads * q_per_seq, num_kv_heads, max_seq_len).workspace_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Decode of q_per_seq query tokens per sequence (1 for plain decode).
+nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype, int32_t batch,
+                           int32_t q_per_seq, int32_t num_q_heads, const int32_t* block_table,
+                           int32_t block_table_stride, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
   const nvfp4_status_t st = check_layer(layer);
   if (st != NVFP4_OK) return st;
-  if (!dtype_ok(q_dtype) || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!dtype_ok(q_dtype) || batch < 0 || q_per_seq < 1 || num_q_heads <= 0 || max_seq_len < 0)
+    return NVFP4_ERR_INVALID_ARGUMENT;
   if (num_q_heads % layer->num_kv_heads != 0) return NVFP4_ERR_INVALID_ARGUMENT;
-  if (num_q_heads / layer->num_kv_heads > kMaxGroup || batch > kMaxDecodeBatch) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t G = num_q_heads / layer->num_kv_heads;
+  if (G * q_per_seq > kMaxGroup || batch > kMaxDecodeBatch) return NVFP4_ERR_UNSUPPORTED;
+  if ((int64_t)q_per_seq * num_q_heads * kHeadDim * 4 >= ((int64_t)1 << 31)) return NVFP4_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
   if (!decode_size_ok(batch, layer->num_kv_heads, max_seq_len)) return NVFP4_ERR_UNSUPPORTED;
   if (batch == 0) return NVFP4_OK;
@@ -103,7 +116,8 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   if ((int64_t)block_table_stride * kPageSize < (int64_t)max_seq_len || block_table_stride < 0)
     return NVFP4_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16)) return NVFP4_ERR_UNSUPPORTED;
-  const DecodeGeometry geo = decode_geometry(batch, num_q_heads, layer->num_kv_heads, max_seq_len);
+  const int32_t R = (int32_t)(G * q_per_seq);
+  const DecodeGeometry geo = decode_geometry(batch, R, layer->num_kv_heads, max_seq_len);
   if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARGUMENT;
   const double qk = (double)sm_scale * (double)layer->k_global * 1.4426950408889634;  // log2(e)
@@ -116,13 +130,14 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   p.q = q;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
-  const int64_t G = num_q_heads / layer->num_kv_heads;
   p.counters = static_cast<int32_t*>(workspace);
   p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + geo.counters_bytes);
   p.out = out;
   p.num_pages = layer->num_pages;
   p.H = layer->num_kv_heads;
   p.G = (int32_t)G;
+  p.T = q_per_seq;
+  p.R = R;
   p.Hq = num_q_heads;
   p.batch = batch;
   p.bt_stride = block_table_stride;
@@ -131,6 +146,29 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
   p.qk_scale_log2 = (float)qk;
   p.v_global = layer->v_global;
   return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  return decode_impl(layer, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride, seq_lens, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* layer, const void* q,
+                                                       nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq,
+                                                       int32_t num_q_heads, const int32_t* block_table,
+                                                       int32_t block_table_stride, const int32_t* seq_lens,
+                                                       int32_t max_seq_len, float sm_scale, float* out,
+                                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(layer, q, q_dtype, batch, q_per_seq, num_q_heads, block_table, block_table_stride, seq_lens,
+                     max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* layer, const int32_t* block_table,

@@ -88,22 +88,21 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Q of one lane: dims 32*q4 .. 32*q4+31 of row `lane_row` of a group whose G
-// rows start at `group_base`; rows past the group read as 0 (buffer range).
-// The raw words are loaded first and widened later, so other loads can be
-// issued in between.
+// Q of one lane: dims 32*q4 .. 32*q4+31 of the query row that starts `row_off`
+// elements after the sequence's first query element `seq_base`; row_off < 0
+// reads as 0 (past the buffer range).  The raw words are loaded first and
+// widened later, so other loads can be issued in between.
 template <bool QF32>
 struct QRaw {
   uint4 w[QF32 ? 8 : 4];
 };
 
 template <bool QF32>
-__device__ __forceinline__ QRaw<QF32> load_q_raw(const void* q, int64_t group_base, int G, int lane_row, int q4) {
+__device__ __forceinline__ QRaw<QF32> load_q_raw(const void* q, int64_t seq_base, int seq_elems, int row_off, int q4) {
   constexpr int esz = QF32 ? 4 : 2;
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(q) + group_base * kHeadDim * esz), 0,
-      G * kHeadDim * esz, 0x00020000);
-  const int off = (lane_row * kHeadDim + 32 * q4) * esz;
+      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(q) + seq_base * esz), 0, seq_elems * esz, 0x00020000);
+  const int off = row_off >= 0 ? (row_off + 32 * q4) * esz : seq_elems * esz;
   QRaw<QF32> r;
 #pragma unroll
   for (int i = 0; i < (QF32 ? 8 : 4); ++i)
@@ -208,7 +207,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // A value every lane of the wave holds (read from LDS): keep it in an SGPR.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <bool QF32, bool kPlane>
+// kMulti: several query tokens per sequence (per-row causal limits); the
+// one-token instance keeps the plain decode's code.
+template <bool QF32, bool kPlane, bool kMulti>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ int s_pref[kMaxDecodeBatch + 1];  // exclusive prefix of pages per sequence
   __shared__ int s_wsum[kWaves];
@@ -223,6 +224,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int lane = tid & 63;
   const int q4 = lane >> 4;
   const int B = p.batch, H = p.H, G = p.G;
+  const int NT = kMulti ? p.T : 1, R = kMulti ? p.R : G;  // NT query tokens per sequence; R = G*NT query rows per unit
+  // output row of query row r (token r / G, head r % G) of unit (b, h): out is [B][NT][Hq][128]
+  auto out_row = [&](int b, int h, int r) -> int64_t {
+    return kMulti ? ((int64_t)b * NT + r / G) * p.Hq + (int64_t)h * G + r % G : (int64_t)b * p.Hq + (int64_t)h * G + r;
+  };
   const PlaneRsrc planes = plane_rsrc<kPlane>(p);
 
   // ---- pages of every sequence and their exclusive prefix sums (4 sequences per thread)
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // ---- empty sequences: zero their outputs (spread over the workgroups)
   for (int b = wg; b < B; b += p.num_groups) {
     if (uni(s_pref[b + 1]) == uni(s_pref[b]))
-      for (int e = tid; e < p.Hq * kHeadDim; e += kThreads) p.out[(int64_t)b * p.Hq * kHeadDim + e] = 0.0f;
+      for (int e = tid; e < NT * p.Hq * kHeadDim; e += kThreads) p.out[(int64_t)b * NT * p.Hq * kHeadDim + e] = 0.0f;
   }
 
   // ---- this workgroup's share [x0, x1) of the flattened work.  Unit u = b*H+h
@@ -318,8 +324,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
     // The segment's independent loads go out together: Q, the first chunk's
     // page indices and the sequence length.
-    // ---- Q as the B operand: lane (q head r of the group, dims 32*q4 .. 32*q4+31)
-    const QRaw<QF32> q_raw = load_q_raw<QF32>(p.q, (int64_t)b * p.Hq + (int64_t)h * G, G, er, eq);
+    // ---- Q as the B operand: lane (query row r = token i * G + head g of the group,
+    // dims 32*q4 .. 32*q4+31); rows past R read as 0
+    const int ti = kMulti ? er / G : 0, tg = kMulti ? er - (er / G) * G : er;
+    const QRaw<QF32> q_raw = load_q_raw<QF32>(p.q, (int64_t)b * NT * p.Hq * kHeadDim, NT * p.Hq * kHeadDim,
+                                              er < R ? (ti * p.Hq + h * G + tg) * kHeadDim : -1, eq);
     // this wave's pages of a chunk [c0, c1): pg_j = c0 + wave + kWaves*j, j < n_mine <= 128;
     // their indices sit in two lane registers (pages j and j + 64 in lane j), read
     // through a descriptor that ends at the chunk's end (entries past it read 0)
@@ -384,7 +393,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto process = [&](const PageRegs& cur, int valid) {
+    // rem: tokens of the sequence from this page's first slot on (0 for a page
+    // index outside the cache); the page holds min(rem, 16) of them
+    auto process = [&](const PageRegs& cur, int rem) {
 
       // ---- S^T = K . Q^T over the page; lane (q head r, tokens 4*q4 .. 4*q4+3)
       const half2_t ks0 = e4m3_pair_to_f16_scaled(cur.ksw & 0xFFu, cur.ksw & 0xFFu);
@@ -411,10 +422,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // ---- online softmax (log2 domain) on t = S * tscale (tscale >= 0, so the
       // maximum of t is the maximum of S times tscale).  Raw v_exp_f32: weights
       // below 2^-126 of the running max flush to 0, which f16 could not hold.
-      if (valid != kPageSize) {  // tokens past the sequence end (or a bad page index)
+      if (rem - (NT - 1) < kPageSize) {  // tokens past the end of some query row (or a bad page index)
+        // query token i of NT sits at position seq_len - NT + i: its row sees
+        // NT-1-i fewer keys than the sequence holds
+        const int r = threadIdx.x & 15;
+        const int vlim = kMulti ? rem - (r < R ? NT - 1 - r / G : 0) : rem;  // keys of this page the lane's row sees
   #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * q4 + i >= valid) S[i] = -__builtin_inff();
+          if (4 * q4 + i >= vlim) S[i] = -__builtin_inff();
       }
       const float pm = vmax_over_groups(vmax(vmax3(S[0], S[1], S[2]), S[3])) * tscale;  // -inf: all masked
       if (__any(pm > m_lim)) {
@@ -438,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
       // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3)
       uint32_t vsw = cur.vsw;
-      if (valid != kPageSize) {
-        const int nv = min(max(valid - 4 * q4, 0), 4);
+      if (rem < kPageSize) {
+        const int nv = min(max(rem - 4 * q4, 0), 4);
         vsw &= nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);  // zero the scales of tokens past the end
       }
       // scale bytes (s0, s1) -> f16 pair (s0 << 7, s1 << 7): bytes moved to 0 and 2, then one shift
@@ -466,10 +481,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     };
 
     while (true) {
-      // valid tokens of page j (0 for a page index outside the cache): uniform
+      // tokens of the sequence from page j's first slot on, 0 for a page index
+      // outside the cache (uniform)
       auto valid_of = [&](int j) {
-        return (unsigned)page_of(j) < (unsigned)p.num_pages ? min(kPageSize, seq_len - (c0 + wave + kWaves * j) * kPageSize)
-                                                            : 0;
+        return (unsigned)page_of(j) < (unsigned)p.num_pages ? seq_len - (c0 + wave + kWaves * j) * kPageSize : 0;
       };
       // Two register sets, unrolled by two: each set is loaded one page ahead of
       // its use and refilled right after, so no register copy waits on a load in
@@ -516,8 +531,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int u = b * H + h;
     const bool whole = seg_begin == 0 && seg_end == pages_b;
     const int64_t slot = (int64_t)u + wg;
-    for (int e = mt; e < G * kHeadDim; e += kThreads) {
-      const int g = e >> 7, d = e & 127;
+    for (int e = mt; e < R * kHeadDim; e += kThreads) {
+      const int g = e >> 7, d = e & 127;  // g: query row of the unit
       float M = -__builtin_inff();
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
@@ -529,9 +544,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         L += s_l[w][g] * f;
       }
       if (whole) {
-        p.out[((int64_t)b * p.Hq + (int64_t)h * G + g) * kHeadDim + d] = L > 0.0f ? O / L * p.v_global : 0.0f;
+        p.out[out_row(b, h, g) * kHeadDim + d] = L > 0.0f ? O / L * p.v_global : 0.0f;
       } else {
-        float* ps = p.part + (slot * G + g) * kPartStride;
+        float* ps = p.part + (slot * R + g) * kPartStride;
         store_coherent(ps + d, O);
         if (d == 0) {
           store_coherent(ps + kHeadDim, M);
@@ -550,19 +565,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
       __syncthreads();
       if (uni(s_flag)) {  // every other share of this unit is stored: merge them all
-        for (int e = mt; e < G * kHeadDim; e += kThreads) {
+        for (int e = mt; e < R * kHeadDim; e += kThreads) {
           const int g = e >> 7, d = e & 127;
           float M = -__builtin_inff();
           for (int w2 = w_first; w2 <= w_last; ++w2)
-            M = fmaxf(M, load_coherent(p.part + (((int64_t)u + w2) * G + g) * kPartStride + kHeadDim));
+            M = fmaxf(M, load_coherent(p.part + (((int64_t)u + w2) * R + g) * kPartStride + kHeadDim));
           float O = 0.0f, L = 0.0f;
           for (int w2 = w_first; w2 <= w_last; ++w2) {
-            const float* ps = p.part + (((int64_t)u + w2) * G + g) * kPartStride;
+            const float* ps = p.part + (((int64_t)u + w2) * R + g) * kPartStride;
             const float f = exp2f(load_coherent(ps + kHeadDim) - M);
             O += load_coherent(ps + d) * f;
             L += load_coherent(ps + kHeadDim + 1) * f;
           }
-          p.out[((int64_t)b * p.Hq + (int64_t)h * G + g) * kHeadDim + d] = L > 0.0f ? O / L * p.v_global : 0.0f;
+          p.out[out_row(b, h, g) * kHeadDim + d] = L > 0.0f ? O / L * p.v_global : 0.0f;
         }
         if (tid == 0) __hip_atomic_store(p.counters + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -574,18 +589,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
 }  // namespace
 
-DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
+DecodeGeometry decode_geometry(int32_t batch, int32_t rows_per_unit, int32_t num_kv_heads, int32_t max_seq_len) {
   DecodeGeometry geo{0, 0, 0};
-  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0) return geo;
+  if (batch <= 0 || num_kv_heads <= 0 || rows_per_unit <= 0) return geo;
   const int64_t max_pages = ((int64_t)max(max_seq_len, 0) + kPageSize - 1) / kPageSize;
   // about one CU per 64 pages of the largest possible call, at most one workgroup per CU
   int64_t groups = ((int64_t)batch * num_kv_heads * max_pages + 63) / 64;
   groups = groups < 1 ? 1 : (groups > kMaxGroups ? kMaxGroups : groups);
   geo.num_groups = (int32_t)groups;
-  const int64_t G = num_q_heads / num_kv_heads;
   const int64_t units = (int64_t)batch * num_kv_heads;
   geo.counters_bytes = (size_t)((units * 4 + 255) / 256 * 256);
-  geo.workspace_bytes = geo.counters_bytes + (size_t)((units + groups) * G * kPartStride * sizeof(float));
+  geo.workspace_bytes = geo.counters_bytes + (size_t)((units + groups) * rows_per_unit * kPartStride * sizeof(float));
   return geo;
 }
 
@@ -595,14 +609,18 @@ hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream
   // one descriptor per plane when every tile offset fits the 32-bit buffer offset
   const bool plane = (int64_t)p.num_pages * p.H * kTileCodeBytes <= (int64_t)UINT32_MAX;
   const bool f32 = q_dtype == NVFP4_DTYPE_F32;
-  if (f32 && plane)
-    hipLaunchKernelGGL((decode_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
-  else if (f32)
-    hipLaunchKernelGGL((decode_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
-  else if (plane)
-    hipLaunchKernelGGL((decode_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p); };
+  if (p.T > 1) {
+    if (f32 && plane) go(decode_kernel<true, true, true>);
+    else if (f32) go(decode_kernel<true, false, true>);
+    else if (plane) go(decode_kernel<false, true, true>);
+    else go(decode_kernel<false, false, true>);
+  } else {
+    if (f32 && plane) go(decode_kernel<true, true, false>);
+    else if (f32) go(decode_kernel<true, false, false>);
+    else if (plane) go(decode_kernel<false, true, false>);
+    else go(decode_kernel<false, false, false>);
+  }
   return hipGetLastError();
 }
 

@@ -40,15 +40,17 @@ struct DecodeParams {
   const uint8_t* k_scales;
   const uint8_t* v_codes;
   const uint8_t* v_scales;
-  const void* q;           // [B][Hq][128]
+  const void* q;           // [B][T][Hq][128]
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* part;             // [B*H + num_groups][G][128 + 2]: unnormalised O, running max (log2), sum
+  float* part;             // [B*H + num_groups][R][128 + 2]: unnormalised O, running max (log2), sum
   int32_t* counters;       // [B*H] arrival counters of split sequences; zero between calls
-  float* out;              // [B][Hq][128]
+  float* out;              // [B][T][Hq][128]
   int32_t num_pages;
   int32_t H;
   int32_t G;
+  int32_t T;               // query tokens per sequence
+  int32_t R;               // query rows per (sequence, kv head) unit: G * T <= 16
   int32_t Hq;
   int32_t batch;
   int32_t bt_stride;
@@ -75,7 +77,7 @@ struct DecodeGeometry {
   size_t counters_bytes;
   size_t workspace_bytes;
 };
-DecodeGeometry decode_geometry(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len);
+DecodeGeometry decode_geometry(int32_t batch, int32_t rows_per_unit, int32_t num_kv_heads, int32_t max_seq_len);
 
 hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
 

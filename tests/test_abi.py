@@ -197,3 +197,24 @@ def test_fp8_extend_checks():
     assert _ext(nk, pl=0) == 1
     assert _ext(nk, q=FAKE + 4) == 2
     assert _ext(nk, wk=FAKE + 8) == 2
+
+
+def test_multi_token_decode_checks_and_sizes():
+    nk = _lib()
+    L = _layer(nk)
+
+    def call(T=2, hq=64, ws=1 << 20, q=FAKE, dtype=1, batch=4):
+        return nk.lib.nvfp4_paged_decode_attn_multi(ctypes.byref(L), ctypes.c_void_p(q), dtype, batch, T, hq,
+                                                    ctypes.c_void_p(FAKE), 8, ctypes.c_void_p(FAKE), 100, 0.088,
+                                                    ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ws, None)
+    assert call(T=0) == 1
+    assert call(T=3) == 2            # 8 heads per kv head x 3 tokens > 16 rows
+    assert call(hq=60) == 1
+    assert call(q=FAKE + 4) == 2
+    assert call(ws=16) == 3          # workspace too small
+    assert call(batch=0) == 0
+    m = nk.decode_multi_workspace_bytes
+    assert m(32, 1, 64, 8, 8192) == nk.decode_workspace_bytes(32, 64, 8, 8192)
+    assert m(32, 2, 64, 8, 8192) > nk.decode_workspace_bytes(32, 64, 8, 8192)   # 16 partial rows per unit, not 8
+    assert m(32, 3, 64, 8, 8192) == 0 and m(32, 0, 64, 8, 8192) == 0
+    assert m(4, 16, 16, 16, 100) > 0                                               # one head per kv head, 16 tokens

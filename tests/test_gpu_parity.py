@@ -259,3 +259,56 @@ def test_dequant_ws_bitexact(g_one):
     assert np.array_equal(ws_k[:total].cpu().numpy(), ref_k)
     assert np.array_equal(ws_v[:total].cpu().numpy(), ref_v)
     assert not ws_k[total:].any() and not ws_v[total:].any()
+
+
+# ------------------------------------------------------- multi-token decode
+def _multi_both(c, T, Hq, qdt, seed, max_seq_len=None):
+    """Decode of T new tokens per sequence against the oracle: query token i of
+    sequence b is a plain decode over its first lens[b] - (T-1-i) tokens."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    B = len(c.lens)
+    q = synth.queries(B * T, Hq, qdt, "cpu", seed, 2).reshape(B, T, Hq, 128)
+    msl = max(max(c.lens), 1) if max_seq_len is None else max_seq_len
+    bt = c.bt
+    need = (msl + 15) // 16
+    if bt.shape[1] < need:
+        bt = np.concatenate([bt, np.zeros((B, need - bt.shape[1]), np.int32)], 1)
+    out = nk.paged_decode_attn_multi(c.layer, q.cuda().contiguous(), torch.from_numpy(np.ascontiguousarray(bt)).cuda(),
+                                     torch.tensor(c.lens, dtype=torch.int32, device="cuda"), msl, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    vlens = np.array([max(c.lens[b] - (T - 1 - i), 0) for b in range(B) for i in range(T)], np.int32)
+    vbt = np.repeat(c.bt, T, axis=0)
+    ref = oracle.decode_attention(c.planes, c.g_k, c.g_v, host_f32(q).reshape(B * T, Hq, 128), vbt, vlens,
+                                  float(np.float32(1 / math.sqrt(128))))
+    return out.cpu().numpy().reshape(B * T * Hq, 128), ref
+
+
+@pytest.mark.parametrize("lens,H,G,T,qdt", [
+    ([40, 17, 300], 2, 8, 2, torch.bfloat16),      # 16 query rows: the full MFMA tile
+    ([1, 2, 3, 64, 65], 2, 4, 4, torch.bfloat16),   # tokens without keys, page boundaries
+    ([100], 1, 1, 16, torch.float32),               # 16 tokens of one head
+    ([257, 31], 3, 3, 5, torch.bfloat16),           # odd group: 15 rows
+    ([9000, 20, 6000], 2, 8, 2, torch.bfloat16),    # units shared by several workgroups (partials)
+])
+def test_decode_multi_matches_oracle(lens, H, G, T, qdt):
+    _say(f"case: multi-token decode lens={lens} H={H} G={G} T={T} q={qdt}")
+    c = build_cache(lens, H, torch.bfloat16, "sparse6", 0.003, False, seed=sum(lens) + 17 * T)
+    got, ref = _multi_both(c, T, H * G, qdt, seed=T)
+    err = row_rel_err(got, ref)
+    assert err.max() <= ATTN_TOL, (err.max(), int(np.argmax(err)))
+
+
+def test_decode_multi_one_token_is_plain_decode():
+    """T = 1 through the multi-token entry point gives the plain decode's result bit for bit."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: multi-token decode T=1 vs plain decode")
+    c = build_cache([700, 33, 1500], 2, torch.bfloat16, "sparse6", 0.003, False, seed=91)
+    q = synth.queries(3, 16, torch.bfloat16, "cpu", 91, 1).cuda()
+    bt = torch.from_numpy(c.bt).cuda()
+    sl = torch.tensor(c.lens, dtype=torch.int32, device="cuda")
+    a = nk.paged_decode_attn(c.layer, q, bt, sl, 1500, 0.088)
+    b = nk.paged_decode_attn_multi(c.layer, q.reshape(3, 1, 16, 128).contiguous(), bt, sl, 1500, 0.088)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b.reshape(3, 16, 128))
