@@ -449,14 +449,35 @@ def main():
         step(i % L)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, wall clock
+    # ---- the same step in one launch: the decode kernel appends the new token itself
+    kn_f = [newk[l].reshape(B, 1, H, 128) for l in range(L)]
+    vn_f = [newv[l].reshape(B, 1, H, 128) for l in range(L)]
+    q_f = [qs[l].reshape(B, 1, Hq, 128) for l in range(L)]
+    out_f = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device=dev)
+
+    def fused_step(l):
+        nk.paged_decode_step(layers[l], kn_f[l], vn_f[l], q_f[l], tables[l], seq_lens, ctx, sm, out=out_f,
+                             workspace=workspace)
+
+    for i in range(args.warmup):
+        fused_step(i % L)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, wall clock; the step in one launch (the value),
+    # then as two launches (quantize-append kernel, decode kernel) for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused_step(i % L)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i % L)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    wall_two = time.perf_counter() - t0
 
     # ---- same steps again with HIP events on the launch stream (per-call durations)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -473,6 +494,7 @@ def main():
         l = i % L
         nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
     dec_avg_s = back_to_back(stream, args.steps, dec_call)
+    fused_s = back_to_back(stream, args.steps, lambda i: fused_step(i % L))
 
     # ---- multi-token decode: T = 16 / G new tokens per sequence (the last T of
     # the context) fill the 16-row MFMA tile in the same pass over the cache
@@ -534,12 +556,15 @@ def main():
         "data": "synthetic (seeded torch generators)",
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
                    "context": ctx, "page_size": 16, "layers_rotated": L,
-                   "step": "append 1 token/seq + decode attention, one layer"},
+                   "step": "append 1 token/seq + decode attention, one layer, in one launch (nvfp4_paged_decode_step)"},
         "pct_of_peak": round(100 * bytes_step / (wall / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
         "decode_attn_gbs_events": round(achieved, 2),
         "decode_attn_us": round(dec_avg_s * 1e6, 3),
         "decode_attn_us_per_call_events": round(float(dec_ms.mean()) * 1e3, 3),
         "decode_multi_token": multi,
+        "step_one_launch_us_b2b": round(fused_s * 1e6, 3),
+        "step_two_launches": {"ms_per_step": round(wall_two * 1e3 / args.steps, 5),
+                              "value": round(bytes_step / (wall_two / args.steps) / 1e9, 2)},
         "append_step_us": round(float(app_ms.mean()) * 1e3, 3),
         "quantize_append_bulk_gbs": round(app_total_b / app_total_s / 1e9, 2),
         "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),

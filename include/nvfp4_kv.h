@@ -169,6 +169,28 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
                                                        int32_t max_seq_len, float sm_scale, float* out,
                                                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step in one launch: quantize-on-append of each sequence's
+ * q_per_seq new tokens (blog section 3, first data flow) and the decode
+ * attention over the cache that now holds them (third data flow), fused
+ * (the survey's next row).  The new tokens of sequence b sit at positions
+ * seq_lens[b] - q_per_seq + i, i < q_per_seq (seq_lens already counts them);
+ * their slots come from block_table.  The result is the same as
+ * nvfp4_kv_quantize_append of those tokens followed by
+ * nvfp4_paged_decode_attn_multi: the same cache bytes and the same output.
+ * The workgroup that reads a page holding a new token quantizes and stores
+ * that token itself before it loads the page, so no workgroup waits on another.
+ *   k_new, v_new : [batch][q_per_seq][num_kv_heads][128] of dtype (the
+ *                  query's dtype), 16-byte aligned.  Positions < 0
+ *                  (seq_lens[b] < q_per_seq) and out-of-range page indices
+ *                  are skipped.
+ *   Other arguments and the workspace as nvfp4_paged_decode_attn_multi. */
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_step(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                 const void* q, nvfp4_dtype_t dtype, int32_t batch, int32_t q_per_seq,
+                                                 int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream);
+
 /* Extend-path dequantization into one FP8 workspace pair (blog section 3,
  * second data flow: cached NVFP4 pages are dequantized into a single FP8
  * workspace that every layer reuses; nmedialink.com, Fig. 3: values are taken

@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "nvfp4_paged_decode_attn",
     "nvfp4_paged_decode_multi_workspace_bytes",
     "nvfp4_paged_decode_attn_multi",
+    "nvfp4_paged_decode_step",
     "nvfp4_dequant_to_fp8_workspace",
     "nvfp4_fp8_rows_to_workspace",
     "nvfp4_fp8_extend_attn",
@@ -88,6 +89,9 @@ def _load():
     L.nvfp4_paged_decode_attn_multi.argtypes = [lp, vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz,
                                                 vp]
     L.nvfp4_paged_decode_attn_multi.restype = ctypes.c_int
+    L.nvfp4_paged_decode_step.argtypes = [lp, vp, vp, vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
+                                          sz, vp]
+    L.nvfp4_paged_decode_step.restype = ctypes.c_int
     L.nvfp4_dequant_to_fp8_workspace.argtypes = [lp, vp, i32, i32, vp, vp, i32, f32, f32, vp, vp, i32, vp]
     L.nvfp4_dequant_to_fp8_workspace.restype = ctypes.c_int
     L.nvfp4_fp8_rows_to_workspace.argtypes = [vp, vp, ctypes.c_int, i32, i64, i32, vp, f32, f32, vp, vp, i32, vp]
@@ -256,6 +260,38 @@ def paged_decode_attn_multi(layer: KVCacheLayer, q: torch.Tensor, block_table: t
                                            block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(sm_scale),
                                            _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "nvfp4_paged_decode_attn_multi")
+    return out
+
+
+def paged_decode_step(layer: KVCacheLayer, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """One decode step in one launch: append k_new, v_new [B, T, H, 128] at the last T positions
+    (seq_lens counts them) and attend with q [B, T, Hq, 128]; returns f32 [B, T, Hq, 128]."""
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, T, Hq, 128] tensor")
+    B, T, Hq, _ = q.shape
+    for x in (k_new, v_new):
+        if x.shape != (B, T, layer.num_kv_heads, HEAD_DIM) or x.dtype != q.dtype or not x.is_contiguous():
+            raise ValueError("k_new / v_new must be contiguous [B, T, H, 128] tensors of the query's dtype")
+    _dev_i32(block_table, "block_table")
+    _dev_i32(seq_lens, "seq_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table must be [B, stride] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, T, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (B, T, Hq, HEAD_DIM):
+        raise ValueError("out must be a contiguous float32 [B, T, Hq, 128] tensor")
+    need = decode_multi_workspace_bytes(B, T, Hq, layer.num_kv_heads, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = layer.c_struct()
+    st = lib.nvfp4_paged_decode_step(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(q), _dtype_code(q), B, T, Hq,
+                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                                     float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_paged_decode_step")
     return out
 
 

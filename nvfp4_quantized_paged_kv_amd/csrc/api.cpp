@@ -96,11 +96,13 @@ NVFP4_API size_t nvfp4_paged_decode_multi_workspace_bytes(int32_t batch, int32_t
 
 namespace {
 
-// Decode of q_per_seq query tokens per sequence (1 for plain decode).
-nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype, int32_t batch,
-                           int32_t q_per_seq, int32_t num_q_heads, const int32_t* block_table,
-                           int32_t block_table_stride, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
-                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+// Decode of q_per_seq query tokens per sequence (1 for plain decode); with
+// k_new / v_new the kernel first appends the q_per_seq new tokens itself.
+nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new, const void* q,
+                           nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+                           int32_t max_seq_len, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   const nvfp4_status_t st = check_layer(layer);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(q_dtype) || batch < 0 || q_per_seq < 1 || num_q_heads <= 0 || max_seq_len < 0)
@@ -116,6 +118,8 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_d
   if ((int64_t)block_table_stride * kPageSize < (int64_t)max_seq_len || block_table_stride < 0)
     return NVFP4_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16)) return NVFP4_ERR_UNSUPPORTED;
+  if ((k_new == nullptr) != (v_new == nullptr)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return NVFP4_ERR_UNSUPPORTED;
   const int32_t R = (int32_t)(G * q_per_seq);
   const DecodeGeometry geo = decode_geometry(batch, R, layer->num_kv_heads, max_seq_len);
   if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
@@ -144,7 +148,10 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* q, nvfp4_d
   p.max_seq_len = max_seq_len;
   p.num_groups = geo.num_groups;
   p.qk_scale_log2 = (float)qk;
+  p.k_global = layer->k_global;
   p.v_global = layer->v_global;
+  p.k_new = k_new;
+  p.v_new = v_new;
   return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -157,8 +164,8 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
                                                  int32_t block_table_stride, const int32_t* seq_lens,
                                                  int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                                                  size_t workspace_bytes, void* stream) {
-  return decode_impl(layer, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride, seq_lens, max_seq_len,
-                     sm_scale, out, workspace, workspace_bytes, stream);
+  return decode_impl(layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* layer, const void* q,
@@ -167,8 +174,19 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
                                                        int32_t block_table_stride, const int32_t* seq_lens,
                                                        int32_t max_seq_len, float sm_scale, float* out,
                                                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(layer, q, q_dtype, batch, q_per_seq, num_q_heads, block_table, block_table_stride, seq_lens,
-                     max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
+  return decode_impl(layer, nullptr, nullptr, q, q_dtype, batch, q_per_seq, num_q_heads, block_table,
+                     block_table_stride, seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_step(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                 const void* q, nvfp4_dtype_t dtype, int32_t batch, int32_t q_per_seq,
+                                                 int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  if (batch > 0 && (!k_new || !v_new)) return NVFP4_ERR_INVALID_ARGUMENT;
+  return decode_impl(layer, k_new, v_new, q, dtype, batch, q_per_seq, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_dequant_to_fp8_workspace(const nvfp4_kv_layer_t* layer, const int32_t* block_table,

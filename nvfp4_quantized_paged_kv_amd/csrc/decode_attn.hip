@@ -39,8 +39,9 @@
 // last merges the unit's partials, writes the output and resets the counter
 // (no second kernel; agent-scope stores and loads keep the partials coherent
 // across the XCDs' separate L2 caches).
-#include "nvfp4_device.h"
-#include "nvfp4_kv_internal.h"
+#include <type_traits>
+
+#include "nvfp4_quant_device.h"
 
 namespace nvfp4kv {
 namespace {
@@ -207,9 +208,39 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // A value every lane of the wave holds (read from LDS): keep it in an SGPR.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Decode step with its own append: the step's NT new tokens of unit (b, h)
+// sit at positions sl-NT .. sl-1.  The wave that owns the page holding some of
+// them in this segment quantizes and stores them (the exact quantizer of
+// quantize-on-append) before it loads any page, and waits for the stores; no
+// other wave or workgroup reads that page, so nothing waits across waves.
+// k_new / v_new are [B][NT][H][128] in the query's dtype.
+template <bool QF32>
+__device__ __forceinline__ void append_own_tokens(const DecodeParams& p, int b, int h, int NT, int sl, int seg_begin,
+                                                  int seg_end, int wave, int lane) {
+  if (sl <= 0) return;
+  const int first = max(sl - NT, 0);  // first new position
+  for (int pg = first / kPageSize; pg <= (sl - 1) / kPageSize; ++pg) {  // at most 2 pages (NT <= 16)
+    if (pg < seg_begin || pg >= seg_end || (pg - seg_begin) % kWaves != wave) continue;  // not this wave's page
+    const int page = __builtin_amdgcn_readfirstlane(p.block_table[(int64_t)b * p.bt_stride + pg]);
+    if ((unsigned)page >= (unsigned)p.num_pages) continue;  // a bad page index is skipped, as in quantize-on-append
+    const int t_lo = max(first, kPageSize * pg), t_hi = min(sl, kPageSize * pg + kPageSize);
+    for (int j = lane; j < (t_hi - t_lo) * 16; j += 64) {  // (token, tensor, block) jobs
+      const int pos = t_lo + (j >> 4), which = (j >> 3) & 1, blk = j & 7;
+      const int64_t src = (((int64_t)b * NT + (pos - (sl - NT))) * p.H + h) * kHeadDim + 16 * blk;
+      float x[16];
+      if (QF32) load_block<float>(reinterpret_cast<const float*>(which ? p.v_new : p.k_new) + src, x);
+      else load_block<uint16_t>(reinterpret_cast<const uint16_t*>(which ? p.v_new : p.k_new) + src, x);
+      const QuantBlock q = quantize_block16(x, which ? p.v_global : p.k_global);
+      store_block(const_cast<uint8_t*>(which ? p.v_codes : p.k_codes), const_cast<uint8_t*>(which ? p.v_scales : p.k_scales),
+                  p.H, which != 0, page * kPageSize + pos % kPageSize, h, blk, q);
+    }
+  }
+}
+
 // kMulti: several query tokens per sequence (per-row causal limits); the
-// one-token instance keeps the plain decode's code.
-template <bool QF32, bool kPlane, bool kMulti>
+// one-token instance keeps the plain decode's code.  kAppend: the step's new
+// tokens are appended by the kernel itself (append_own_tokens).
+template <bool QF32, bool kPlane, bool kMulti, bool kAppend>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ int s_pref[kMaxDecodeBatch + 1];  // exclusive prefix of pages per sequence
   __shared__ int s_wsum[kWaves];
@@ -350,11 +381,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     auto page_of = [&](int j) {
       return j < 64 ? __builtin_amdgcn_readlane(pidx0, j) : __builtin_amdgcn_readlane(pidx1, j - 64);
     };
-    auto load_mine = [&](int j) { return load_page<kPlane>(p, planes, page_of(min(j, n_mine - 1)), h, lo); };
+    // kAppend: a wave stores the new tokens of its pages, and its stores must
+    // be complete before it loads one of those pages (pages >= new_pg).  The
+    // append goes after the first page's loads unless that page is one of
+    // them, and the wait is deferred to the first load of such a page.
+    const int new_sl = kAppend ? min(uni(len_v), p.max_seq_len) : 0;
+    const int new_pg = kAppend ? max(new_sl - NT, 0) / kPageSize : 0;
+    bool stores_pending = false;
+    auto load_mine = [&](int j) {
+      const int jj = min(j, n_mine - 1);
+      if (kAppend && stores_pending && c0 + wave + kWaves * jj >= new_pg) {
+        wait_vmem();
+        stores_pending = false;
+      }
+      return load_page<kPlane>(p, planes, page_of(jj), h, lo);
+    };
+    const bool append_first = kAppend && c0 + wave >= new_pg;
+    if (append_first) {
+      append_own_tokens<QF32>(p, b, h, NT, new_sl, seg_begin, seg_end, wave, el);
+      stores_pending = true;
+    }
     // the first page's loads go out before the Q conversion below
     PageRegs A;
     if (n_mine > 0) A = load_mine(0);
     __builtin_amdgcn_sched_barrier(0);
+    if (kAppend && !append_first) {
+      append_own_tokens<QF32>(p, b, h, NT, new_sl, seg_begin, seg_end, wave, el);
+      stores_pending = true;
+    }
 
     float qv[32];
     widen_q<QF32>(q_raw, qv);
@@ -610,16 +664,20 @@ hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream
   const bool plane = (int64_t)p.num_pages * p.H * kTileCodeBytes <= (int64_t)UINT32_MAX;
   const bool f32 = q_dtype == NVFP4_DTYPE_F32;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p); };
+  auto pick = [&](auto multi, auto append) {
+    constexpr bool M = decltype(multi)::value, A = decltype(append)::value;
+    if (f32 && plane) go(decode_kernel<true, true, M, A>);
+    else if (f32) go(decode_kernel<true, false, M, A>);
+    else if (plane) go(decode_kernel<false, true, M, A>);
+    else go(decode_kernel<false, false, M, A>);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  const bool append = p.k_new != nullptr;
   if (p.T > 1) {
-    if (f32 && plane) go(decode_kernel<true, true, true>);
-    else if (f32) go(decode_kernel<true, false, true>);
-    else if (plane) go(decode_kernel<false, true, true>);
-    else go(decode_kernel<false, false, true>);
+    if (append) pick(T_{}, T_{}); else pick(T_{}, F_{});
   } else {
-    if (f32 && plane) go(decode_kernel<true, true, false>);
-    else if (f32) go(decode_kernel<true, false, false>);
-    else if (plane) go(decode_kernel<false, true, false>);
-    else go(decode_kernel<false, false, false>);
+    if (append) pick(F_{}, T_{}); else pick(F_{}, F_{});
   }
   return hipGetLastError();
 }

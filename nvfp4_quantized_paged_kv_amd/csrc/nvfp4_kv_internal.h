@@ -57,7 +57,10 @@ struct DecodeParams {
   int32_t max_seq_len;
   int32_t num_groups;      // workgroups of the launch
   float qk_scale_log2;     // sm_scale * k_global * log2(e)
+  float k_global;
   float v_global;
+  const void* k_new;       // decode step with its own append: [B][T][H][128] new K (q dtype), else null
+  const void* v_new;
 };
 
 constexpr int kMaxDecodeBatch = 4096;  // sequences per decode call (prefix sums kept in LDS)

@@ -1,0 +1,141 @@
+// NVFP4 quantization of one 16-value block for the gfx950 kernels: the exact
+// rounding used by quantize-on-append (quant_append.hip) and by the decode
+// step that appends its new tokens itself (decode_attn.hip), so both write
+// the same bytes.  grer.cn blog "NVFP4 KV cache and the memory wall",
+// section 2: 16 consecutive values share an E4M3 scale, the tensor an FP32
+// scale, and a block's amax maps to the E2M1 maximum 6.
+//
+// Scale: bs = E4M3 nearest to amax/(6g), from the correctly rounded float64
+// quotient (no float64 rounding can cross or land on an E4M3 midpoint).
+// Codes, fast path: v_cvt_scalef32_pk_fp4_f32 (nearest E2M1, ties to even,
+// saturating at 6) of |x| times c_lo and times c_hi, two float32 bounds of
+// 1/(bs*g) (the float64 reciprocal scaled by 1 -/+ 2^-21); equal codes are
+// the exact code, and an exact tie always makes them differ.  Codes, exact
+// path (a block where any pair differs, or a zero scale): the magnitude is the
+// number of float32 thresholds u_k the value exceeds, where u_k = RN(mid_k*bs*g)
+// corrected by the sign of the exact FMA residual (ties count for odd k).
+// Every file that includes this is compiled with -ffp-contract=off.
+#pragma once
+
+#include "nvfp4_device.h"
+#include "nvfp4_kv_internal.h"
+
+namespace nvfp4kv {
+
+__device__ __forceinline__ float threshold_f32(float a, float g, bool odd) {
+  const float hi = a * g;                      // rounded product (no contraction)
+  const float lo = __builtin_fmaf(a, g, -hi);  // exact residual a*g - hi
+  const float pred = __int_as_float(__float_as_int(hi) - 1);
+  const bool down = odd ? (lo <= 0.0f) : (lo < 0.0f);
+  return down ? pred : hi;
+}
+
+// Values 2Q and 2Q+1, times c_lo and times c_hi, to E2M1 codes in byte Q%4 of
+// word Q/4 of lo and hi (low nibble = value 2Q).
+template <int Q>
+__device__ __forceinline__ void cvt_pair(uint32_t (&lo)[2], uint32_t (&hi)[2], const float (&x)[16], float c_lo,
+                                         float c_hi) {
+  lo[Q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[Q >> 2], x[2 * Q] * c_lo, x[2 * Q + 1] * c_lo, 1.0f, Q & 3);
+  hi[Q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[Q >> 2], x[2 * Q] * c_hi, x[2 * Q + 1] * c_hi, 1.0f, Q & 3);
+}
+
+template <typename InT>
+__device__ __forceinline__ void load_block(const InT* src, float (&x)[16]);
+
+template <>
+__device__ __forceinline__ void load_block<uint16_t>(const uint16_t* src, float (&x)[16]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_block<float>(const float* src, float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+}
+
+// One quantized block: 16 E2M1 codes (low nibble = even value) and the E4M3 scale byte.
+struct QuantBlock {
+  uint32_t packed[2];
+  uint32_t sb;
+};
+
+__device__ __forceinline__ QuantBlock quantize_block16(const float (&x)[16], float g) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+
+  QuantBlock q;
+  q.sb = e4m3_encode_rne_sat((double)amax / (6.0 * (double)g));
+  const float bs = e4m3_value(q.sb);
+
+  q.packed[0] = q.packed[1] = 0u;
+  bool exact_path = bs == 0.0f;  // zero scale: every code is its sign (threshold path, thresholds +inf)
+  if (!exact_path) {
+    const double rcp = 1.0 / ((double)bs * (double)g);  // bs*g exact in float64
+    const float c_lo = (float)(rcp * (1.0 - 0x1p-21)), c_hi = (float)(rcp * (1.0 + 0x1p-21));
+    uint32_t hi[2] = {0u, 0u};
+    cvt_pair<0>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<1>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<2>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<3>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<4>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<5>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<6>(q.packed, hi, x, c_lo, c_hi);
+    cvt_pair<7>(q.packed, hi, x, c_lo, c_hi);
+    exact_path = (q.packed[0] != hi[0]) | (q.packed[1] != hi[1]);
+  }
+  if (exact_path) {
+    float u[7];
+    const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+    for (int k = 0; k < 7; ++k) u[k] = bs == 0.0f ? __builtin_inff() : threshold_f32(mids[k] * bs, g, (k & 1) != 0);
+    q.packed[0] = q.packed[1] = 0u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float ax = fabsf(x[k]);
+      const bool c2 = ax > u[3];
+      const bool c1 = ax > (c2 ? u[5] : u[1]);
+      const float t0 = c2 ? (c1 ? u[6] : u[4]) : (c1 ? u[2] : u[0]);
+      const bool c0 = ax > t0;
+      const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
+      const uint32_t code = mag | ((__float_as_uint(x[k]) >> 28) & 8u);
+      q.packed[k >> 3] |= code << (4 * (k & 7));
+    }
+  }
+  return q;
+}
+
+// Store block b (dims 16b .. 16b+15) of the token in `slot` (>= 0, inside the
+// cache) and kv head h into one tensor's planes: K tiles are token-major
+// (row o: 64 code bytes, 8 scale bytes); V tiles are token-quad interleaved
+// (byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2, scale byte b*16 + o).
+__device__ __forceinline__ void store_block(uint8_t* codes, uint8_t* scales, int H, bool is_v, int32_t slot, int h,
+                                            int b, const QuantBlock& q) {
+  const int64_t page = (uint32_t)slot / kPageSize;
+  const int o = (int)((uint32_t)slot % kPageSize);
+  const int64_t tile = page * H + h;
+  if (!is_v) {
+    *reinterpret_cast<uint2*>(codes + tile * kTileCodeBytes + o * 64 + 8 * b) = make_uint2(q.packed[0], q.packed[1]);
+    scales[tile * kTileScaleBytes + o * 8 + b] = (uint8_t)q.sb;
+  } else {
+    uint8_t* base = codes + tile * kTileCodeBytes + (o >> 2) * 256 + (o & 3) * 4;
+    *reinterpret_cast<uint32_t*>(base + (2 * b) * 16) = q.packed[0];
+    *reinterpret_cast<uint32_t*>(base + (2 * b + 1) * 16) = q.packed[1];
+    scales[tile * kTileScaleBytes + b * 16 + o] = (uint8_t)q.sb;
+  }
+}
+
+}  // namespace nvfp4kv

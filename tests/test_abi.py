@@ -218,3 +218,19 @@ def test_multi_token_decode_checks_and_sizes():
     assert m(32, 2, 64, 8, 8192) > nk.decode_workspace_bytes(32, 64, 8, 8192)   # 16 partial rows per unit, not 8
     assert m(32, 3, 64, 8, 8192) == 0 and m(32, 0, 64, 8, 8192) == 0
     assert m(4, 16, 16, 16, 100) > 0                                               # one head per kv head, 16 tokens
+
+
+def test_decode_step_checks():
+    nk = _lib()
+    L = _layer(nk)
+
+    def call(k=FAKE, v=FAKE, T=1, ws=1 << 20, batch=4):
+        return nk.lib.nvfp4_paged_decode_step(ctypes.byref(L), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                              ctypes.c_void_p(FAKE), 1, batch, T, 64, ctypes.c_void_p(FAKE), 8,
+                                              ctypes.c_void_p(FAKE), 100, 0.088, ctypes.c_void_p(FAKE),
+                                              ctypes.c_void_p(FAKE), ws, None)
+    assert call(k=0) == 1 and call(v=0) == 1     # the new tokens are required
+    assert call(k=FAKE + 4) == 2                   # alignment
+    assert call(T=3) == 2                          # 8 heads per kv head x 3 tokens > 16 rows
+    assert call(ws=16) == 3
+    assert call(batch=0, k=0, v=0) == 0

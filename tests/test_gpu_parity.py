@@ -312,3 +312,47 @@ def test_decode_multi_one_token_is_plain_decode():
     b = nk.paged_decode_attn_multi(c.layer, q.reshape(3, 1, 16, 128).contiguous(), bt, sl, 1500, 0.088)
     torch.cuda.synchronize()
     assert torch.equal(a, b.reshape(3, 16, 128))
+
+
+# ------------------------------------------------- decode step with its append
+@pytest.mark.parametrize("lens,H,G,T,qdt", [
+    ([33, 16, 17, 1000], 2, 8, 1, torch.bfloat16),   # the new token opens a page / ends one / mid-page
+    ([17, 40, 2], 2, 8, 2, torch.bfloat16),          # two new tokens straddling pages 0 and 1
+    ([12000, 50, 9000], 2, 4, 4, torch.float32),     # units split over several workgroups, float32
+    ([1, 3, 5], 1, 2, 4, torch.bfloat16),            # sequences shorter than the new tokens
+])
+def test_decode_step_equals_append_then_decode(lens, H, G, T, qdt):
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say(f"case: decode step lens={lens} H={H} G={G} T={T} q={qdt}")
+    B, Hq = len(lens), H * G
+    c = build_cache(lens, H, torch.bfloat16, "sparse6", 0.003, False, seed=sum(lens) + 5 * T)
+    kn = synth.kv_values(B * T, H, "sparse6", 0.003, 0, qdt, "cpu", 77, T).reshape(B, T, H, 128)
+    vn = synth.kv_values(B * T, H, "sparse6", 0.003, 1, qdt, "cpu", 77, T).reshape(B, T, H, 128)
+    q = synth.queries(B * T, Hq, qdt, "cpu", 78, T).reshape(B, T, Hq, 128)
+    msl = max(lens)
+    bt = torch.from_numpy(c.bt).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    # the new tokens' slots (positions len - T + i >= 0)
+    pos = [(b, i, lens[b] - T + i) for b in range(B) for i in range(T)]
+    slots = np.array([c.bt[b, p // 16] * 16 + p % 16 if p >= 0 else -1 for (b, i, p) in pos], np.int32)
+    # reference path on a copy of the cache: append, then multi-token decode
+    ref_layer = nk.KVCacheLayer(*(t.clone() for t in (c.layer.k_codes, c.layer.k_scales, c.layer.v_codes,
+                                                        c.layer.v_scales)), c.layer.num_pages, H, c.g_k, c.g_v)
+    nk.quantize_append(ref_layer, kn.reshape(B * T, H, 128).cuda(), vn.reshape(B * T, H, 128).cuda(),
+                       torch.from_numpy(slots).cuda())
+    ref_out = nk.paged_decode_attn_multi(ref_layer, q.cuda(), bt, sl, msl, 1 / math.sqrt(128))
+    out = nk.paged_decode_step(c.layer, kn.cuda(), vn.cuda(), q.cuda(), bt, sl, msl, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        assert torch.equal(getattr(c.layer, name), getattr(ref_layer, name)), name
+    assert torch.equal(out, ref_out)
+    # and against the oracle: the appended bytes, then attention of every (sequence, token) row
+    oracle.quantize_append(c.planes, host_f32(kn).reshape(B * T, H, 128), host_f32(vn).reshape(B * T, H, 128), slots,
+                           c.g_k, c.g_v)
+    assert planes_equal(c.layer, c.planes) == []
+    vlens = np.array([max(lens[b] - (T - 1 - i), 0) for b in range(B) for i in range(T)], np.int32)
+    ref = oracle.decode_attention(c.planes, c.g_k, c.g_v, host_f32(q).reshape(B * T, Hq, 128),
+                                  np.repeat(c.bt, T, axis=0), vlens, float(np.float32(1 / math.sqrt(128))))
+    err = row_rel_err(out.cpu().numpy().reshape(-1, 128), ref)
+    assert err.max() <= ATTN_TOL, err.max()
