@@ -72,6 +72,21 @@ def lib():
     L.nvfp4o_extend_attention.argtypes = [_u8p, _u8p, _int, _flt, _flt, _f32p, _int, _int, _i32p, _i32p, _i32p, _flt,
                                           _i64p, _i64, _f64p]
     L.nvfp4o_extend_attention.restype = None
+    L.nvfp4o_e8m0_value.argtypes = [_int]
+    L.nvfp4o_e8m0_value.restype = _dbl
+    L.nvfp4o_e8m0_scale_for.argtypes = [_dbl]
+    L.nvfp4o_e8m0_scale_for.restype = _int
+    L.nvfp4o_mx_quantize_rows.argtypes = [_f32p, _i64, _u8p, _u8p]
+    L.nvfp4o_mx_quantize_rows.restype = None
+    L.nvfp4o_mx_dequantize_rows.argtypes = [_u8p, _u8p, _i64, _f64p]
+    L.nvfp4o_mx_dequantize_rows.restype = None
+    L.nvfp4o_mx_scatter_rows.argtypes = [_u8p, _u8p, _i64, _int, _i32p, _int, _u8p, _u8p]
+    L.nvfp4o_mx_scatter_rows.restype = None
+    L.nvfp4o_mx_gather_rows.argtypes = [_u8p, _u8p, _i64, _int, _i32p, _int, _u8p, _u8p]
+    L.nvfp4o_mx_gather_rows.restype = None
+    L.nvfp4o_mx_decode_attention.argtypes = [_u8p, _u8p, _u8p, _u8p, _int, _f32p, _int, _i32p, _int, _i32p, _flt,
+                                             _i64p, _i64, _f64p]
+    L.nvfp4o_mx_decode_attention.restype = None
     L.nvfp4o_page_mode_dequant.argtypes = [_f64p, _i64, _i64, _f64p]
     L.nvfp4o_page_mode_dequant.restype = None
     L.nvfp4o_bytes_per_token_head.argtypes = []
@@ -222,6 +237,84 @@ def extend_attention(ws_k: np.ndarray, ws_v: np.ndarray, k_ws_scale: float, v_ws
     lib().nvfp4o_extend_attention(np.ascontiguousarray(ws_k).reshape(-1), np.ascontiguousarray(ws_v).reshape(-1), H,
                                   float(np.float32(k_ws_scale)), float(np.float32(v_ws_scale)), q, Hq, n, qo, wo, pl,
                                   float(np.float32(sm_scale)), rows, rows.size, out)
+    return out
+
+
+# -------------------------------------------------------------------- MXFP4
+def e8m0_value(byte: int) -> float:
+    return lib().nvfp4o_e8m0_value(int(byte))
+
+
+def e8m0_scale_for(amax: float) -> int:
+    return lib().nvfp4o_e8m0_scale_for(float(amax))
+
+
+def mx_quantize_rows(x: np.ndarray):
+    """x: float32 [..., 128] -> (codes uint8 [n, 64], E8M0 scales uint8 [n, 4])."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, 128)
+    n = x.shape[0]
+    codes = np.zeros((n, 64), np.uint8)
+    scales = np.zeros((n, 4), np.uint8)
+    lib().nvfp4o_mx_quantize_rows(x, n, codes, scales)
+    return codes, scales
+
+
+def mx_dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, 64)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, 4)
+    out = np.zeros((codes.shape[0], 128), np.float64)
+    lib().nvfp4o_mx_dequantize_rows(codes, scales, codes.shape[0], out)
+    return out
+
+
+class MxPlanes:
+    """One layer's paged MXFP4 cache: NVFP4-layout code planes, 64-byte scale tiles."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int):
+        self.num_pages = int(num_pages)
+        self.H = int(num_kv_heads)
+        self.k_codes = np.zeros(self.num_pages * self.H * 1024, np.uint8)
+        self.k_scales = np.zeros(self.num_pages * self.H * 64, np.uint8)
+        self.v_codes = np.zeros(self.num_pages * self.H * 1024, np.uint8)
+        self.v_scales = np.zeros(self.num_pages * self.H * 64, np.uint8)
+
+
+def mx_quantize_append(planes: MxPlanes, k: np.ndarray, v: np.ndarray, slot_mapping):
+    """Quantize new tokens k, v (float32 [T, H, 128]) to MXFP4 and write them at their slots."""
+    H = planes.H
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    out = []
+    for x, is_v, cp, sp in ((k, 0, planes.k_codes, planes.k_scales), (v, 1, planes.v_codes, planes.v_scales)):
+        c, s = mx_quantize_rows(x)
+        assert c.shape[0] == slots.size * H
+        lib().nvfp4o_mx_scatter_rows(c, s, slots.size, H, slots, is_v, cp, sp)
+        out += [c, s]
+    return tuple(out)
+
+
+def mx_gather_rows(code_plane, scale_plane, slot_mapping, H: int, is_v: bool):
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    codes = np.zeros((slots.size * H, 64), np.uint8)
+    scales = np.zeros((slots.size * H, 4), np.uint8)
+    lib().nvfp4o_mx_gather_rows(code_plane, scale_plane, slots.size, int(H), slots, int(bool(is_v)), codes, scales)
+    return codes, scales
+
+
+def mx_decode_attention(planes: MxPlanes, q: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+                        sm_scale: float, rows=None) -> np.ndarray:
+    """Decode attention over MXFP4 pages; q: float32 [B, Hq, 128]. Returns float64 [len(rows), 128]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    assert D == 128 and Hq % planes.H == 0
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    assert bt.shape[0] == B
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if rows is None:
+        rows = np.arange(B * Hq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, 128), np.float64)
+    lib().nvfp4o_mx_decode_attention(planes.k_codes, planes.k_scales, planes.v_codes, planes.v_scales, planes.H, q, Hq,
+                                     bt, bt.shape[1], sl, float(np.float32(sm_scale)), rows, rows.size, out)
     return out
 
 

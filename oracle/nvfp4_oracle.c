@@ -31,6 +31,8 @@
  *   R7 low nibble = even element.
  *   R8 a zero scale (amax == 0 or amax/(6g) rounding to 0) gives scale byte 0
  *      and magnitude code 0 for every element.
+ *   R9 MXFP4 (the comparison format) follows the OCP MX v1.0 definition; see
+ *      the MXFP4 section below.
  *
  * Exactness of the float64 quotients used below.  Inputs are float32 (24-bit
  * significands), g is float32, block scales are E4M3 (4-bit significands) and
@@ -244,9 +246,13 @@ void nvfp4o_gather_rows(const uint8_t* code_plane, const uint8_t* scale_plane, i
  *   o   = sum_t p_t * V_hat[t]
  * token t lives in slot block_table[b*bt_stride + t/16]*16 + t%16.  An empty
  * sequence gives o = 0.  rows[i] = b*Hq + qh; out is n_rows x 128 float64. */
-void nvfp4o_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int Hkv, float g_k,
-                             float g_v, const float* q, int Hq, const int32_t* block_table, int bt_stride,
-                             const int32_t* seq_lens, float sm_scale, const int64_t* rows, int64_t n_rows, double* out) {
+typedef double (*plane_value_fn)(const uint8_t* code_plane, const uint8_t* scale_plane, int is_v, int64_t s, int h,
+                                 int H, int d, double g);
+
+static void decode_attention_with(plane_value_fn value, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                                  const uint8_t* vs, int Hkv, float g_k, float g_v, const float* q, int Hq,
+                                  const int32_t* block_table, int bt_stride, const int32_t* seq_lens, float sm_scale,
+                                  const int64_t* rows, int64_t n_rows, double* out) {
   const int G = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < n_rows; ++i) {
@@ -263,7 +269,7 @@ void nvfp4o_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint8_t
     for (int64_t t = 0; t < n; ++t) {
       int64_t slot = (int64_t)block_table[b * bt_stride + t / 16] * 16 + t % 16;
       double acc = 0.0;
-      for (int d = 0; d < 128; ++d) acc += (double)qr[d] * plane_value(kc, ks, 0, slot, h, Hkv, d, g_k);
+      for (int d = 0; d < 128; ++d) acc += (double)qr[d] * value(kc, ks, 0, slot, h, Hkv, d, g_k);
       s[t] = (double)sm_scale * acc;
       if (s[t] > m) m = s[t];
     }
@@ -272,11 +278,18 @@ void nvfp4o_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint8_t
       int64_t slot = (int64_t)block_table[b * bt_stride + t / 16] * 16 + t % 16;
       double pt = exp(s[t] - m);
       l += pt;
-      for (int d = 0; d < 128; ++d) o[d] += pt * plane_value(vc, vs, 1, slot, h, Hkv, d, g_v);
+      for (int d = 0; d < 128; ++d) o[d] += pt * value(vc, vs, 1, slot, h, Hkv, d, g_v);
     }
     free(s);
     for (int d = 0; d < 128; ++d) o[d] /= l;
   }
+}
+
+void nvfp4o_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int Hkv, float g_k,
+                             float g_v, const float* q, int Hq, const int32_t* block_table, int bt_stride,
+                             const int32_t* seq_lens, float sm_scale, const int64_t* rows, int64_t n_rows, double* out) {
+  decode_attention_with(plane_value, kc, ks, vc, vs, Hkv, g_k, g_v, q, Hq, block_table, bt_stride, seq_lens, sm_scale,
+                        rows, n_rows, out);
 }
 
 /* ----------------------------------------------------- FP8 workspace dequant
@@ -377,6 +390,140 @@ void nvfp4o_extend_attention(const uint8_t* ws_k, const uint8_t* ws_v, int Hkv, 
     free(s);
     for (int d = 0; d < 128; ++d) o[d] /= l;
   }
+}
+
+/* ------------------------------------------------------------------ MXFP4
+ * The 4-bit format the pages compare NVFP4 against ([NV] accuracy section and
+ * Fig. 6: NVFP4 KV caches score higher than MXFP4 ones, credited to the finer
+ * blocks and the E4M3 scales; [TC] "E2M1 encoding and two-level scaling":
+ * MXFP4 shares one scale among 32 values where NVFP4 uses 16).  The pages
+ * define no more of it; the rest is the published OCP Microscaling (MX) v1.0
+ * definition of MXFP4 (reading R9):
+ *   - E2M1 elements, 32 consecutive values along head_dim per block (so a
+ *     128-value row has 4 blocks), no tensor-wide scale;
+ *   - the block scale is a power of two X = 2^(byte - 127) stored as an E8M0
+ *     byte (0xFF is NaN);
+ *   - X = 2^(floor(log2 amax) - 2), where 2 is the exponent of the largest
+ *     E2M1 value (6 = 1.5 * 2^2), clamped to 2^-127 .. 2^127; amax = 0 takes
+ *     2^-127 (byte 0);
+ *   - element = sign(x) | E2M1 nearest to |x| / X, ties to the even code and
+ *     saturating at 6 (R1, R3, R5, R7 as for NVFP4).
+ * |x| / X is exact in float64 (a power of two), so the rounding is exact. */
+double nvfp4o_e8m0_value(int byte) { return byte == 255 ? NAN : ldexp(1.0, byte - 127); }
+
+/* E8M0 byte of the MXFP4 block scale for a block maximum amax >= 0. */
+int nvfp4o_e8m0_scale_for(double amax) {
+  if (!(amax > 0.0)) return 0;
+  int e;
+  (void)frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+  int x = (e - 1) - 2;
+  if (x < -127) x = -127;
+  if (x > 127) x = 127;
+  return x + 127;
+}
+
+/* Rows of 128 values to MXFP4: codes n_rows x 64 bytes (byte j = code(2j) |
+ * code(2j+1) << 4), scales n_rows x 4 E8M0 bytes (byte b: values 32b..32b+31). */
+void nvfp4o_mx_quantize_rows(const float* x, int64_t n_rows, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const float* xr = x + r * 128;
+    uint8_t* cr = codes + r * 64;
+    memset(cr, 0, 64);
+    for (int b = 0; b < 4; ++b) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        double a = fabs((double)xr[32 * b + i]);
+        if (a > amax) amax = a;
+      }
+      int sb = nvfp4o_e8m0_scale_for(amax);
+      double X = nvfp4o_e8m0_value(sb);
+      scales[r * 4 + b] = (uint8_t)sb;
+      for (int i = 0; i < 32; ++i) {
+        int d = 32 * b + i;
+        double v = (double)xr[d];
+        int code = (signbit(v) ? 8 : 0) | nvfp4o_e2m1_encode(fabs(v) / X);
+        cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
+      }
+    }
+  }
+}
+
+/* x_hat = E2M1(code) * 2^(scale byte - 127), exact in float64. */
+void nvfp4o_mx_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, double* out) {
+  for (int64_t r = 0; r < n_rows; ++r)
+    for (int d = 0; d < 128; ++d) {
+      int code = (codes[r * 64 + d / 2] >> (4 * (d & 1))) & 15;
+      out[r * 128 + d] = nvfp4o_e2m1_value(code) * nvfp4o_e8m0_value(scales[r * 4 + d / 32]);
+    }
+}
+
+/* MXFP4 pages: the code planes have the NVFP4 code layouts; a scale tile is
+ * 64 bytes (4 per token):
+ *   K scales: tile byte o*4 + d/32         V scales: tile byte (d/32)*16 + o
+ * Tile (p, h) starts at (p*H + h)*64 in a scale plane: 68 bytes per (token,
+ * kv head) per tensor, 17/32 byte per value. */
+static int64_t mx_scale_byte(int is_v, int64_t p, int h, int H, int o, int b) {
+  return (p * H + h) * 64 + (is_v ? b * 16 + o : o * 4 + b);
+}
+
+void nvfp4o_mx_scatter_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_tokens, int H,
+                            const int32_t* slot_mapping, int is_v, uint8_t* code_plane, uint8_t* scale_plane) {
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t p = s / 16;
+    int o = (int)(s % 16);
+    for (int h = 0; h < H; ++h) {
+      const uint8_t* cr = codes + (t * H + h) * 64;
+      for (int d = 0; d < 128; ++d) {
+        int code = (cr[d / 2] >> (4 * (d & 1))) & 15;
+        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+        int sh = 4 * (d & 1);
+        code_plane[at] = (uint8_t)((code_plane[at] & ~(15 << sh)) | (code << sh));
+      }
+      for (int b = 0; b < 4; ++b) scale_plane[mx_scale_byte(is_v, p, h, H, o, b)] = scales[(t * H + h) * 4 + b];
+    }
+  }
+}
+
+void nvfp4o_mx_gather_rows(const uint8_t* code_plane, const uint8_t* scale_plane, int64_t n_tokens, int H,
+                           const int32_t* slot_mapping, int is_v, uint8_t* codes, uint8_t* scales) {
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    int64_t p = s / 16;
+    int o = (int)(s % 16);
+    for (int h = 0; h < H; ++h) {
+      uint8_t* cr = codes + (t * H + h) * 64;
+      memset(cr, 0, 64);
+      for (int d = 0; d < 128; ++d) {
+        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+        int code = (code_plane[at] >> (4 * (d & 1))) & 15;
+        cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
+      }
+      for (int b = 0; b < 4; ++b) scales[(t * H + h) * 4 + b] = scale_plane[mx_scale_byte(is_v, p, h, H, o, b)];
+    }
+  }
+}
+
+static double mx_plane_value(const uint8_t* code_plane, const uint8_t* scale_plane, int is_v, int64_t s, int h, int H,
+                             int d, double g) {
+  (void)g;
+  int64_t p = s / 16;
+  int o = (int)(s % 16);
+  int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+  int code = (code_plane[at] >> (4 * (d & 1))) & 15;
+  return nvfp4o_e2m1_value(code) * nvfp4o_e8m0_value(scale_plane[mx_scale_byte(is_v, p, h, H, o, d / 32)]);
+}
+
+/* Decode attention over MXFP4 pages: the same attention as
+ * nvfp4o_decode_attention with K_hat / V_hat the MXFP4 values. */
+void nvfp4o_mx_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int Hkv,
+                                const float* q, int Hq, const int32_t* block_table, int bt_stride,
+                                const int32_t* seq_lens, float sm_scale, const int64_t* rows, int64_t n_rows,
+                                double* out) {
+  decode_attention_with(mx_plane_value, kc, ks, vc, vs, Hkv, 1.0f, 1.0f, q, Hq, block_table, bt_stride, seq_lens,
+                        sm_scale, rows, n_rows, out);
 }
 
 /* --------------------------------------------------- the page's experiment
