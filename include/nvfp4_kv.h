@@ -142,8 +142,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
                                                  size_t workspace_bytes, void* stream);
 
 /* Decode of several new query tokens per sequence (multi-token or
- * speculative decoding; the survey's next row after the three data flows).
- * It is the decode data flow of blog section 3 with q_per_seq query tokens
+ * speculative decoding).  It is the decode data flow of blog section 3 with q_per_seq query tokens
  * that share one pass over the cache: their G * q_per_seq query rows fill the
  * 16-row MFMA tile that plain decode fills only to G.  The q_per_seq new
  * tokens are already appended: query token i < q_per_seq of sequence b sits
@@ -171,8 +170,8 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
 
 /* One decode step in one launch: quantize-on-append of each sequence's
  * q_per_seq new tokens (blog section 3, first data flow) and the decode
- * attention over the cache that now holds them (third data flow), fused
- * (the survey's next row).  The new tokens of sequence b sit at positions
+ * attention over the cache that now holds them (third data flow), fused.
+ * The new tokens of sequence b sit at positions
  * seq_lens[b] - q_per_seq + i, i < q_per_seq (seq_lens already counts them);
  * their slots come from block_table.  The result is the same as
  * nvfp4_kv_quantize_append of those tokens followed by
@@ -267,6 +266,51 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn(const void* q, nvfp4_dtype_t q_dt
                                                const uint8_t* ws_k, const uint8_t* ws_v, int32_t ws_capacity_tokens,
                                                float k_ws_scale, float v_ws_scale, float sm_scale, float* out,
                                                void* stream);
+
+/* ------------------------------------------------------------------ MXFP4
+ * The 4-bit format the NVFP4 pages compare against (nmedialink.com, accuracy
+ * section and Fig. 6: NVFP4 KV caches score above MXFP4 ones, credited to the
+ * finer blocks and the E4M3 scales; cloud.tencent.com.cn, E2M1 encoding and
+ * two-level scaling section: MXFP4 shares one scale among 32 values).  The
+ * scale rule is the OCP MX v1.0 one, which the pages do not spell out: per
+ * 32 consecutive values along head_dim, X = 2^(floor(log2 amax) - 2) clamped
+ * to 2^-127 .. 2^127 (2^-127 for amax = 0), stored as an E8M0 byte
+ * (X = 2^(byte - 127)); code = sign(x) | E2M1 nearest to |x|/X (ties to even,
+ * saturating at 6).  No tensor-wide scale.  17/32 byte per value.
+ *
+ * Layout: the code planes are laid out exactly as the NVFP4 ones; a scale
+ * tile is 64 bytes:
+ *   k_scales [num_pages][H][64] u8: byte o*4 + d/32 = E8M0 scale of dims
+ *            32*(d/32) .. +31 of token o.
+ *   v_scales [num_pages][H][64] u8: byte (d/32)*16 + o. */
+typedef struct mxfp4_kv_layer {
+  uint8_t* k_codes;  /* [num_pages][H][1024], 16-byte aligned */
+  uint8_t* k_scales; /* [num_pages][H][64], 4-byte aligned */
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;  /* must be 128 */
+  int32_t page_size; /* must be 16 */
+} mxfp4_kv_layer_t;
+
+/* MXFP4 quantize-on-append: the data flow of nvfp4_kv_quantize_append with
+ * the MXFP4 rounding above; arguments, skipping of bad slots, duplicate
+ * slots, limits and errors as there.  Values must be finite. */
+NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append(const mxfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                  const int32_t* slot_mapping, void* stream);
+
+/* Decode attention over MXFP4 pages: the computation, arguments, workspace
+ * (nvfp4_paged_decode_workspace_bytes), limits and errors of
+ * nvfp4_paged_decode_attn, with K_hat / V_hat the MXFP4 values.  Dequantized
+ * values are exact in bf16 and the products run on bf16 MFMA with fp32
+ * accumulation; P enters as a bf16 hi + lo pair. */
+NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn(const mxfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream);
 
 /* Static string for a status code. */
 NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);

@@ -23,6 +23,7 @@ HEAD_DIM = 128
 PAGE_SIZE = 16
 TILE_CODE_BYTES = 1024
 TILE_SCALE_BYTES = 128
+MX_TILE_SCALE_BYTES = 64
 
 NVFP4_OK = 0
 NVFP4_ERR_INVALID_ARGUMENT = 1
@@ -44,6 +45,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_dequant_to_fp8_workspace",
     "nvfp4_fp8_rows_to_workspace",
     "nvfp4_fp8_extend_attn",
+    "mxfp4_kv_quantize_append",
+    "mxfp4_paged_decode_attn",
     "nvfp4_status_string",
 )
 
@@ -62,6 +65,21 @@ class CKVLayer(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("k_global", ctypes.c_float),
         ("v_global", ctypes.c_float),
+    ]
+
+
+class CMxLayer(ctypes.Structure):
+    """Mirror of ``mxfp4_kv_layer_t``."""
+
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
     ]
 
 
@@ -99,6 +117,11 @@ def _load():
     L.nvfp4_fp8_extend_attn.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, f32, f32,
                                         f32, vp, vp]
     L.nvfp4_fp8_extend_attn.restype = ctypes.c_int
+    mp = ctypes.POINTER(CMxLayer)
+    L.mxfp4_kv_quantize_append.argtypes = [mp, vp, vp, ctypes.c_int, i32, i64, vp, vp]
+    L.mxfp4_kv_quantize_append.restype = ctypes.c_int
+    L.mxfp4_paged_decode_attn.argtypes = [mp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    L.mxfp4_paged_decode_attn.restype = ctypes.c_int
     L.nvfp4_status_string.argtypes = [ctypes.c_int]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     return L
@@ -172,9 +195,8 @@ class KVCacheLayer:
         return sum(t.numel() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
 
 
-def quantize_append(layer: KVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-                    stream=None) -> None:
-    """Quantize k, v ([T, H, 128] or [T, H*128], bf16/f32, token-strided) into their slots."""
+def _check_new_kv(layer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor) -> int:
+    """Validate new K/V and their slots; returns the token stride in elements."""
     if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
         raise ValueError("k and v must have the same shape, dtype and strides")
     T = k.shape[0]
@@ -187,9 +209,15 @@ def quantize_append(layer: KVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_
             raise ValueError("k/v must be [T, H, 128] with contiguous heads")
     elif k.dim() != 2 or k.shape[1] != layer.num_kv_heads * HEAD_DIM or k.stride(1) != 1:
         raise ValueError("k/v must be [T, H, 128] or [T, H*128]")
+    return k.stride(0) if T > 0 else layer.num_kv_heads * HEAD_DIM
+
+
+def quantize_append(layer: KVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    stream=None) -> None:
+    """Quantize k, v ([T, H, 128] or [T, H*128], bf16/f32, token-strided) into their slots."""
+    stride = _check_new_kv(layer, k, v, slot_mapping)
     c = layer.c_struct()
-    st = lib.nvfp4_kv_quantize_append(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), T,
-                                      k.stride(0) if T > 0 else layer.num_kv_heads * HEAD_DIM,
+    st = lib.nvfp4_kv_quantize_append(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), k.shape[0], stride,
                                       _ptr(slot_mapping), _stream(stream))
     _check(st, "nvfp4_kv_quantize_append")
 
@@ -208,6 +236,17 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
                       max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Decode attention of q [B, Hq, 128] (bf16/f32) over the cache; returns f32 [B, Hq, 128]."""
+    out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace)
+    c = layer.c_struct()
+    st = lib.nvfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
+                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                                     float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_paged_decode_attn")
+    return out
+
+
+def _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace):
+    """Validate one-token decode arguments; allocate out / workspace when not given."""
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
     B, Hq, _ = q.shape
@@ -223,12 +262,7 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
     if workspace is None and need > 0:
         workspace = decode_workspace(B, Hq, layer.num_kv_heads, max_seq_len, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    c = layer.c_struct()
-    st = lib.nvfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), B, Hq, _ptr(block_table),
-                                     block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(sm_scale),
-                                     _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "nvfp4_paged_decode_attn")
-    return out
+    return out, workspace, ws_bytes
 
 
 def decode_multi_workspace_bytes(batch: int, q_per_seq: int, num_q_heads: int, num_kv_heads: int,
@@ -372,4 +406,55 @@ def fp8_extend_attn(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.
                                    ws_k.shape[0], float(k_ws_scale), float(v_ws_scale), float(sm_scale), _ptr(out),
                                    _stream(stream))
     _check(st, "nvfp4_fp8_extend_attn")
+    return out
+
+
+# -------------------------------------------------------------------- MXFP4
+@dataclass
+class MxKVCacheLayer:
+    """One layer's paged MXFP4 cache: NVFP4-layout code planes and 64-byte E8M0 scale tiles."""
+
+    k_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_codes: torch.Tensor
+    v_scales: torch.Tensor
+    num_pages: int
+    num_kv_heads: int
+
+    @staticmethod
+    def allocate(num_pages: int, num_kv_heads: int, device="cuda") -> "MxKVCacheLayer":
+        n = int(num_pages) * int(num_kv_heads)
+        z = lambda per: torch.zeros(n * per, dtype=torch.uint8, device=device)
+        return MxKVCacheLayer(z(TILE_CODE_BYTES), z(MX_TILE_SCALE_BYTES), z(TILE_CODE_BYTES), z(MX_TILE_SCALE_BYTES),
+                              int(num_pages), int(num_kv_heads))
+
+    def c_struct(self) -> CMxLayer:
+        return CMxLayer(self.k_codes.data_ptr(), self.k_scales.data_ptr(), self.v_codes.data_ptr(),
+                        self.v_scales.data_ptr(), self.num_pages, self.num_kv_heads, HEAD_DIM, PAGE_SIZE)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+
+
+def mx_quantize_append(layer: MxKVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                       stream=None) -> None:
+    """MXFP4 quantize-append of k, v (shapes as quantize_append) into their slots."""
+    stride = _check_new_kv(layer, k, v, slot_mapping)
+    c = layer.c_struct()
+    st = lib.mxfp4_kv_quantize_append(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), k.shape[0], stride,
+                                      _ptr(slot_mapping), _stream(stream))
+    _check(st, "mxfp4_kv_quantize_append")
+
+
+def mx_paged_decode_attn(layer: MxKVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                         max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention of q [B, Hq, 128] over MXFP4 pages; returns f32 [B, Hq, 128]."""
+    out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace)
+    c = layer.c_struct()
+    st = lib.mxfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
+                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                                     float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "mxfp4_paged_decode_attn")
     return out

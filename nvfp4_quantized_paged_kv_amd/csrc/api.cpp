@@ -30,6 +30,17 @@ nvfp4_status_t check_layer(const nvfp4_kv_layer_t* L) {
 
 bool dtype_ok(nvfp4_dtype_t d) { return d == NVFP4_DTYPE_F32 || d == NVFP4_DTYPE_BF16; }
 
+nvfp4_status_t check_mx_layer(const mxfp4_kv_layer_t* L) {
+  if (L == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (L->head_dim != kHeadDim || L->page_size != kPageSize) return NVFP4_ERR_UNSUPPORTED;
+  if (!L->k_codes || !L->k_scales || !L->v_codes || !L->v_scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (L->num_pages <= 0 || L->num_kv_heads <= 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((int64_t)L->num_pages * kPageSize > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(L->k_codes, 16) || !aligned(L->v_codes, 16) || !aligned(L->k_scales, 4) || !aligned(L->v_scales, 4))
+    return NVFP4_ERR_UNSUPPORTED;
+  return NVFP4_OK;
+}
+
 nvfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
 }  // namespace
@@ -102,7 +113,7 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
                            nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
                            const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                            int32_t max_seq_len, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           void* stream, bool mx = false) {
   const nvfp4_status_t st = check_layer(layer);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(q_dtype) || batch < 0 || q_per_seq < 1 || num_q_heads <= 0 || max_seq_len < 0)
@@ -152,6 +163,7 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
   p.v_global = layer->v_global;
   p.k_new = k_new;
   p.v_new = v_new;
+  p.mx = mx ? 1 : 0;
   return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -293,6 +305,50 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn(const void* q, nvfp4_dtype_t q_dt
   p.qk_scale_log2 = (float)qk;
   p.v_scale = v_ws_scale;
   return from_hip(launch_extend(p, q_dtype, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- MXFP4
+
+NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append(const mxfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                  const int32_t* slot_mapping, void* stream) {
+  const nvfp4_status_t st = check_mx_layer(layer);
+  if (st != NVFP4_OK) return st;
+  if (!dtype_ok(dtype) || num_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return NVFP4_OK;
+  if (!k_new || !v_new || !slot_mapping) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (token_stride_elems < (int64_t)layer->num_kv_heads * kHeadDim) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (((int64_t)num_tokens + 15) / 16 * layer->num_kv_heads >= ((int64_t)1 << 31)) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t esize = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || (token_stride_elems * esize) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  MxAppendParams p;
+  p.x[0] = k_new;
+  p.x[1] = v_new;
+  p.codes[0] = layer->k_codes;
+  p.codes[1] = layer->v_codes;
+  p.scales[0] = layer->k_scales;
+  p.scales[1] = layer->v_scales;
+  p.slots = slot_mapping;
+  p.token_stride = token_stride_elems;
+  p.num_tokens = num_tokens;
+  p.H = layer->num_kv_heads;
+  p.num_pages = layer->num_pages;
+  return from_hip(launch_mx_append(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn(const mxfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  const nvfp4_status_t st = check_mx_layer(layer);
+  if (st != NVFP4_OK) return st;
+  // the decode path reads the same fields; MXFP4 has no tensor-wide scale
+  const nvfp4_kv_layer_t as_layer{layer->k_codes,    layer->k_scales,  layer->v_codes,   layer->v_scales,
+                                  layer->num_pages,  layer->num_kv_heads, layer->head_dim, layer->page_size,
+                                  1.0f,              1.0f};
+  return decode_impl(&as_layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -33,6 +33,14 @@
 // magnitude in [2^-10, 2688]).  The FP32 global scales are applied to the
 // logits (K) and to the final output (V).  Q is converted to f16 after an
 // exact power-of-two prescale (float32 Q: as an f16 hi + lo pair).
+// MXFP4 planes (kMX; E8M0 scale per 32 values, the format the NVFP4 pages
+// compare against): a lane's K bytes are one whole 32-value block, so
+// v_cvt_scalef32_pk_bf16_fp4 takes the block's E8M0 byte as its scale operand
+// and returns the exact value in bf16 (every E2M1 code times 2^-127 .. 2^125
+// is a bf16 number; f16 has too few exponent bits).  V is converted per token
+// with that token's scale and re-paired by token with v_perm_b32.  QK^T and PV
+// run on the bf16 MFMAs; P enters as a bf16 hi + lo pair filling the k = 32
+// operand of one 16x16x32 MFMA (the same issue cost as 16x16x16 on gfx950).
 // The waves merge their (max, sum, O) in LDS.  A workgroup that covered a whole
 // unit writes its normalised output; otherwise it stores an unnormalised
 // partial and bumps the unit's arrival counter, and the workgroup that arrives
@@ -60,6 +68,28 @@ constexpr int kPartStride = kHeadDim + 2;                   // floats per (parti
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max must move
 
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// An E8M0 byte as the f32 scale operand of the scaled conversions: the
+// conversion takes the operand's exponent field as the power of two, so the
+// byte goes there (byte 0 means 2^-127; every byte and E2M1 code was checked
+// exact against c * 2^(byte - 127) on gfx950).
+__device__ __forceinline__ float e8m0_f32(uint32_t b) { return __uint_as_float(b << 23); }
+
+// MXFP4 byte SEL of w (two E2M1 codes, low nibble first) times 2^(e - 127) as two bf16, in one word.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+// f32 pair -> bf16 pair (round to nearest even), and the bf16 values back as f32.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Cross-lane max/sum over lanes l, l^16, l^32, l^48 (the 4 token groups of one
 // query head) with the gfx950 row/half swaps: with both operands equal,
@@ -132,9 +162,9 @@ __device__ __forceinline__ void widen_q(const QRaw<QF32>& r, float (&v)[32]) {
 // valid tokens in that page (0 for an out-of-range page index).
 struct PageRegs {
   uint4 kw;      // K codes: token r, dims 32*q4 .. 32*q4+31
-  uint32_t ksw;  // K scales: token r, blocks 2*q4, 2*q4+1
+  uint32_t ksw;  // K scales: token r, blocks 2*q4, 2*q4+1 (MXFP4: block q4)
   uint4 vw;      // V codes: tokens 4*q4 .. 4*q4+3, dims 8*r .. 8*r+7
-  uint32_t vsw;  // V scales: block r/2, tokens 4*q4 .. 4*q4+3
+  uint32_t vsw;  // V scales: block r/2 (MXFP4: r/4), tokens 4*q4 .. 4*q4+3
 };
 
 // Raw buffer loads from a per-page descriptor: the page's base address lives
@@ -158,39 +188,43 @@ struct PlaneRsrc {
   __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
 };
 
-template <bool kPlane>
+template <bool kPlane, bool kMX>
 __device__ __forceinline__ PlaneRsrc plane_rsrc(const DecodeParams& p) {
+  constexpr int kScaleBytes = kMX ? kMxTileScaleBytes : kTileScaleBytes;
   PlaneRsrc r;
   if (kPlane) {
     const int64_t tiles = (int64_t)p.num_pages * p.H;
     r.kc = tile_rsrc(p.k_codes, 0, (int)(uint32_t)(tiles * kTileCodeBytes));
-    r.ks = tile_rsrc(p.k_scales, 0, (int)(uint32_t)(tiles * kTileScaleBytes));
+    r.ks = tile_rsrc(p.k_scales, 0, (int)(uint32_t)(tiles * kScaleBytes));
     r.vc = tile_rsrc(p.v_codes, 0, (int)(uint32_t)(tiles * kTileCodeBytes));
-    r.vs = tile_rsrc(p.v_scales, 0, (int)(uint32_t)(tiles * kTileScaleBytes));
+    r.vs = tile_rsrc(p.v_scales, 0, (int)(uint32_t)(tiles * kScaleBytes));
   }
   return r;
 }
 
-template <bool kPlane>
+template <bool kPlane, bool kMX>
 __device__ __forceinline__ PageRegs load_page(const DecodeParams& p, const PlaneRsrc& pr, int page, int h,
                                               const LaneOffsets& lo) {
+  constexpr int kScaleBytes = kMX ? kMxTileScaleBytes : kTileScaleBytes;
   const bool ok = (unsigned)page < (unsigned)p.num_pages;
   PageRegs d;
   if (kPlane) {
     const uint32_t tile = (uint32_t)(ok ? page : 0) * (uint32_t)p.H + (uint32_t)h;
-    const int so_c = (int)(tile * kTileCodeBytes), so_s = (int)(tile * kTileScaleBytes);
+    const int so_c = (int)(tile * kTileCodeBytes), so_s = (int)(tile * kScaleBytes);
     d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.kc, lo.kc, so_c, 0));
-    d.ksw = __builtin_amdgcn_raw_buffer_load_b16(pr.ks, lo.ks, so_s, 0);
+    d.ksw = kMX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(pr.ks, lo.ks, so_s, 0)
+                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pr.ks, lo.ks, so_s, 0);
     d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.vc, lo.vc, so_c, 0));
     d.vsw = __builtin_amdgcn_raw_buffer_load_b32(pr.vs, lo.vs, so_s, 0);
   } else {
     const int64_t tile = (int64_t)(ok ? page : 0) * p.H + h;
     const auto kc = tile_rsrc(p.k_codes, tile * kTileCodeBytes, kTileCodeBytes);
-    const auto ks = tile_rsrc(p.k_scales, tile * kTileScaleBytes, kTileScaleBytes);
+    const auto ks = tile_rsrc(p.k_scales, tile * kScaleBytes, kScaleBytes);
     const auto vc = tile_rsrc(p.v_codes, tile * kTileCodeBytes, kTileCodeBytes);
-    const auto vs = tile_rsrc(p.v_scales, tile * kTileScaleBytes, kTileScaleBytes);
+    const auto vs = tile_rsrc(p.v_scales, tile * kScaleBytes, kScaleBytes);
     d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, lo.kc, 0, 0));
-    d.ksw = __builtin_amdgcn_raw_buffer_load_b16(ks, lo.ks, 0, 0);
+    d.ksw = kMX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ks, lo.ks, 0, 0)
+                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks, lo.ks, 0, 0);
     d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, lo.vc, 0, 0));
     d.vsw = __builtin_amdgcn_raw_buffer_load_b32(vs, lo.vs, 0, 0);
   }
@@ -239,8 +273,9 @@ __device__ __forceinline__ void append_own_tokens(const DecodeParams& p, int b, 
 
 // kMulti: several query tokens per sequence (per-row causal limits); the
 // one-token instance keeps the plain decode's code.  kAppend: the step's new
-// tokens are appended by the kernel itself (append_own_tokens).
-template <bool QF32, bool kPlane, bool kMulti, bool kAppend>
+// tokens are appended by the kernel itself (append_own_tokens).  kMX: MXFP4
+// planes (one-token decode only).
+template <bool QF32, bool kPlane, bool kMulti, bool kAppend, bool kMX>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ int s_pref[kMaxDecodeBatch + 1];  // exclusive prefix of pages per sequence
   __shared__ int s_wsum[kWaves];
@@ -260,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   auto out_row = [&](int b, int h, int r) -> int64_t {
     return kMulti ? ((int64_t)b * NT + r / G) * p.Hq + (int64_t)h * G + r % G : (int64_t)b * p.Hq + (int64_t)h * G + r;
   };
-  const PlaneRsrc planes = plane_rsrc<kPlane>(p);
+  const PlaneRsrc planes = plane_rsrc<kPlane, kMX>(p);
 
   // ---- pages of every sequence and their exclusive prefix sums (4 sequences per thread)
   int pg[4];
@@ -377,7 +412,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p.seq_lens), 0, 4 * B, kBufferFlags), 4 * b, 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // all of them in flight before Q is used
 
-    const LaneOffsets lo{er * 64 + eq * 16, er * 8 + eq * 2, el * 16, (er >> 1) * 16 + eq * 4};
+    const LaneOffsets lo = kMX ? LaneOffsets{er * 64 + eq * 16, er * 4 + eq, el * 16, (er >> 2) * 16 + eq * 4}
+                               : LaneOffsets{er * 64 + eq * 16, er * 8 + eq * 2, el * 16, (er >> 1) * 16 + eq * 4};
     auto page_of = [&](int j) {
       return j < 64 ? __builtin_amdgcn_readlane(pidx0, j) : __builtin_amdgcn_readlane(pidx1, j - 64);
     };
@@ -394,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         wait_vmem();
         stores_pending = false;
       }
-      return load_page<kPlane>(p, planes, page_of(jj), h, lo);
+      return load_page<kPlane, kMX>(p, planes, page_of(jj), h, lo);
     };
     const bool append_first = kAppend && c0 + wave >= new_pg;
     if (append_first) {
@@ -424,15 +460,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     // exact power of two, with the sign of the logit scale so that tscale >= 0
     // (then the page maximum can be taken on the raw scores)
     const float qscale = __builtin_copysignf(qmax > 0.0f ? __builtin_ldexpf(1.0f, 15 - qe) : 1.0f, p.qk_scale_log2);
-    half8_t qa[4];
-    half8_t ql[4];
+    using QVec = std::conditional_t<kMX, bf16x8_t, half8_t>;
+    using QElem = std::conditional_t<kMX, __bf16, _Float16>;
+    QVec qa[4];
+    QVec ql[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float xq = qv[8 * c + j] * qscale;
-        qa[c][j] = (_Float16)xq;
-        if (QF32) ql[c][j] = (_Float16)(xq - (float)qa[c][j]);
+        const QElem hq = (QElem)xq;
+        qa[c][j] = hq;
+        if (QF32) ql[c][j] = (QElem)(xq - (float)hq);
       }
     // > 0: a zero logit scale becomes FLT_MIN (uniform weights to fp32
     // precision), so masked scores (-inf) always give weight exactly 0
@@ -452,20 +491,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     auto process = [&](const PageRegs& cur, int rem) {
 
       // ---- S^T = K . Q^T over the page; lane (q head r, tokens 4*q4 .. 4*q4+3)
-      const half2_t ks0 = e4m3_pair_to_f16_scaled(cur.ksw & 0xFFu, cur.ksw & 0xFFu);
-      const half2_t ks1 = e4m3_pair_to_f16_scaled(cur.ksw >> 8, cur.ksw >> 8);
       float4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
       const uint32_t kwa[4] = {cur.kw.x, cur.kw.y, cur.kw.z, cur.kw.w};
+      if constexpr (kMX) {
+        const float ksc = e8m0_f32(cur.ksw & 0xFFu);  // the lane's 32 dims are one block
   #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const half2_t sc = c < 2 ? ks0 : ks1;
-        const half2_t e0 = fp4x2_to_f16_x256<0>(kwa[c]) * sc;
-        const half2_t e1 = fp4x2_to_f16_x256<1>(kwa[c]) * sc;
-        const half2_t e2 = fp4x2_to_f16_x256<2>(kwa[c]) * sc;
-        const half2_t e3 = fp4x2_to_f16_x256<3>(kwa[c]) * sc;
-        const half8_t a = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qa[c], S, 0, 0, 0);
-        if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[c], S, 0, 0, 0);
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, make_uint4(fp4x2_to_bf16<0>(kwa[c], ksc), fp4x2_to_bf16<1>(kwa[c], ksc),
+                                   fp4x2_to_bf16<2>(kwa[c], ksc), fp4x2_to_bf16<3>(kwa[c], ksc)));
+          S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qa[c], S, 0, 0, 0);
+          if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[c], S, 0, 0, 0);
+        }
+      } else {
+        const half2_t ks0 = e4m3_pair_to_f16_scaled(cur.ksw & 0xFFu, cur.ksw & 0xFFu);
+        const half2_t ks1 = e4m3_pair_to_f16_scaled(cur.ksw >> 8, cur.ksw >> 8);
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const half2_t sc = c < 2 ? ks0 : ks1;
+          const half2_t e0 = fp4x2_to_f16_x256<0>(kwa[c]) * sc;
+          const half2_t e1 = fp4x2_to_f16_x256<1>(kwa[c]) * sc;
+          const half2_t e2 = fp4x2_to_f16_x256<2>(kwa[c]) * sc;
+          const half2_t e3 = fp4x2_to_f16_x256<3>(kwa[c]) * sc;
+          const half8_t a = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+          S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qa[c], S, 0, 0, 0);
+          if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[c], S, 0, 0, 0);
+        }
       }
       // The MFMA result is read next, possibly across the partial-page branch;
       // the compiler's wait-state insertion missed that path (the first read
@@ -501,8 +552,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
       float pr[4];
   #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], tscale, -m_run));
+      // the rounded product, as in the page maximum (not a fused multiply-add):
+      // t - m_run <= kLazyMax then holds for every logit, however large
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(S[i] * tscale - m_run);
       l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      if constexpr (kMX) {
+        // ---- O += P . V: A = (P hi | P lo) of tokens 4*q4 .. 4*q4+3, B = (V | V) of the same tokens
+        const uint32_t h01 = bf16_pair(pr[0], pr[1]), h23 = bf16_pair(pr[2], pr[3]);
+        const uint32_t l01 = bf16_pair(pr[0] - bf16_lo(h01), pr[1] - bf16_hi(h01));
+        const uint32_t l23 = bf16_pair(pr[2] - bf16_lo(h23), pr[3] - bf16_hi(h23));
+        const bf16x8_t pa8 = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));
+        // lane: token 4*q4 + i in word i (dims 8*r .. 8*r+7, block r/4); tokens past
+        // the end get zero codes and scale 1, so stale bytes never reach the MFMA
+        uint32_t vw[4] = {cur.vw.x, cur.vw.y, cur.vw.z, cur.vw.w};
+        float vsc[4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) vsc[i] = e8m0_f32((cur.vsw >> (8 * i)) & 0xFFu);
+        if (rem < kPageSize) {
+          const int nv = min(max(rem - 4 * q4, 0), 4);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i >= nv) {
+              vw[i] = 0u;
+              vsc[i] = 1.0f;
+            }
+        }
+  #define NVFP4_MX_PV_STEP(C)                                                                        \
+    {                                                                                                \
+      const uint32_t c0 = fp4x2_to_bf16<C>(vw[0], vsc[0]), c1 = fp4x2_to_bf16<C>(vw[1], vsc[1]);    \
+      const uint32_t c2 = fp4x2_to_bf16<C>(vw[2], vsc[2]), c3 = fp4x2_to_bf16<C>(vw[3], vsc[3]);    \
+      const uint32_t e01 = __builtin_amdgcn_perm(c1, c0, 0x05040100u);                               \
+      const uint32_t o01 = __builtin_amdgcn_perm(c1, c0, 0x07060302u);                               \
+      const uint32_t e23 = __builtin_amdgcn_perm(c3, c2, 0x05040100u);                               \
+      const uint32_t o23 = __builtin_amdgcn_perm(c3, c2, 0x07060302u);                               \
+      const bf16x8_t ve = __builtin_bit_cast(bf16x8_t, make_uint4(e01, e23, e01, e23));              \
+      const bf16x8_t vo = __builtin_bit_cast(bf16x8_t, make_uint4(o01, o23, o01, o23));              \
+      acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8, ve, acc[2 * C], 0, 0, 0);           \
+      acc[2 * C + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8, vo, acc[2 * C + 1], 0, 0, 0);   \
+    }
+        NVFP4_MX_PV_STEP(0)
+        NVFP4_MX_PV_STEP(1)
+        NVFP4_MX_PV_STEP(2)
+        NVFP4_MX_PV_STEP(3)
+  #undef NVFP4_MX_PV_STEP
+        return;
+      }
       const half4_t pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 
       // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3)
@@ -664,20 +758,23 @@ hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream
   const bool plane = (int64_t)p.num_pages * p.H * kTileCodeBytes <= (int64_t)UINT32_MAX;
   const bool f32 = q_dtype == NVFP4_DTYPE_F32;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p); };
-  auto pick = [&](auto multi, auto append) {
-    constexpr bool M = decltype(multi)::value, A = decltype(append)::value;
-    if (f32 && plane) go(decode_kernel<true, true, M, A>);
-    else if (f32) go(decode_kernel<true, false, M, A>);
-    else if (plane) go(decode_kernel<false, true, M, A>);
-    else go(decode_kernel<false, false, M, A>);
+  auto pick = [&](auto multi, auto append, auto mx) {
+    constexpr bool M = decltype(multi)::value, A = decltype(append)::value, X = decltype(mx)::value;
+    if (f32 && plane) go(decode_kernel<true, true, M, A, X>);
+    else if (f32) go(decode_kernel<true, false, M, A, X>);
+    else if (plane) go(decode_kernel<false, true, M, A, X>);
+    else go(decode_kernel<false, false, M, A, X>);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   const bool append = p.k_new != nullptr;
-  if (p.T > 1) {
-    if (append) pick(T_{}, T_{}); else pick(T_{}, F_{});
+  if (p.mx) {  // MXFP4 planes: one query token, no append (checked by the host)
+    if (p.T != 1 || append) return hipErrorInvalidValue;
+    pick(F_{}, F_{}, T_{});
+  } else if (p.T > 1) {
+    if (append) pick(T_{}, T_{}, F_{}); else pick(T_{}, F_{}, F_{});
   } else {
-    if (append) pick(F_{}, T_{}); else pick(F_{}, F_{});
+    if (append) pick(F_{}, T_{}, F_{}); else pick(F_{}, F_{}, F_{});
   }
   return hipGetLastError();
 }

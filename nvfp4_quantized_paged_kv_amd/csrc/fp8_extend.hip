@@ -334,7 +334,8 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
       for (int kb = 0; kb < 2; ++kb) {
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][rb][i], tscale[rb], -m_run[rb]));
+        for (int i = 0; i < 4; ++i)  // the rounded product, as in pm: t - m_run <= kExtLazyMax for any logit
+          pr[i] = __builtin_amdgcn_exp2f(S[kb][rb][i] * tscale[rb] - m_run[rb]);
         l_run[rb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         pa[rb][kb] = half4_t{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
       }

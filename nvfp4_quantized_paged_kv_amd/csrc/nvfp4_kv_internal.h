@@ -14,6 +14,7 @@ constexpr int kHeadDim = 128;
 constexpr int kPageSize = 16;
 constexpr int kTileCodeBytes = 1024;  // 16 tokens x 64 code bytes, per (page, kv head)
 constexpr int kTileScaleBytes = 128;  // 16 tokens x 8 E4M3 scale bytes
+constexpr int kMxTileScaleBytes = 64; // MXFP4: 16 tokens x 4 E8M0 scale bytes
 constexpr int kMaxGroup = 16;         // query heads per kv head handled by one MFMA tile
 
 // One tensor (K or V) of a quantize-append call.
@@ -34,6 +35,20 @@ struct AppendParams {
 };
 
 hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream);
+
+// MXFP4 quantize-append: [0] = K, [1] = V, the NVFP4 code layouts with 64-byte scale tiles.
+struct MxAppendParams {
+  const void* x[2];      // [num_tokens][H][128], token stride `token_stride` elements
+  uint8_t* codes[2];
+  uint8_t* scales[2];
+  const int32_t* slots;  // [num_tokens]
+  int64_t token_stride;
+  int32_t num_tokens;
+  int32_t H;
+  int32_t num_pages;
+};
+
+hipError_t launch_mx_append(const MxAppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream);
 
 struct DecodeParams {
   const uint8_t* k_codes;
@@ -61,6 +76,7 @@ struct DecodeParams {
   float v_global;
   const void* k_new;       // decode step with its own append: [B][T][H][128] new K (q dtype), else null
   const void* v_new;
+  int32_t mx;              // 1: the planes hold MXFP4 (E8M0 per 32 values, 64-byte scale tiles)
 };
 
 constexpr int kMaxDecodeBatch = 4096;  // sequences per decode call (prefix sums kept in LDS)

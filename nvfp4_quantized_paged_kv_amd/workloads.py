@@ -9,13 +9,13 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import KVCacheLayer, quantize_append
+from . import KVCacheLayer, MxKVCacheLayer, mx_quantize_append, quantize_append
 from . import synth
 
 
 @dataclass
 class FilledLayer:
-    layer: KVCacheLayer
+    layer: KVCacheLayer         # (MxKVCacheLayer for an MXFP4 fill)
     block_table: np.ndarray     # [B, width] int32 (host)
     block_table_dev: torch.Tensor
     append_ms: list             # per-chunk append durations (HIP events), if timed
@@ -23,15 +23,21 @@ class FilledLayer:
 
 
 def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device="cuda", on_chunk=None,
-                timed: bool = False) -> FilledLayer:
+                timed: bool = False, mx: bool = False) -> FilledLayer:
     """Quantize-append the first fill_lens[b] tokens of every sequence b.
 
     pool_lens[b] >= fill_lens[b] sizes each sequence's pages (room for tokens
-    appended later).  on_chunk(c0, n, k, v, seq, pos) sees every generated chunk."""
+    appended later).  on_chunk(c0, n, k, v, seq, pos) sees every generated chunk.
+    mx: fill an MXFP4 layer with the same tokens, slots and page table."""
     pool_lens = [int(x) for x in pool_lens]
     bt, pool = synth.page_tables(pool_lens, seed=1000 + layer_idx)
-    g_k, g_v = synth.layer_global_scales(wl, fill_lens, layer_idx, device)
-    layer = KVCacheLayer.allocate(pool, wl.kv_heads, g_k, g_v, device)
+    if mx:
+        layer = MxKVCacheLayer.allocate(pool, wl.kv_heads, device)
+        append, per_head = mx_quantize_append, 2 * 68
+    else:
+        g_k, g_v = synth.layer_global_scales(wl, fill_lens, layer_idx, device)
+        layer = KVCacheLayer.allocate(pool, wl.kv_heads, g_k, g_v, device)
+        append, per_head = quantize_append, 2 * 72
     seq_all, pos_all = synth.token_positions(fill_lens)
     stream = torch.cuda.current_stream()
     ms, by = [], []
@@ -45,12 +51,12 @@ def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device
             torch.cuda._sleep(1 << 20)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        quantize_append(layer, k, v, sl)
+        append(layer, k, v, sl)
         if timed:
             e1.record(stream)
             torch.cuda.synchronize()
             ms.append(e0.elapsed_time(e1))
-            by.append(n * wl.kv_heads * (2 * 128 * k.element_size() + 144) + 4 * n)
+            by.append(n * wl.kv_heads * (2 * 128 * k.element_size() + per_head) + 4 * n)
         if on_chunk is not None:
             on_chunk(c0, n, k, v, seq, pos)
         del k, v

@@ -19,7 +19,7 @@ def _lib():
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]+?\b(nvfp4_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]+?\b((?:nvfp4|mxfp4)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_three_entry_points():
@@ -234,3 +234,56 @@ def test_decode_step_checks():
     assert call(T=3) == 2                          # 8 heads per kv head x 3 tokens > 16 rows
     assert call(ws=16) == 3
     assert call(batch=0, k=0, v=0) == 0
+
+
+# ---------------------------------------------------------------- MXFP4
+def _mx_layer(nk, **kw):
+    d = dict(k_codes=FAKE, k_scales=FAKE + 0x100000, v_codes=FAKE + 0x200000, v_scales=FAKE + 0x300000,
+             num_pages=10, num_kv_heads=8, head_dim=128, page_size=16)
+    d.update(kw)
+    return nk.CMxLayer(**d)
+
+
+def test_header_declares_the_mxfp4_entry_points():
+    fns = _declared_functions()
+    assert "mxfp4_kv_quantize_append" in fns and "mxfp4_paged_decode_attn" in fns
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 2), (dict(page_size=32), 2), (dict(k_codes=0), 1), (dict(v_scales=0), 1),
+    (dict(num_pages=0), 1), (dict(num_kv_heads=0), 1), (dict(k_codes=FAKE + 8), 2), (dict(k_scales=FAKE + 1), 2),
+    (dict(num_pages=1 << 28), 2),
+])
+def test_mx_layer_checks(kw, status):
+    nk = _lib()
+    L = _mx_layer(nk, **kw)
+    st = nk.lib.mxfp4_kv_quantize_append(ctypes.byref(L), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 1, 4, 1024,
+                                         ctypes.c_void_p(FAKE), None)
+    assert st == status
+
+
+def test_mx_append_and_decode_checks():
+    nk = _lib()
+    L = _mx_layer(nk)
+
+    def app(k=FAKE, dtype=1, T=4, stride=1024, slots=FAKE):
+        return nk.lib.mxfp4_kv_quantize_append(ctypes.byref(L), ctypes.c_void_p(k), ctypes.c_void_p(FAKE), dtype, T,
+                                               stride, ctypes.c_void_p(slots), None)
+
+    def dec(q=FAKE, B=2, Hq=64, bts=4, msl=64, sm=0.088, out=FAKE, ws=FAKE, wsb=1 << 30):
+        return nk.lib.mxfp4_paged_decode_attn(ctypes.byref(L), ctypes.c_void_p(q), 1, B, Hq, ctypes.c_void_p(FAKE),
+                                              bts, ctypes.c_void_p(FAKE), msl, sm, ctypes.c_void_p(out),
+                                              ctypes.c_void_p(ws), wsb, None)
+
+    assert nk.lib.mxfp4_kv_quantize_append(None, None, None, 1, 1, 1024, None, None) == 1
+    assert app(T=0, k=0, slots=0) == 0
+    assert app(T=-1) == 1 and app(dtype=7) == 1 and app(k=0) == 1 and app(slots=0) == 1
+    assert app(stride=1023) == 1 and app(k=FAKE + 4) == 2 and app(stride=1028) == 2
+    assert nk.lib.mxfp4_paged_decode_attn(None, None, 1, 1, 8, None, 1, None, 16, 0.1, None, None, 0, None) == 1
+    assert dec(Hq=60) == 1 and dec(Hq=8 * 17) == 2 and dec(B=-1) == 1
+    assert dec(B=0, q=0, out=0) == 0
+    assert dec(q=0) == 1 and dec(out=0) == 1 and dec(bts=3) == 1 and dec(sm=float("nan")) == 1
+    assert dec(q=FAKE + 2) == 2 and dec(B=4097) == 2 and dec(ws=FAKE + 16) == 1
+    need = nk.decode_workspace_bytes(1, 64, 8, 1 << 20)
+    assert dec(B=1, msl=1 << 20, bts=1 << 16, wsb=need - 1) == 3
+
