@@ -12,7 +12,8 @@ Printed: one JSON line.  `value` is decode-step effective HBM bandwidth
 (algorithmic bytes of append + decode per step / step wall time); the same line
 carries the bulk quantize-append GB/s, the FP8 workspace dequant GB/s, the
 roofline of the dominant kernel (decode attention, timed with HIP events on the
-launch stream) and the CPU oracle timed on a bounded sample.
+launch stream), the MXFP4 comparison format's append and decode on the same
+tokens, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -197,6 +198,9 @@ def warm_kernels(wl, dev):
     zero = torch.zeros(1, dtype=torch.int32, device=dev)
     nk.fp8_extend_attn(qx, torch.tensor([0, 4], dtype=torch.int32, device=dev), zero, zero, 4, ws, ws.clone(), 1.0,
                        1.0, 0.088)
+    mx = nk.MxKVCacheLayer.allocate(2, H, dev)
+    nk.mx_quantize_append(mx, x, x, torch.arange(4, dtype=torch.int32, device=dev))
+    nk.mx_paged_decode_attn(mx, q, bt, sl, 4, 0.088)
     torch.cuda.synchronize()
 
 
@@ -541,6 +545,31 @@ def main():
     app_total_s = float(sum(append_ms)) / 1e3
     traffic = read_traffic(DECODE_SOURCES, wl.name)
 
+    # ---- MXFP4, the format the pages compare NVFP4 against (E8M0 scale per 32
+    # values, 17/32 byte per value): the same tokens, slots and queries in
+    # MXFP4 layers; bulk append and decode timed as above
+    mx_layers, mx_app_ms, mx_app_b = [], [], []
+    for l in range(L):
+        fl = build_layer(wl, [ctx] * B, [ctx] * B, l, dev, timed=True, mx=True)
+        mx_layers.append(fl.layer)
+        mx_app_ms += fl.append_ms
+        mx_app_b += fl.append_bytes
+    print("[bench] MXFP4 layers filled", file=sys.stderr, flush=True)
+
+    def mx_call(i):
+        l = i % L
+        nk.mx_paged_decode_attn(mx_layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
+    for i in range(args.warmup):
+        mx_call(i)
+    mx_s = back_to_back(stream, args.steps, mx_call)
+    bytes_mx = B * ctx * H * 136 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
+    mxfp4 = {"decode_us": round(mx_s * 1e6, 3), "decode_gbs": round(bytes_mx / mx_s / 1e9, 2),
+             "decode_frac": round(bytes_mx / mx_s / 1e9 / PEAK_HBM_GBS, 4),
+             "algorithmic_bytes_per_call": int(bytes_mx),
+             "decode_time_vs_nvfp4": round(mx_s / dec_avg_s, 4),
+             "quantize_append_bulk_gbs": round(float(sum(mx_app_b)) / (float(sum(mx_app_ms)) / 1e3) / 1e9, 2)}
+    del mx_layers
+
     result = {
         "metric": METRIC,
         "value": round(bytes_step / (wall / args.steps) / 1e9, 2),
@@ -571,6 +600,7 @@ def main():
         "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),
         "fp8_workspace_gbs": round(ws_gbs, 2),
         "fp8_workspace_tokens": int(n_ext * ctx),
+        "mxfp4": mxfp4,
         "bytes_per_step": int(bytes_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
