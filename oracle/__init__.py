@@ -87,6 +87,8 @@ def lib():
     L.nvfp4o_mx_decode_attention.argtypes = [_u8p, _u8p, _u8p, _u8p, _int, _f32p, _int, _i32p, _int, _i32p, _flt,
                                              _i64p, _i64, _f64p]
     L.nvfp4o_mx_decode_attention.restype = None
+    L.nvfp4o_hadamard_rows.argtypes = [_f64p, _i64, _dbl, _f64p]
+    L.nvfp4o_hadamard_rows.restype = None
     L.nvfp4o_page_mode_dequant.argtypes = [_f64p, _i64, _i64, _f64p]
     L.nvfp4o_page_mode_dequant.restype = None
     L.nvfp4o_bytes_per_token_head.argtypes = []
@@ -316,6 +318,32 @@ def mx_decode_attention(planes: MxPlanes, q: np.ndarray, block_table: np.ndarray
     lib().nvfp4o_mx_decode_attention(planes.k_codes, planes.k_scales, planes.v_codes, planes.v_scales, planes.H, q, Hq,
                                      bt, bt.shape[1], sl, float(np.float32(sm_scale)), rows, rows.size, out)
     return out
+
+
+# ------------------------------------------------------- Hadamard rotation
+K_ROT_SCALE = 2.0 ** -4   # K' = H k / 16
+Q_ROT_SCALE = 2.0 ** -3   # q' = H q / 8, so q'.k' = q.k
+
+
+def hadamard_rows(x, scale: float) -> np.ndarray:
+    """scale * H x for each 128-value row of x (float64 result, same leading shape)."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    shape = a.shape
+    assert shape[-1] == 128
+    a = a.reshape(-1, 128)
+    out = np.zeros_like(a)
+    lib().nvfp4o_hadamard_rows(a, a.shape[0], float(scale), out)
+    return out.reshape(shape)
+
+
+def rotate_k(k) -> np.ndarray:
+    """K rows as stored by the rotated append: float32 nearest to H k / 16."""
+    return hadamard_rows(k, K_ROT_SCALE).astype(np.float32)
+
+
+def rotate_q(q) -> np.ndarray:
+    """Queries as the rotated decode uses them: H q / 8 (float64)."""
+    return hadamard_rows(q, Q_ROT_SCALE)
 
 
 # ------------------------------------------------------ the page experiment

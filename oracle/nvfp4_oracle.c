@@ -33,6 +33,8 @@
  *      and magnitude code 0 for every element.
  *   R9 MXFP4 (the comparison format) follows the OCP MX v1.0 definition; see
  *      the MXFP4 section below.
+ *   R10 the Hadamard rotation of K (and Q) is the 128-point Sylvester matrix
+ *      with power-of-two scales; see the Hadamard section below.
  *
  * Exactness of the float64 quotients used below.  Inputs are float32 (24-bit
  * significands), g is float32, block scales are E4M3 (4-bit significands) and
@@ -524,6 +526,28 @@ void nvfp4o_mx_decode_attention(const uint8_t* kc, const uint8_t* ks, const uint
                                 double* out) {
   decode_attention_with(mx_plane_value, kc, ks, vc, vs, Hkv, 1.0f, 1.0f, q, Hq, block_table, bt_stride, seq_lens,
                         sm_scale, rows, n_rows, out);
+}
+
+/* ------------------------------------------------------- Hadamard rotation
+ * [TC] "E2M1 encoding and two-level scaling" section, quantization tricks: an
+ * orthogonal Hadamard transform applied before quantization spreads a local
+ * outlier over the whole vector.  Reading R10: K rows (128 values along
+ * head_dim) are multiplied by the 128-point Sylvester Walsh-Hadamard matrix
+ * H[i][j] = (-1)^popcount(i & j) times 2^-4 before NVFP4 quantization, and
+ * queries by H times 2^-3 before attention: H H^T = 128 I, so the scores are
+ * unchanged, q'.k' = 2^-7 q^T H^T H k = q.k, and both scales are powers of two.
+ * out[r][i] = scale * sum_j H[i][j] x[r][j], summed in float64 in j order (the
+ * matrix definition; exact whenever the sum fits 53 bits). */
+void nvfp4o_hadamard_rows(const double* x, int64_t n_rows, double scale, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const double* xr = x + r * 128;
+    for (int i = 0; i < 128; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < 128; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -xr[j] : xr[j];
+      out[r * 128 + i] = scale * acc;
+    }
+  }
 }
 
 /* --------------------------------------------------- the page's experiment
