@@ -13,7 +13,8 @@ Printed: one JSON line.  `value` is decode-step effective HBM bandwidth
 carries the bulk quantize-append GB/s, the FP8 workspace dequant GB/s, the
 roofline of the dominant kernel (decode attention, timed with HIP events on the
 launch stream), the MXFP4 comparison format's append and decode on the same
-tokens, and the CPU oracle timed on a bounded sample.
+tokens, both formats with Hadamard-rotated K, and the CPU oracle timed on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -199,8 +200,11 @@ def warm_kernels(wl, dev):
     nk.fp8_extend_attn(qx, torch.tensor([0, 4], dtype=torch.int32, device=dev), zero, zero, 4, ws, ws.clone(), 1.0,
                        1.0, 0.088)
     mx = nk.MxKVCacheLayer.allocate(2, H, dev)
-    nk.mx_quantize_append(mx, x, x, torch.arange(4, dtype=torch.int32, device=dev))
-    nk.mx_paged_decode_attn(mx, q, bt, sl, 4, 0.088)
+    for rot in (False, True):
+        nk.quantize_append(layer, x, x, torch.arange(4, dtype=torch.int32, device=dev), hadamard=rot)
+        nk.paged_decode_attn(layer, q, bt, sl, 4, 0.088, hadamard=rot)
+        nk.mx_quantize_append(mx, x, x, torch.arange(4, dtype=torch.int32, device=dev), hadamard=rot)
+        nk.mx_paged_decode_attn(mx, q, bt, sl, 4, 0.088, hadamard=rot)
     torch.cuda.synchronize()
 
 
@@ -568,6 +572,32 @@ def main():
              "algorithmic_bytes_per_call": int(bytes_mx),
              "decode_time_vs_nvfp4": round(mx_s / dec_avg_s, 4),
              "quantize_append_bulk_gbs": round(float(sum(mx_app_b)) / (float(sum(mx_app_ms)) / 1e3) / 1e9, 2)}
+    # ---- Hadamard-rotated K (both formats): the same tokens stored with K
+    # rotated by the append kernel; the decode rotates Q in its prologue and
+    # takes Q as a hi + lo pair (twice the QK^T MFMAs)
+    hadamard = {}
+    for fmt, mx in (("nvfp4", False), ("mxfp4", True)):
+        rot_layers, rot_ms, rot_b = [], [], []
+        for l in range(L):
+            fl = build_layer(wl, [ctx] * B, [ctx] * B, l, dev, timed=True, mx=mx, hadamard=True)
+            rot_layers.append(fl.layer)
+            rot_ms += fl.append_ms
+            rot_b += fl.append_bytes
+        dec = nk.mx_paged_decode_attn if mx else nk.paged_decode_attn
+
+        def rot_call(i):
+            l = i % L
+            dec(rot_layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace, hadamard=True)
+        for i in range(args.warmup):
+            rot_call(i)
+        rot_s = back_to_back(stream, args.steps, rot_call)
+        b_rot = bytes_mx if mx else bytes_decode
+        plain_s = mx_s if mx else dec_avg_s
+        hadamard[fmt] = {"decode_us": round(rot_s * 1e6, 3), "decode_gbs": round(b_rot / rot_s / 1e9, 2),
+                         "decode_time_vs_unrotated": round(rot_s / plain_s, 4),
+                         "quantize_append_bulk_gbs": round(float(sum(rot_b)) / (float(sum(rot_ms)) / 1e3) / 1e9, 2)}
+        del rot_layers
+    print("[bench] Hadamard-rotated layers timed", file=sys.stderr, flush=True)
     del mx_layers
 
     result = {
@@ -601,6 +631,7 @@ def main():
         "fp8_workspace_gbs": round(ws_gbs, 2),
         "fp8_workspace_tokens": int(n_ext * ctx),
         "mxfp4": mxfp4,
+        "hadamard_k": hadamard,
         "bytes_per_step": int(bytes_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),

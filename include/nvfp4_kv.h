@@ -312,6 +312,54 @@ NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn(const mxfp4_kv_layer_t* layer, 
                                                  int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                                                  size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------ Hadamard-rotated K
+ * cloud.tencent.com.cn "NVFP4: breaking the memory wall of GPU inference",
+ * E2M1 encoding and two-level scaling section, quantization tricks: an
+ * orthogonal Hadamard transform applied before quantization spreads a local
+ * outlier over the whole vector.  Here K rows are rotated before they are
+ * quantized and the query is rotated the same way at decode time, so the
+ * scores are unchanged:
+ *   k' = H k / 16,  q' = H q / 8,  q'.k' = q.k,
+ * H the 128-point Sylvester Walsh-Hadamard matrix, H[i][j] = (-1)^popcount(i & j)
+ * (H H^T = 128 I; both scales are powers of two).  V is stored as usual.
+ * k' is the float32 nearest to the exact H k / 16 whenever that sum is exact
+ * in float64 (every 128-value row of bf16 values spanning at most 38
+ * binades, of float32 values spanning at most 22); it is then quantized like
+ * any K row, so the cache bytes equal those of the unrotated call on k'.
+ * A cache written with a _hadamard append must be read with the _hadamard
+ * decode of the same format; the global scale k_global is calibrated on k'.
+ * The FP8 workspace, multi-token decode and the one-launch step read
+ * unrotated caches only. */
+
+/* nvfp4_kv_quantize_append with K rows rotated (k' above) before quantization. */
+NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append_hadamard(const nvfp4_kv_layer_t* layer, const void* k_new,
+                                                           const void* v_new, nvfp4_dtype_t dtype, int32_t num_tokens,
+                                                           int64_t token_stride_elems, const int32_t* slot_mapping,
+                                                           void* stream);
+
+/* nvfp4_paged_decode_attn over a cache of rotated K: each query row is
+ * rotated (q' above, in fp32) and, no longer exact in 16 bits, enters the
+ * MFMA as an f16 hi + lo pair.  Arguments, workspace, limits and errors as
+ * nvfp4_paged_decode_attn. */
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_hadamard(const nvfp4_kv_layer_t* layer, const void* q,
+                                                          nvfp4_dtype_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                                          const int32_t* block_table, int32_t block_table_stride,
+                                                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                                          float* out, void* workspace, size_t workspace_bytes,
+                                                          void* stream);
+
+/* The same pair for MXFP4 caches. */
+NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append_hadamard(const mxfp4_kv_layer_t* layer, const void* k_new,
+                                                           const void* v_new, nvfp4_dtype_t dtype, int32_t num_tokens,
+                                                           int64_t token_stride_elems, const int32_t* slot_mapping,
+                                                           void* stream);
+NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn_hadamard(const mxfp4_kv_layer_t* layer, const void* q,
+                                                          nvfp4_dtype_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                                          const int32_t* block_table, int32_t block_table_stride,
+                                                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                                          float* out, void* workspace, size_t workspace_bytes,
+                                                          void* stream);
+
 /* Static string for a status code. */
 NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 

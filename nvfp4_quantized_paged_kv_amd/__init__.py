@@ -47,6 +47,10 @@ EXPORTED_SYMBOLS = (
     "nvfp4_fp8_extend_attn",
     "mxfp4_kv_quantize_append",
     "mxfp4_paged_decode_attn",
+    "nvfp4_kv_quantize_append_hadamard",
+    "nvfp4_paged_decode_attn_hadamard",
+    "mxfp4_kv_quantize_append_hadamard",
+    "mxfp4_paged_decode_attn_hadamard",
     "nvfp4_status_string",
 )
 
@@ -122,6 +126,15 @@ def _load():
     L.mxfp4_kv_quantize_append.restype = ctypes.c_int
     L.mxfp4_paged_decode_attn.argtypes = [mp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
     L.mxfp4_paged_decode_attn.restype = ctypes.c_int
+    for f in ("nvfp4_kv_quantize_append_hadamard",):
+        getattr(L, f).argtypes = L.nvfp4_kv_quantize_append.argtypes
+    for f in ("nvfp4_paged_decode_attn_hadamard",):
+        getattr(L, f).argtypes = L.nvfp4_paged_decode_attn.argtypes
+    L.mxfp4_kv_quantize_append_hadamard.argtypes = L.mxfp4_kv_quantize_append.argtypes
+    L.mxfp4_paged_decode_attn_hadamard.argtypes = L.mxfp4_paged_decode_attn.argtypes
+    for f in ("nvfp4_kv_quantize_append_hadamard", "nvfp4_paged_decode_attn_hadamard",
+              "mxfp4_kv_quantize_append_hadamard", "mxfp4_paged_decode_attn_hadamard"):
+        getattr(L, f).restype = ctypes.c_int
     L.nvfp4_status_string.argtypes = [ctypes.c_int]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     return L
@@ -213,13 +226,16 @@ def _check_new_kv(layer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.T
 
 
 def quantize_append(layer: KVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-                    stream=None) -> None:
-    """Quantize k, v ([T, H, 128] or [T, H*128], bf16/f32, token-strided) into their slots."""
+                    stream=None, hadamard: bool = False) -> None:
+    """Quantize k, v ([T, H, 128] or [T, H*128], bf16/f32, token-strided) into their slots.
+
+    hadamard: rotate the K rows (H k / 16) before quantization; read such a cache with hadamard=True."""
     stride = _check_new_kv(layer, k, v, slot_mapping)
     c = layer.c_struct()
-    st = lib.nvfp4_kv_quantize_append(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), k.shape[0], stride,
-                                      _ptr(slot_mapping), _stream(stream))
-    _check(st, "nvfp4_kv_quantize_append")
+    name = "nvfp4_kv_quantize_append_hadamard" if hadamard else "nvfp4_kv_quantize_append"
+    st = getattr(lib, name)(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), k.shape[0], stride,
+                            _ptr(slot_mapping), _stream(stream))
+    _check(st, name)
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int) -> int:
@@ -234,14 +250,17 @@ def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_le
 
 def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                       max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode attention of q [B, Hq, 128] (bf16/f32) over the cache; returns f32 [B, Hq, 128]."""
+                      workspace: torch.Tensor | None = None, stream=None, hadamard: bool = False) -> torch.Tensor:
+    """Decode attention of q [B, Hq, 128] (bf16/f32) over the cache; returns f32 [B, Hq, 128].
+
+    hadamard: the cache holds rotated K (quantize_append(..., hadamard=True)); q is rotated alike."""
     out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace)
     c = layer.c_struct()
-    st = lib.nvfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
-                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
-                                     float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "nvfp4_paged_decode_attn")
+    name = "nvfp4_paged_decode_attn_hadamard" if hadamard else "nvfp4_paged_decode_attn"
+    st = getattr(lib, name)(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
+                            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                            float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, name)
     return out
 
 
@@ -438,23 +457,25 @@ class MxKVCacheLayer:
 
 
 def mx_quantize_append(layer: MxKVCacheLayer, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-                       stream=None) -> None:
+                       stream=None, hadamard: bool = False) -> None:
     """MXFP4 quantize-append of k, v (shapes as quantize_append) into their slots."""
     stride = _check_new_kv(layer, k, v, slot_mapping)
     c = layer.c_struct()
-    st = lib.mxfp4_kv_quantize_append(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), k.shape[0], stride,
-                                      _ptr(slot_mapping), _stream(stream))
-    _check(st, "mxfp4_kv_quantize_append")
+    name = "mxfp4_kv_quantize_append_hadamard" if hadamard else "mxfp4_kv_quantize_append"
+    st = getattr(lib, name)(ctypes.byref(c), _ptr(k), _ptr(v), _dtype_code(k), k.shape[0], stride,
+                            _ptr(slot_mapping), _stream(stream))
+    _check(st, name)
 
 
 def mx_paged_decode_attn(layer: MxKVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                          max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
-                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                         workspace: torch.Tensor | None = None, stream=None, hadamard: bool = False) -> torch.Tensor:
     """Decode attention of q [B, Hq, 128] over MXFP4 pages; returns f32 [B, Hq, 128]."""
     out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace)
     c = layer.c_struct()
-    st = lib.mxfp4_paged_decode_attn(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
-                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
-                                     float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "mxfp4_paged_decode_attn")
+    name = "mxfp4_paged_decode_attn_hadamard" if hadamard else "mxfp4_paged_decode_attn"
+    st = getattr(lib, name)(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
+                            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                            float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, name)
     return out

@@ -58,9 +58,13 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status) {
   return "unknown status";
 }
 
-NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
-                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
-                                                  const int32_t* slot_mapping, void* stream) {
+}  // extern "C"
+
+namespace {
+
+nvfp4_status_t append_impl(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new, nvfp4_dtype_t dtype,
+                           int32_t num_tokens, int64_t token_stride_elems, const int32_t* slot_mapping, void* stream,
+                           bool rot_k) {
   const nvfp4_status_t st = check_layer(layer);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(dtype) || num_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
@@ -79,7 +83,25 @@ NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer,
   p.num_tokens = num_tokens;
   p.H = layer->num_kv_heads;
   p.num_pages = layer->num_pages;
+  p.rot_k = rot_k ? 1 : 0;
   return from_hip(launch_quantize_append(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                  const int32_t* slot_mapping, void* stream) {
+  return append_impl(layer, k_new, v_new, dtype, num_tokens, token_stride_elems, slot_mapping, stream, false);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append_hadamard(const nvfp4_kv_layer_t* layer, const void* k_new,
+                                                           const void* v_new, nvfp4_dtype_t dtype, int32_t num_tokens,
+                                                           int64_t token_stride_elems, const int32_t* slot_mapping,
+                                                           void* stream) {
+  return append_impl(layer, k_new, v_new, dtype, num_tokens, token_stride_elems, slot_mapping, stream, true);
 }
 
 // The decode kernel indexes the (sequence, kv head, page) work of a call, plus
@@ -113,7 +135,7 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
                            nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
                            const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                            int32_t max_seq_len, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                           void* stream, bool mx = false) {
+                           void* stream, bool mx = false, bool rot_q = false) {
   const nvfp4_status_t st = check_layer(layer);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(q_dtype) || batch < 0 || q_per_seq < 1 || num_q_heads <= 0 || max_seq_len < 0)
@@ -164,6 +186,7 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
   p.k_new = k_new;
   p.v_new = v_new;
   p.mx = mx ? 1 : 0;
+  p.rot_q = rot_q ? 1 : 0;
   return from_hip(launch_decode(p, q_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -178,6 +201,16 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
                                                  size_t workspace_bytes, void* stream) {
   return decode_impl(layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
                      seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_hadamard(const nvfp4_kv_layer_t* layer, const void* q,
+                                                          nvfp4_dtype_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                                          const int32_t* block_table, int32_t block_table_stride,
+                                                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                                          float* out, void* workspace, size_t workspace_bytes,
+                                                          void* stream) {
+  return decode_impl(layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream, false, true);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* layer, const void* q,
@@ -309,9 +342,13 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn(const void* q, nvfp4_dtype_t q_dt
 
 // ---------------------------------------------------------------- MXFP4
 
-NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append(const mxfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
-                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
-                                                  const int32_t* slot_mapping, void* stream) {
+}  // extern "C"
+
+namespace {
+
+nvfp4_status_t mx_append_impl(const mxfp4_kv_layer_t* layer, const void* k_new, const void* v_new, nvfp4_dtype_t dtype,
+                              int32_t num_tokens, int64_t token_stride_elems, const int32_t* slot_mapping, void* stream,
+                              bool rot_k) {
   const nvfp4_status_t st = check_mx_layer(layer);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(dtype) || num_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
@@ -333,14 +370,14 @@ NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append(const mxfp4_kv_layer_t* layer,
   p.num_tokens = num_tokens;
   p.H = layer->num_kv_heads;
   p.num_pages = layer->num_pages;
+  p.rot_k = rot_k ? 1 : 0;
   return from_hip(launch_mx_append(p, dtype, static_cast<hipStream_t>(stream)));
 }
 
-NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn(const mxfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
-                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
-                                                 int32_t block_table_stride, const int32_t* seq_lens,
-                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
-                                                 size_t workspace_bytes, void* stream) {
+nvfp4_status_t mx_decode_impl(const mxfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype, int32_t batch,
+                              int32_t num_q_heads, const int32_t* block_table, int32_t block_table_stride,
+                              const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream, bool rot_q) {
   const nvfp4_status_t st = check_mx_layer(layer);
   if (st != NVFP4_OK) return st;
   // the decode path reads the same fields; MXFP4 has no tensor-wide scale
@@ -348,7 +385,43 @@ NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn(const mxfp4_kv_layer_t* layer, 
                                   layer->num_pages,  layer->num_kv_heads, layer->head_dim, layer->page_size,
                                   1.0f,              1.0f};
   return decode_impl(&as_layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
-                     seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream, true);
+                     seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream, true, rot_q);
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append(const mxfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
+                                                  nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                  const int32_t* slot_mapping, void* stream) {
+  return mx_append_impl(layer, k_new, v_new, dtype, num_tokens, token_stride_elems, slot_mapping, stream, false);
+}
+
+NVFP4_API nvfp4_status_t mxfp4_kv_quantize_append_hadamard(const mxfp4_kv_layer_t* layer, const void* k_new,
+                                                           const void* v_new, nvfp4_dtype_t dtype, int32_t num_tokens,
+                                                           int64_t token_stride_elems, const int32_t* slot_mapping,
+                                                           void* stream) {
+  return mx_append_impl(layer, k_new, v_new, dtype, num_tokens, token_stride_elems, slot_mapping, stream, true);
+}
+
+NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn(const mxfp4_kv_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                                 int32_t block_table_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  return mx_decode_impl(layer, q, q_dtype, batch, num_q_heads, block_table, block_table_stride, seq_lens, max_seq_len,
+                        sm_scale, out, workspace, workspace_bytes, stream, false);
+}
+
+NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn_hadamard(const mxfp4_kv_layer_t* layer, const void* q,
+                                                          nvfp4_dtype_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                                          const int32_t* block_table, int32_t block_table_stride,
+                                                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                                          float* out, void* workspace, size_t workspace_bytes,
+                                                          void* stream) {
+  return mx_decode_impl(layer, q, q_dtype, batch, num_q_heads, block_table, block_table_stride, seq_lens, max_seq_len,
+                        sm_scale, out, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -158,6 +158,32 @@ __device__ __forceinline__ void widen_q(const QRaw<QF32>& r, float (&v)[32]) {
   }
 }
 
+// Q for a cache of Hadamard-rotated K: q' = H q / 8 (H the 128-point Sylvester
+// matrix, so q'.k' = q.k for k' = H k / 16).  The lane holds dims 32*q4 + j:
+// fast Walsh-Hadamard stages over j in registers, then over q4 with the lanes
+// l ^ 16 and l ^ 32 (fp32: Q feeds only the scores, not a rounding decision).
+__device__ __forceinline__ void hadamard_rotate_q(float (&v)[32], int q4) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], c = v[i + h];
+        v[i] = a + c;
+        v[i + h] = a - c;
+      }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float o = __shfl_xor(v[i], 16);
+    v[i] = (q4 & 1) ? o - v[i] : v[i] + o;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float o = __shfl_xor(v[i], 32);
+    v[i] = ((q4 & 2) ? o - v[i] : v[i] + o) * 0.125f;
+  }
+}
+
 // The bytes one lane needs from one (page, kv head) tile, and the number of
 // valid tokens in that page (0 for an out-of-range page index).
 struct PageRegs {
@@ -274,9 +300,12 @@ __device__ __forceinline__ void append_own_tokens(const DecodeParams& p, int b, 
 // kMulti: several query tokens per sequence (per-row causal limits); the
 // one-token instance keeps the plain decode's code.  kAppend: the step's new
 // tokens are appended by the kernel itself (append_own_tokens).  kMX: MXFP4
-// planes (one-token decode only).
-template <bool QF32, bool kPlane, bool kMulti, bool kAppend, bool kMX>
+// planes (one-token decode only).  kRot: the cache holds Hadamard-rotated K,
+// so Q is rotated the same way (one-token decode only); rotated Q is not exact
+// in 16 bits, so it always takes the hi + lo split of float32 Q.
+template <bool QF32, bool kPlane, bool kMulti, bool kAppend, bool kMX, bool kRot>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  constexpr bool kSplitQ = QF32 || kRot;
   __shared__ int s_pref[kMaxDecodeBatch + 1];  // exclusive prefix of pages per sequence
   __shared__ int s_wsum[kWaves];
   __shared__ int s_flag;
@@ -448,6 +477,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
     float qv[32];
     widen_q<QF32>(q_raw, qv);
+    if constexpr (kRot) hadamard_rotate_q(qv, eq);
     float qmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qv[i]));
@@ -471,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const float xq = qv[8 * c + j] * qscale;
         const QElem hq = (QElem)xq;
         qa[c][j] = hq;
-        if (QF32) ql[c][j] = (QElem)(xq - (float)hq);
+        if (kSplitQ) ql[c][j] = (QElem)(xq - (float)hq);
       }
     // > 0: a zero logit scale becomes FLT_MIN (uniform weights to fp32
     // precision), so masked scores (-inf) always give weight exactly 0
@@ -501,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
               bf16x8_t, make_uint4(fp4x2_to_bf16<0>(kwa[c], ksc), fp4x2_to_bf16<1>(kwa[c], ksc),
                                    fp4x2_to_bf16<2>(kwa[c], ksc), fp4x2_to_bf16<3>(kwa[c], ksc)));
           S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qa[c], S, 0, 0, 0);
-          if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[c], S, 0, 0, 0);
+          if (kSplitQ) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[c], S, 0, 0, 0);
         }
       } else {
         const half2_t ks0 = e4m3_pair_to_f16_scaled(cur.ksw & 0xFFu, cur.ksw & 0xFFu);
@@ -515,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           const half2_t e3 = fp4x2_to_f16_x256<3>(kwa[c]) * sc;
           const half8_t a = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
           S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qa[c], S, 0, 0, 0);
-          if (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[c], S, 0, 0, 0);
+          if (kSplitQ) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[c], S, 0, 0, 0);
         }
       }
       // The MFMA result is read next, possibly across the partial-page branch;
@@ -758,23 +788,26 @@ hipError_t launch_decode(const DecodeParams& p, nvfp4_dtype_t q_dtype, hipStream
   const bool plane = (int64_t)p.num_pages * p.H * kTileCodeBytes <= (int64_t)UINT32_MAX;
   const bool f32 = q_dtype == NVFP4_DTYPE_F32;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p); };
-  auto pick = [&](auto multi, auto append, auto mx) {
-    constexpr bool M = decltype(multi)::value, A = decltype(append)::value, X = decltype(mx)::value;
-    if (f32 && plane) go(decode_kernel<true, true, M, A, X>);
-    else if (f32) go(decode_kernel<true, false, M, A, X>);
-    else if (plane) go(decode_kernel<false, true, M, A, X>);
-    else go(decode_kernel<false, false, M, A, X>);
+  auto pick = [&](auto multi, auto append, auto mx, auto rot) {
+    constexpr bool M = decltype(multi)::value, A = decltype(append)::value, X = decltype(mx)::value,
+                   Q = decltype(rot)::value;
+    if (f32 && plane) go(decode_kernel<true, true, M, A, X, Q>);
+    else if (f32) go(decode_kernel<true, false, M, A, X, Q>);
+    else if (plane) go(decode_kernel<false, true, M, A, X, Q>);
+    else go(decode_kernel<false, false, M, A, X, Q>);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   const bool append = p.k_new != nullptr;
-  if (p.mx) {  // MXFP4 planes: one query token, no append (checked by the host)
-    if (p.T != 1 || append) return hipErrorInvalidValue;
-    pick(F_{}, F_{}, T_{});
+  if ((p.mx || p.rot_q) && (p.T != 1 || append)) return hipErrorInvalidValue;  // one-token decode only (host-checked)
+  if (p.mx) {
+    if (p.rot_q) pick(F_{}, F_{}, T_{}, T_{}); else pick(F_{}, F_{}, T_{}, F_{});
+  } else if (p.rot_q) {
+    pick(F_{}, F_{}, F_{}, T_{});
   } else if (p.T > 1) {
-    if (append) pick(T_{}, T_{}, F_{}); else pick(T_{}, F_{}, F_{});
+    if (append) pick(T_{}, T_{}, F_{}, F_{}); else pick(T_{}, F_{}, F_{}, F_{});
   } else {
-    if (append) pick(F_{}, T_{}, F_{}); else pick(F_{}, F_{}, F_{});
+    if (append) pick(F_{}, T_{}, F_{}, F_{}); else pick(F_{}, F_{}, F_{}, F_{});
   }
   return hipGetLastError();
 }

@@ -15,7 +15,9 @@
 // is E - 127 (E >= 1), so the scale byte is max(E - 2, 0).  |x| * 2^(127 -
 // byte) is then exact (a power of two, result below 8), and the E2M1 code is
 // found by comparisons against the exact midpoints, ties to the even code.
-#include "nvfp4_kv_internal.h"
+#include <type_traits>
+
+#include "nvfp4_quant_device.h"
 
 namespace nvfp4kv {
 namespace {
@@ -67,23 +69,28 @@ struct MxTensor {
   uint8_t* scales;
 };
 
-template <typename InT>
+// kRotK: K rows are Hadamard-rotated before quantization (the 4 blocks of a
+// row sit in lanes l, l^4, l^8, l^12; lanes without a token hold token 0 and
+// take part in the exchanges, then skip the store).
+template <typename InT, bool kRotK>
 __global__ __launch_bounds__(256) void mx_append_kernel(MxTensor k, MxTensor v, const int32_t* slots,
                                                         int64_t token_stride, int32_t num_tokens, int32_t H,
                                                         int32_t num_pages, int64_t n_threads) {
   const MxTensor& T = blockIdx.y ? v : k;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_threads) return;
+  if (i >= n_threads) return;  // n_threads is a multiple of 64: whole waves leave together
   const int tq = (int)(i & 3), b = (int)((i >> 2) & 3), tg = (int)((i >> 4) & 3);
   const uint32_t gh = (uint32_t)(i >> 6);  // group of 16 tokens * H + kv head (< 2^31, checked by the host)
   const int h = (int)(gh % (uint32_t)H);
   const int64_t t = 16 * (int64_t)(gh / (uint32_t)H) + 4 * tg + tq;
-  if (t >= num_tokens) return;
-  const int32_t slot = slots[t];
-  if (slot < 0 || (int64_t)slot >= (int64_t)num_pages * kPageSize) return;
+  const int32_t slot = t < num_tokens ? slots[t] : -1;
+  const bool store = slot >= 0 && (int64_t)slot < (int64_t)num_pages * kPageSize;
 
   float x[32];
-  load_block32<InT>(reinterpret_cast<const InT*>(T.x) + t * token_stride + (int64_t)h * kHeadDim + 32 * b, x);
+  load_block32<InT>(reinterpret_cast<const InT*>(T.x) + (store ? t : 0) * token_stride + (int64_t)h * kHeadDim + 32 * b,
+                    x);
+  if (kRotK && blockIdx.y == 0) hadamard_rotate_k<32, 4>(x, b);
+  if (!store) return;
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
@@ -119,12 +126,16 @@ hipError_t launch_mx_append(const MxAppendParams& p, nvfp4_dtype_t dtype, hipStr
   if (n_threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_threads + 255) / 256), 2, 1);
   const MxTensor k{p.x[0], p.codes[0], p.scales[0]}, v{p.x[1], p.codes[1], p.scales[1]};
-  if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(mx_append_kernel<uint16_t>, grid, dim3(256), 0, stream, k, v, p.slots, p.token_stride,
-                       p.num_tokens, p.H, p.num_pages, n_threads);
-  else
-    hipLaunchKernelGGL(mx_append_kernel<float>, grid, dim3(256), 0, stream, k, v, p.slots, p.token_stride,
-                       p.num_tokens, p.H, p.num_pages, n_threads);
+  auto go = [&](auto rot) {
+    constexpr bool R = decltype(rot)::value;
+    if (dtype == NVFP4_DTYPE_BF16)
+      hipLaunchKernelGGL((mx_append_kernel<uint16_t, R>), grid, dim3(256), 0, stream, k, v, p.slots, p.token_stride,
+                         p.num_tokens, p.H, p.num_pages, n_threads);
+    else
+      hipLaunchKernelGGL((mx_append_kernel<float, R>), grid, dim3(256), 0, stream, k, v, p.slots, p.token_stride,
+                         p.num_tokens, p.H, p.num_pages, n_threads);
+  };
+  if (p.rot_k) go(std::true_type{}); else go(std::false_type{});
   return hipGetLastError();
 }
 

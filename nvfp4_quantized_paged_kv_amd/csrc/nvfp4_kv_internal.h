@@ -32,6 +32,7 @@ struct AppendParams {
   int32_t num_tokens;
   int32_t H;
   int32_t num_pages;
+  int32_t rot_k;         // 1: Hadamard-rotate K rows before quantization
 };
 
 hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream);
@@ -46,6 +47,7 @@ struct MxAppendParams {
   int32_t num_tokens;
   int32_t H;
   int32_t num_pages;
+  int32_t rot_k;         // 1: Hadamard-rotate K rows before quantization
 };
 
 hipError_t launch_mx_append(const MxAppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream);
@@ -77,6 +79,7 @@ struct DecodeParams {
   const void* k_new;       // decode step with its own append: [B][T][H][128] new K (q dtype), else null
   const void* v_new;
   int32_t mx;              // 1: the planes hold MXFP4 (E8M0 per 32 values, 64-byte scale tiles)
+  int32_t rot_q;           // 1: the cache holds Hadamard-rotated K; rotate Q the same way
 };
 
 constexpr int kMaxDecodeBatch = 4096;  // sequences per decode call (prefix sums kept in LDS)

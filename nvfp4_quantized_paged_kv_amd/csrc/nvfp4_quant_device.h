@@ -66,6 +66,60 @@ __device__ __forceinline__ void load_block<float>(const float* src, float (&x)[1
   }
 }
 
+// Lane exchange within 32 lanes: the value of lane l ^ X (ds_swizzle, bitmask mode).
+template <int X>
+__device__ __forceinline__ double swz_xor(double v) {
+  const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(v), (X << 10) | 0x1F);
+  const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(v), (X << 10) | 0x1F);
+  return __hiloint2double(hi, lo);
+}
+
+// One fast Walsh-Hadamard stage across lanes: this lane holds the elements
+// whose index has bit `mine` (0 or 1) set at this stage, its partner lane l ^ X
+// the others: (a, c) -> (a + c, a - c).
+template <int X>
+__device__ __forceinline__ void wht_cross(double* d, int n, bool mine) {
+  for (int i = 0; i < n; ++i) {
+    const double o = swz_xor<X>(d[i]);
+    d[i] = mine ? o - d[i] : d[i] + o;
+  }
+}
+
+// Fast Walsh-Hadamard stages over the N values one lane holds (index bits below log2 N).
+template <int N>
+__device__ __forceinline__ void wht_local(double (&d)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & h) == 0) {
+        const double a = d[i], c = d[i + h];
+        d[i] = a + c;
+        d[i + h] = a - c;
+      }
+}
+
+// Hadamard rotation of K before quantization (cloud.tencent.com.cn "NVFP4:
+// breaking the memory wall of GPU inference", quantization tricks: an
+// orthogonal transform spreads outliers over the vector): k' = H k * 2^-4 with
+// H the 128-point Sylvester matrix, H[i][j] = (-1)^popcount(i & j).  A row is
+// NB blocks of N values, block b in the lanes l ^ (4 * b) of one 32-lane
+// group; the transform runs in float64 (every sum of 128 values with a
+// 24-bit significand spanning at most 22 binades -- 38 for bf16 -- is exact)
+// and is rounded to float32 once.
+template <int N, int NB>
+__device__ __forceinline__ void hadamard_rotate_k(float (&x)[N], int b) {
+  double d[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) d[i] = (double)x[i];
+  wht_local<N>(d);
+  wht_cross<4>(d, N, (b & 1) != 0);
+  wht_cross<8>(d, N, (b & 2) != 0);
+  if (NB == 8) wht_cross<16>(d, N, (b & 4) != 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = (float)(d[i] * 0.0625);
+}
+
 // One quantized block: 16 E2M1 codes (low nibble = even value) and the E4M3 scale byte.
 struct QuantBlock {
   uint32_t packed[2];

@@ -17,6 +17,8 @@
 // The block quantizer (exact E4M3 scale, E2M1 codes by the hardware
 // conversion with an exact threshold fallback) is in nvfp4_quant_device.h,
 // shared with the decode step that appends its own new tokens.
+#include <type_traits>
+
 #include "nvfp4_quant_device.h"
 
 namespace nvfp4kv {
@@ -42,7 +44,10 @@ __device__ __forceinline__ void block_coords(int64_t i, const AppendParams& p, i
 // pass keeps the page-tile lane pattern); all of their loads are issued before
 // any of them is quantized.  R = 2 for bulk appends (more bytes in flight per
 // wave), R = 1 for small ones, where the per-thread chain is the latency.
-template <typename InT, int R>
+// kRotK: K rows are Hadamard-rotated before quantization (the 8 blocks of a
+// row sit in lanes l, l^4, .., l^28, so every lane of a 32-lane group takes
+// part in the exchanges; idle lanes hold token 0 and skip the store).
+template <typename InT, int R, bool kRotK>
 __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p, int64_t n_threads) {
   const int which = blockIdx.y;  // 0 = K, 1 = V
   const AppendTensor& T = p.t[which];
@@ -61,6 +66,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p, in
       t = 0;  // load token 0 (in range) and skip the store
     }
     load_block<InT>(reinterpret_cast<const InT*>(T.x) + t * p.token_stride + (int64_t)h[k] * kHeadDim + 16 * b[k], x[k]);
+  }
+  if (kRotK && which == 0) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) hadamard_rotate_k<16, 8>(x[k], b[k]);
   }
 #pragma unroll
   for (int k = 0; k < R; ++k)
@@ -82,14 +91,18 @@ hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hi
   const int64_t n_threads = (n_blocks / 128 + r - 1) / r * 128;
   const dim3 grid((unsigned)((n_threads + 255) / 256), 2, 1);
   const bool bf16 = dtype == NVFP4_DTYPE_BF16;
-  if (bf16 && bulk)
-    hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 2>), grid, dim3(256), 0, stream, p, n_threads);
-  else if (bf16)
-    hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, p, n_threads);
-  else if (bulk)
-    hipLaunchKernelGGL((quantize_append_kernel<float, 2>), grid, dim3(256), 0, stream, p, n_threads);
-  else
-    hipLaunchKernelGGL((quantize_append_kernel<float, 1>), grid, dim3(256), 0, stream, p, n_threads);
+  auto go = [&](auto rot) {
+    constexpr bool K = decltype(rot)::value;
+    if (bf16 && bulk)
+      hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 2, K>), grid, dim3(256), 0, stream, p, n_threads);
+    else if (bf16)
+      hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 1, K>), grid, dim3(256), 0, stream, p, n_threads);
+    else if (bulk)
+      hipLaunchKernelGGL((quantize_append_kernel<float, 2, K>), grid, dim3(256), 0, stream, p, n_threads);
+    else
+      hipLaunchKernelGGL((quantize_append_kernel<float, 1, K>), grid, dim3(256), 0, stream, p, n_threads);
+  };
+  if (p.rot_k) go(std::true_type{}); else go(std::false_type{});
   return hipGetLastError();
 }
 

@@ -23,12 +23,13 @@ class FilledLayer:
 
 
 def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device="cuda", on_chunk=None,
-                timed: bool = False, mx: bool = False) -> FilledLayer:
+                timed: bool = False, mx: bool = False, hadamard: bool = False) -> FilledLayer:
     """Quantize-append the first fill_lens[b] tokens of every sequence b.
 
     pool_lens[b] >= fill_lens[b] sizes each sequence's pages (room for tokens
     appended later).  on_chunk(c0, n, k, v, seq, pos) sees every generated chunk.
-    mx: fill an MXFP4 layer with the same tokens, slots and page table."""
+    mx: fill an MXFP4 layer with the same tokens, slots and page table.
+    hadamard: store K Hadamard-rotated (the global scales stay those of the unrotated K)."""
     pool_lens = [int(x) for x in pool_lens]
     bt, pool = synth.page_tables(pool_lens, seed=1000 + layer_idx)
     if mx:
@@ -51,7 +52,7 @@ def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device
             torch.cuda._sleep(1 << 20)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        append(layer, k, v, sl)
+        append(layer, k, v, sl, hadamard=hadamard)
         if timed:
             e1.record(stream)
             torch.cuda.synchronize()

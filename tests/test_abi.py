@@ -287,3 +287,24 @@ def test_mx_append_and_decode_checks():
     need = nk.decode_workspace_bytes(1, 64, 8, 1 << 20)
     assert dec(B=1, msl=1 << 20, bts=1 << 16, wsb=need - 1) == 3
 
+
+def test_hadamard_entry_points_check_like_their_plain_twins():
+    nk = _lib()
+    L, M = _layer(nk), _mx_layer(nk)
+    for f, lay in (("nvfp4_kv_quantize_append_hadamard", L), ("mxfp4_kv_quantize_append_hadamard", M)):
+        fn = getattr(nk.lib, f)
+        assert fn(None, None, None, 1, 1, 1024, None, None) == 1
+        assert fn(ctypes.byref(lay), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 1, 0, 1024, None, None) == 0
+        assert fn(ctypes.byref(lay), ctypes.c_void_p(FAKE + 4), ctypes.c_void_p(FAKE), 1, 4, 1024,
+                  ctypes.c_void_p(FAKE), None) == 2
+    for f, lay in (("nvfp4_paged_decode_attn_hadamard", L), ("mxfp4_paged_decode_attn_hadamard", M)):
+        fn = getattr(nk.lib, f)
+
+        def dec(q=FAKE, B=2, Hq=64, bts=4, msl=64, ws=FAKE, wsb=1 << 30):
+            return fn(ctypes.byref(lay), ctypes.c_void_p(q), 1, B, Hq, ctypes.c_void_p(FAKE), bts,
+                      ctypes.c_void_p(FAKE), msl, 0.088, ctypes.c_void_p(FAKE), ctypes.c_void_p(ws), wsb, None)
+        assert dec(Hq=60) == 1 and dec(Hq=8 * 17) == 2 and dec(bts=3) == 1 and dec(q=FAKE + 2) == 2
+        assert dec(B=0, q=0) == 0 and dec(ws=FAKE + 16) == 1
+        need = nk.decode_workspace_bytes(1, 64, 8, 1 << 20)
+        assert dec(B=1, msl=1 << 20, bts=1 << 16, wsb=need - 1) == 3
+
