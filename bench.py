@@ -10,7 +10,9 @@ token (one per sequence) + decode attention over the 8192-token caches.
 
 Printed: one JSON line.  `value` is decode-step effective HBM bandwidth
 (algorithmic bytes of append + decode per step / step wall time); the same line
-carries the bulk quantize-append GB/s, the FP8 workspace dequant GB/s, the
+carries the bulk quantize-append GB/s (a fill chunk re-appended back to back,
+alternating over two layers; the single-call figure of the fill beside it),
+the FP8 workspace dequant GB/s, the
 roofline of the dominant kernel (decode attention, timed with HIP events on the
 launch stream), the MXFP4 comparison format's append and decode on the same
 tokens, both formats with Hadamard-rotated K, and the CPU oracle timed on a
@@ -101,6 +103,23 @@ def back_to_back(stream, n, launch):
                   f"{gpu_s * 1e3:.2f} ms on the GPU; the back-to-back time includes host gaps", file=sys.stderr)
         per_call.append(gpu_s / n)
     return float(np.median(per_call))
+
+
+def append_b2b(stream, steps, chunks, targets, append, per_head, **kw):
+    """Bulk quantize-append timed like decode: calls queued back to back, each
+    re-appending the first fill chunk of a layer (the same tokens into the same
+    slots, so the cache keeps its bytes), alternating over the layers so that
+    no call finds its inputs in the caches.  Returns (us per call, GB/s of
+    algorithmic bytes)."""
+    def launch(i):
+        j = i % len(chunks)
+        k, v, sl = chunks[j]
+        append(targets[j], k, v, sl, **kw)
+    s = back_to_back(stream, steps, launch)
+    k0 = chunks[0][0]
+    n, H = k0.shape[0], k0.shape[1]
+    b = n * H * (2 * 128 * k0.element_size() + per_head) + 4 * n
+    return s * 1e6, b / s / 1e9
 
 
 def read_traffic(kernel_files, workload: str):
@@ -297,6 +316,18 @@ def bench_mixed(args, wl, dev):
         nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
                              workspace=dws)
     dec_b2b = back_to_back(stream, args.steps, dec_call)
+    # the step's append back to back (each call rewrites its layer's new tokens: the same bytes)
+    def app_call(i):
+        st = steps[i % L]
+        nk.quantize_append(st.filled.layer, st.new_k, st.new_v, st.new_slots)
+    app_b2b = back_to_back(stream, args.steps, app_call)
+    # bulk append back to back over the first fill chunk of two layers
+    from nvfp4_quantized_paged_kv_amd.workloads import first_chunk
+    b2b_layers = list(range(min(L, 2)))
+    bulk_us, bulk_gbs = append_b2b(stream, args.steps,
+                                   [first_chunk(wl, list(wl.lens), l, steps[l].filled.block_table, dev)
+                                    for l in b2b_layers],
+                                   [steps[l].filled.layer for l in b2b_layers], nk.quantize_append, 144)
 
     # ---- extend chunks: their K/V as FP8 rows after each prefix, then causal
     # attention of the chunk queries over [prefix | chunk] in the workspace
@@ -339,8 +370,9 @@ def bench_mixed(args, wl, dev):
         "decode_attn_gbs_events": round(achieved, 2),
         "decode_attn_us": round(dec_b2b * 1e6, 3),
         "decode_attn_us_per_call_events": round(dec.mean() * 1e6, 3),
-        "append_step_gbs": round(b_app / app.mean() / 1e9, 2),
-        "append_step_us": round(app.mean() * 1e6, 3),
+        "append_step_gbs": round(b_app / app_b2b / 1e9, 2),
+        "append_step_us": round(app_b2b * 1e6, 3),
+        "append_step_us_per_call_events": round(app.mean() * 1e6, 3),
         "fp8_workspace_gbs": round(b_ws / wsd.mean() / 1e9, 2),
         "fp8_workspace_us": round(wsd.mean() * 1e6, 3),
         "fp8_rows_us": round(float(np.median(rows_ms)) * 1e3, 3),
@@ -351,7 +383,9 @@ def bench_mixed(args, wl, dev):
                             "unit": "TFLOP/s", "frac": round(ext_tf / PEAK_F16_TFLOPS, 4),
                             "kernel": "nvfp4_fp8_extend_attn (extend_kernel)", "flops_per_call": int(ext_flops),
                             "query_tokens": t_ext, "key_pairs": int(pairs)},
-        "quantize_append_bulk_gbs": round(sum(append_bytes) / (sum(append_ms) / 1e3) / 1e9, 2),
+        "quantize_append_bulk_gbs": round(bulk_gbs, 2),
+        "quantize_append_bulk_us": round(bulk_us, 2),
+        "quantize_append_bulk_gbs_single_call": round(sum(append_bytes) / (sum(append_ms) / 1e3) / 1e9, 2),
         "bytes_per_step": int(b_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(DECODE_SOURCES, wl.name),
@@ -411,7 +445,7 @@ def main():
     from nvfp4_quantized_paged_kv_amd.workloads import build_layer
     warm_kernels(wl, dev)
 
-    layers, tables, newk, newv, slots_new, qs = [], [], [], [], [], []
+    layers, tables, newk, newv, slots_new, qs, bts = [], [], [], [], [], [], []
     append_ms, append_bytes = [], []
     for l in range(L):
         fl = build_layer(wl, [ctx - 1] * B, [ctx] * B, l, dev, timed=True)
@@ -420,6 +454,7 @@ def main():
         layers.append(fl.layer)
         tables.append(fl.block_table_dev)
         bt_np = fl.block_table
+        bts.append(bt_np)
         newk.append(synth.kv_values(B, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, dev, 3, l))
         newv.append(synth.kv_values(B, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, dev, 3, l))
         slots_new.append(torch.from_numpy(
@@ -548,6 +583,18 @@ def main():
     app_total_b = float(sum(append_bytes))
     app_total_s = float(sum(append_ms)) / 1e3
     traffic = read_traffic(DECODE_SOURCES, wl.name)
+    # bulk append back to back over the first fill chunk of two layers
+    from nvfp4_quantized_paged_kv_amd.workloads import first_chunk
+    b2b_layers = list(range(min(L, 2)))
+    chunks = {}
+
+    def chunk_set(fill):
+        if fill not in chunks:
+            chunks[fill] = [first_chunk(wl, [fill] * B, l, bts[l], dev) for l in b2b_layers]
+        return chunks[fill]
+    app_us, app_gbs = append_b2b(stream, args.steps, chunk_set(ctx - 1), [layers[l] for l in b2b_layers],
+                                 nk.quantize_append, 144)
+    print("[bench] bulk append timed back to back", file=sys.stderr, flush=True)
 
     # ---- MXFP4, the format the pages compare NVFP4 against (E8M0 scale per 32
     # values, 17/32 byte per value): the same tokens, slots and queries in
@@ -566,12 +613,16 @@ def main():
     for i in range(args.warmup):
         mx_call(i)
     mx_s = back_to_back(stream, args.steps, mx_call)
+    mx_app_us, mx_app_gbs = append_b2b(stream, args.steps, chunk_set(ctx), [mx_layers[l] for l in b2b_layers],
+                                       nk.mx_quantize_append, 136)
     bytes_mx = B * ctx * H * 136 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
     mxfp4 = {"decode_us": round(mx_s * 1e6, 3), "decode_gbs": round(bytes_mx / mx_s / 1e9, 2),
              "decode_frac": round(bytes_mx / mx_s / 1e9 / PEAK_HBM_GBS, 4),
              "algorithmic_bytes_per_call": int(bytes_mx),
              "decode_time_vs_nvfp4": round(mx_s / dec_avg_s, 4),
-             "quantize_append_bulk_gbs": round(float(sum(mx_app_b)) / (float(sum(mx_app_ms)) / 1e3) / 1e9, 2)}
+             "quantize_append_bulk_gbs": round(mx_app_gbs, 2), "quantize_append_bulk_us": round(mx_app_us, 2),
+             "quantize_append_bulk_gbs_single_call":
+                 round(float(sum(mx_app_b)) / (float(sum(mx_app_ms)) / 1e3) / 1e9, 2)}
     # ---- Hadamard-rotated K (both formats): the same tokens stored with K
     # rotated by the append kernel; the decode rotates Q in its prologue and
     # takes Q as a hi + lo pair (twice the QK^T MFMAs)
@@ -591,11 +642,17 @@ def main():
         for i in range(args.warmup):
             rot_call(i)
         rot_s = back_to_back(stream, args.steps, rot_call)
+        rot_app_us, rot_app_gbs = append_b2b(stream, args.steps, chunk_set(ctx), [rot_layers[l] for l in b2b_layers],
+                                             nk.mx_quantize_append if mx else nk.quantize_append, 136 if mx else 144,
+                                             hadamard=True)
         b_rot = bytes_mx if mx else bytes_decode
         plain_s = mx_s if mx else dec_avg_s
         hadamard[fmt] = {"decode_us": round(rot_s * 1e6, 3), "decode_gbs": round(b_rot / rot_s / 1e9, 2),
                          "decode_time_vs_unrotated": round(rot_s / plain_s, 4),
-                         "quantize_append_bulk_gbs": round(float(sum(rot_b)) / (float(sum(rot_ms)) / 1e3) / 1e9, 2)}
+                         "quantize_append_bulk_gbs": round(rot_app_gbs, 2),
+                         "quantize_append_bulk_us": round(rot_app_us, 2),
+                         "quantize_append_bulk_gbs_single_call":
+                             round(float(sum(rot_b)) / (float(sum(rot_ms)) / 1e3) / 1e9, 2)}
         del rot_layers
     print("[bench] Hadamard-rotated layers timed", file=sys.stderr, flush=True)
     del mx_layers
@@ -626,7 +683,10 @@ def main():
                             "value": round(bytes_step / (wall_one / args.steps) / 1e9, 2),
                             "kernel_us_b2b": round(fused_s * 1e6, 3)},
         "append_step_us": round(float(app_ms.mean()) * 1e3, 3),
-        "quantize_append_bulk_gbs": round(app_total_b / app_total_s / 1e9, 2),
+        "quantize_append_bulk_gbs": round(app_gbs, 2),
+        "quantize_append_bulk_us": round(app_us, 2),
+        "quantize_append_bulk_chunk_tokens": int(chunk_set(ctx - 1)[0][0].shape[0]),
+        "quantize_append_bulk_gbs_single_call": round(app_total_b / app_total_s / 1e9, 2),
         "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),
         "fp8_workspace_gbs": round(ws_gbs, 2),
         "fp8_workspace_tokens": int(n_ext * ctx),

@@ -76,8 +76,8 @@ nvfp4_status_t append_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
   const int64_t esize = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || (token_stride_elems * esize) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
   AppendParams p;
-  p.t[0] = AppendTensor{k_new, layer->k_codes, layer->k_scales, layer->k_global};
-  p.t[1] = AppendTensor{v_new, layer->v_codes, layer->v_scales, layer->v_global};
+  p.t[0] = AppendTensor{k_new, layer->k_codes, layer->k_scales, layer->k_global, 1.0 / (6.0 * (double)layer->k_global)};
+  p.t[1] = AppendTensor{v_new, layer->v_codes, layer->v_scales, layer->v_global, 1.0 / (6.0 * (double)layer->v_global)};
   p.slots = slot_mapping;
   p.token_stride = token_stride_elems;
   p.num_tokens = num_tokens;

@@ -290,7 +290,8 @@ __device__ __forceinline__ void append_own_tokens(const DecodeParams& p, int b, 
       float x[16];
       if (QF32) load_block<float>(reinterpret_cast<const float*>(which ? p.v_new : p.k_new) + src, x);
       else load_block<uint16_t>(reinterpret_cast<const uint16_t*>(which ? p.v_new : p.k_new) + src, x);
-      const QuantBlock q = quantize_block16(x, which ? p.v_global : p.k_global);
+      const float g = which ? p.v_global : p.k_global;
+      const QuantBlock q = quantize_block16(x, g, 1.0 / (6.0 * (double)g));
       store_block(const_cast<uint8_t*>(which ? p.v_codes : p.k_codes), const_cast<uint8_t*>(which ? p.v_scales : p.k_scales),
                   p.H, which != 0, page * kPageSize + pos % kPageSize, h, blk, q);
     }

@@ -23,6 +23,7 @@ struct AppendTensor {
   uint8_t* codes;        // code plane
   uint8_t* scales;       // scale plane
   float g;               // FP32 global scale
+  double r6;             // 1/(6g) rounded to float64
 };
 
 struct AppendParams {

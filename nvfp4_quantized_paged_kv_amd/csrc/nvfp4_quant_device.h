@@ -5,11 +5,12 @@
 // section 2: 16 consecutive values share an E4M3 scale, the tensor an FP32
 // scale, and a block's amax maps to the E2M1 maximum 6.
 //
-// Scale: bs = E4M3 nearest to amax/(6g), from the correctly rounded float64
-// quotient (no float64 rounding can cross or land on an E4M3 midpoint).
+// Scale: bs = E4M3 nearest to amax/(6g), from a float64 quotient within
+// about 2^-104 of the exact one (no such error can cross or land on an E4M3
+// midpoint, and an exact midpoint comes out exactly).
 // Codes, fast path: v_cvt_scalef32_pk_fp4_f32 (nearest E2M1, ties to even,
 // saturating at 6) of |x| times c_lo and times c_hi, two float32 bounds of
-// 1/(bs*g) (the float64 reciprocal scaled by 1 -/+ 2^-21); equal codes are
+// 1/(bs*g) (the float32 reciprocal scaled by 1 -/+ 2^-20); equal codes are
 // the exact code, and an exact tie always makes them differ.  Codes, exact
 // path (a block where any pair differs, or a zero scale): the magnitude is the
 // number of float32 thresholds u_k the value exceeds, where u_k = RN(mid_k*bs*g)
@@ -126,20 +127,39 @@ struct QuantBlock {
   uint32_t sb;
 };
 
-__device__ __forceinline__ QuantBlock quantize_block16(const float (&x)[16], float g) {
+// r6 = 1/(6g) rounded to float64 (computed once per call by the caller).
+__device__ __forceinline__ QuantBlock quantize_block16(const float (&x)[16], float g, double r6) {
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
 
   QuantBlock q;
-  q.sb = e4m3_encode_rne_sat((double)amax / (6.0 * (double)g));
+  {
+    // amax/(6g) without a division: q0 = amax*r6 is within 2^-52 (relative) of
+    // the quotient, and one correction with the exact residual amax - q0*6g
+    // (one fma; 6g is exact in float64) brings it within about 2^-104.  An
+    // exact quotient that is an E4M3 midpoint (5 significant bits) then comes
+    // out exactly, and any other quotient lies at least 2^-31 (relative) from
+    // every midpoint (amax has 24 significant bits, 6*g*midpoint at most 31),
+    // so the E4M3 rounding below sees the same side as for the exact quotient.
+    const double a = (double)amax, g6 = 6.0 * (double)g;
+    const double q0 = a * r6;
+    q.sb = e4m3_encode_rne_sat(__builtin_fma(__builtin_fma(-q0, g6, a), r6, q0));
+  }
   const float bs = e4m3_value(q.sb);
 
   q.packed[0] = q.packed[1] = 0u;
-  bool exact_path = bs == 0.0f;  // zero scale: every code is its sign (threshold path, thresholds +inf)
+  // the fast path needs bs*g (rounded) to be a normal float32 whose reciprocal
+  // is normal too; a zero scale (every code is its sign) and extreme global
+  // scales take the threshold path
+  const float bsg = bs * g;
+  bool exact_path = !(bsg >= 0x1p-125f && bsg <= 0x1p125f);
   if (!exact_path) {
-    const double rcp = 1.0 / ((double)bs * (double)g);  // bs*g exact in float64
-    const float c_lo = (float)(rcp * (1.0 - 0x1p-21)), c_hi = (float)(rcp * (1.0 + 0x1p-21));
+    // r is within 1 ulp (2^-23) of 1/bsg and bsg within 2^-24 of bs*g, so the
+    // margins of 2^-20 keep c_lo below and c_hi above 1/(bs*g) by more than
+    // 0.74 * 2^-20 after rounding
+    const float r = __builtin_amdgcn_rcpf(bsg);
+    const float c_lo = r * (1.0f - 0x1p-20f), c_hi = r * (1.0f + 0x1p-20f);
     uint32_t hi[2] = {0u, 0u};
     cvt_pair<0>(q.packed, hi, x, c_lo, c_hi);
     cvt_pair<1>(q.packed, hi, x, c_lo, c_hi);

@@ -13,10 +13,17 @@
 // group of 16 tokens.  Sixteen consecutive tokens usually fill one page, so a
 // 256-lane workgroup writes whole (page, kv head) tiles of two heads: its K and
 // V code runs and its 128-B scale rows are complete lines written by one CU.
+// A thread's input load never waits for its slot: the slot is checked at the
+// store.  Plain appends take one job per thread and run at the rate of the
+// memory system.  Bulk appends of Hadamard-rotated K, whose arithmetic is the
+// limit, run on a grid the device holds at once, each thread walking jobs a
+// grid-wide stride apart and loading the next pair's inputs before it
+// quantizes the current pair.
 //
 // The block quantizer (exact E4M3 scale, E2M1 codes by the hardware
 // conversion with an exact threshold fallback) is in nvfp4_quant_device.h,
 // shared with the decode step that appends its own new tokens.
+#include <algorithm>
 #include <type_traits>
 
 #include "nvfp4_quant_device.h"
@@ -27,7 +34,7 @@ namespace {
 // Quantize one 16-value block x and store its codes and scale byte at `slot`.
 __device__ __forceinline__ void quantize_store(const float (&x)[16], const AppendTensor& T, const AppendParams& p,
                                                int which, int32_t slot, int h, int b) {
-  store_block(T.codes, T.scales, p.H, which != 0, slot, h, b, quantize_block16(x, T.g));
+  store_block(T.codes, T.scales, p.H, which != 0, slot, h, b, quantize_block16(x, T.g, T.r6));
 }
 
 // Block index i of the flattened work -> (token t, kv head h, block b); t < 0 if past the end.
@@ -40,70 +47,165 @@ __device__ __forceinline__ void block_coords(int64_t i, const AppendParams& p, i
   if (t >= p.num_tokens) t = -1;
 }
 
-// Each thread takes R blocks, n_threads apart in the flattened order (so every
-// pass keeps the page-tile lane pattern); all of their loads are issued before
-// any of them is quantized.  R = 2 for bulk appends (more bytes in flight per
-// wave), R = 1 for small ones, where the per-thread chain is the latency.
+// The raw input words of one block (16 values): 32 B of bf16 or 64 B of f32.
+template <typename InT>
+struct RawBlock {
+  uint4 w[sizeof(InT) == 2 ? 2 : 4];
+};
+
+template <typename InT>
+__device__ __forceinline__ RawBlock<InT> load_raw(const InT* src) {
+  RawBlock<InT> r;
+#pragma unroll
+  for (int i = 0; i < (sizeof(InT) == 2 ? 2 : 4); ++i) r.w[i] = reinterpret_cast<const uint4*>(src)[i];
+  return r;
+}
+
+template <typename InT>
+__device__ __forceinline__ void widen(const RawBlock<InT>& r, float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < (sizeof(InT) == 2 ? 2 : 4); ++i) {
+    const uint32_t w[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (sizeof(InT) == 2) {
+        x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      } else {
+        x[4 * i + j] = __uint_as_float(w[j]);
+      }
+    }
+  }
+}
+
+// One job: its block coordinates, slot (stored only if live and inside the
+// cache) and raw inputs.
+template <typename InT>
+struct Job {
+  RawBlock<InT> raw;
+  int32_t slot;
+  bool live;
+  int h, b;
+};
+
+// The input load does not wait for the slot: a job past the end, or of a
+// skipped token, loads token 0 (always in range) and is dropped at the store.
+// Both loads are unconditional (no branch around them), so the compiler can
+// count the memory operations in flight and wait only for the ones it needs.
+template <typename InT>
+__device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const AppendTensor& T, int64_t i, int64_t n_jobs) {
+  Job<InT> j;
+  int64_t t;
+  block_coords(i < n_jobs ? i : 0, p, t, j.h, j.b);
+  j.live = i < n_jobs && t >= 0;
+  const int64_t tt = j.live ? t : 0;
+  j.slot = p.slots[tt];  // issued first: waiting for it never waits for the inputs
+  j.raw = load_raw<InT>(reinterpret_cast<const InT*>(T.x) + tt * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b);
+  return j;
+}
+
+template <typename InT, bool kRotK>
+__device__ __forceinline__ void finish_job(const Job<InT>& j, const AppendTensor& T, const AppendParams& p, int which) {
+  float x[16];
+  widen<InT>(j.raw, x);
+  if (kRotK && which == 0) hadamard_rotate_k<16, 8>(x, j.b);
+  if (j.live && j.slot >= 0 && (int64_t)j.slot < (int64_t)p.num_pages * kPageSize)
+    quantize_store(x, T, p, which, j.slot, j.h, j.b);
+}
+
+// One job per thread: a single load, quantize and store chain per thread.
 // kRotK: K rows are Hadamard-rotated before quantization (the 8 blocks of a
 // row sit in lanes l, l^4, .., l^28, so every lane of a 32-lane group takes
 // part in the exchanges; idle lanes hold token 0 and skip the store).
-template <typename InT, int R, bool kRotK>
-__global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p, int64_t n_threads) {
+template <typename InT, bool kRotK>
+__global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p, int64_t n_jobs) {
   const int which = blockIdx.y;  // 0 = K, 1 = V
   const AppendTensor& T = p.t[which];
-  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i0 >= n_threads) return;
-  float x[R][16];
-  int32_t slot[R];
-  int h[R], b[R];
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    int64_t t;
-    block_coords(i0 + k * n_threads, p, t, h[k], b[k]);
-    slot[k] = t >= 0 ? p.slots[t] : -1;
-    if (slot[k] < 0 || (int64_t)slot[k] >= (int64_t)p.num_pages * kPageSize) {
-      slot[k] = -1;
-      t = 0;  // load token 0 (in range) and skip the store
-    }
-    load_block<InT>(reinterpret_cast<const InT*>(T.x) + t * p.token_stride + (int64_t)h[k] * kHeadDim + 16 * b[k], x[k]);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_jobs) return;
+  finish_job<InT, kRotK>(fetch_job<InT>(p, T, i, n_jobs), T, p, which);
+}
+
+// Bulk rotated-K appends: a fixed grid of what the device holds at once walks the
+// jobs with a stride that is a multiple of 128 (whole 16-token groups of one
+// head, so every pass keeps the page-tile lane pattern), two jobs per step,
+// and loads the next step's inputs before it quantizes the current ones, so
+// each wave keeps reads in flight while it computes.  All lanes of a wave see
+// the same trip count (jobs come in aligned groups of 128), so the lane
+// exchanges of the rotated-K path stay uniform.
+template <typename InT, bool kRotK>
+__global__ __launch_bounds__(256) void quantize_append_stream_kernel(AppendParams p, int64_t n_jobs) {
+  const int which = blockIdx.y;  // 0 = K, 1 = V
+  const AppendTensor& T = p.t[which];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_jobs) return;
+  // two register sets, each loaded a step ahead of its use and consumed in
+  // place (a copy of a set in flight would wait for its loads)
+  Job<InT> a0 = fetch_job<InT>(p, T, i, n_jobs);
+  Job<InT> a1 = fetch_job<InT>(p, T, i + stride, n_jobs);
+  while (true) {
+    const Job<InT> b0 = fetch_job<InT>(p, T, i + 2 * stride, n_jobs);
+    const Job<InT> b1 = fetch_job<InT>(p, T, i + 3 * stride, n_jobs);
+    finish_job<InT, kRotK>(a0, T, p, which);
+    finish_job<InT, kRotK>(a1, T, p, which);
+    if (i + 2 * stride >= n_jobs) break;  // uniform across the wave
+    a0 = fetch_job<InT>(p, T, i + 4 * stride, n_jobs);
+    a1 = fetch_job<InT>(p, T, i + 5 * stride, n_jobs);
+    finish_job<InT, kRotK>(b0, T, p, which);
+    finish_job<InT, kRotK>(b1, T, p, which);
+    i += 4 * stride;
+    if (i >= n_jobs) break;
   }
-  if (kRotK && which == 0) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) hadamard_rotate_k<16, 8>(x[k], b[k]);
-  }
-#pragma unroll
-  for (int k = 0; k < R; ++k)
-    if (slot[k] >= 0) quantize_store(x[k], T, p, which, slot[k], h[k], b[k]);
 }
 
 // blocks (16 values of one token and head) from which an append counts as bulk
 constexpr int64_t kAppendBulkBlocks = 1 << 18;
 
+// Workgroups of one tensor's streaming grid: half of what the device holds at
+// once (K and V share the launch), so no workgroup waits for another to end.
+template <typename Kernel>
+hipError_t stream_groups(Kernel kernel, int64_t n_blocks, int64_t& groups) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+  if (e != hipSuccess) return e;
+  groups = std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * per_cu / 2, (n_blocks + 255) / 256));
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream) {
-  const int64_t n_blocks = (int64_t)((p.num_tokens + 15) / 16) * 16 * p.H * 8;  // tokens rounded up to groups of 16
+  // jobs: one per 16-value block, tokens rounded up to whole groups of 16 (a
+  // multiple of 128 jobs, one group of one head)
+  const int64_t n_blocks = (int64_t)((p.num_tokens + 15) / 16) * 16 * p.H * 8;
   if (n_blocks == 0) return hipSuccess;
-  // threads per pass, a multiple of 128 (one 16-token group of one head) so
-  // every pass starts on a group boundary
-  const bool bulk = n_blocks >= kAppendBulkBlocks;
-  const int r = bulk ? 2 : 1;
-  const int64_t n_threads = (n_blocks / 128 + r - 1) / r * 128;
-  const dim3 grid((unsigned)((n_threads + 255) / 256), 2, 1);
-  const bool bf16 = dtype == NVFP4_DTYPE_BF16;
-  auto go = [&](auto rot) {
+  hipError_t err = hipSuccess;
+  auto go = [&](auto in, auto rot) {
+    using InT = decltype(in);
     constexpr bool K = decltype(rot)::value;
-    if (bf16 && bulk)
-      hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 2, K>), grid, dim3(256), 0, stream, p, n_threads);
-    else if (bf16)
-      hipLaunchKernelGGL((quantize_append_kernel<uint16_t, 1, K>), grid, dim3(256), 0, stream, p, n_threads);
-    else if (bulk)
-      hipLaunchKernelGGL((quantize_append_kernel<float, 2, K>), grid, dim3(256), 0, stream, p, n_threads);
-    else
-      hipLaunchKernelGGL((quantize_append_kernel<float, 1, K>), grid, dim3(256), 0, stream, p, n_threads);
+    if (K && n_blocks >= kAppendBulkBlocks) {
+      // the rotation's arithmetic is what limits a bulk rotated append: overlap it with the next loads
+      int64_t groups = 0;
+      err = stream_groups(quantize_append_stream_kernel<InT, K>, n_blocks, groups);
+      if (err != hipSuccess) return;
+      hipLaunchKernelGGL((quantize_append_stream_kernel<InT, K>), dim3((unsigned)groups, 2, 1), dim3(256), 0, stream, p,
+                         n_blocks);
+    } else {
+      // plain appends run at the memory system's rate with one job per thread
+      hipLaunchKernelGGL((quantize_append_kernel<InT, K>), dim3((unsigned)((n_blocks + 255) / 256), 2, 1), dim3(256), 0,
+                         stream, p, n_blocks);
+    }
   };
-  if (p.rot_k) go(std::true_type{}); else go(std::false_type{});
-  return hipGetLastError();
+  const bool bf16 = dtype == NVFP4_DTYPE_BF16;
+  if (p.rot_k) {
+    if (bf16) go(uint16_t{}, std::true_type{}); else go(float{}, std::true_type{});
+  } else {
+    if (bf16) go(uint16_t{}, std::false_type{}); else go(float{}, std::false_type{});
+  }
+  return err != hipSuccess ? err : hipGetLastError();
 }
 
 }  // namespace nvfp4kv

@@ -64,6 +64,17 @@ def build_layer(wl: synth.Workload, fill_lens, pool_lens, layer_idx: int, device
     return FilledLayer(layer, bt, torch.from_numpy(bt).to(device), ms, by)
 
 
+def first_chunk(wl: synth.Workload, fill_lens, layer_idx: int, block_table: np.ndarray, device="cuda"):
+    """The first chunk build_layer appends to layer layer_idx: (k, v, slots) on
+    the device, the same tokens and slots, so appending it again rewrites the
+    same bytes."""
+    seq_all, pos_all = synth.token_positions(fill_lens)
+    c0, n, k, v = next(iter(synth.layer_token_chunks(wl, fill_lens, layer_idx, device)))
+    seq, pos = seq_all[c0:c0 + n], pos_all[c0:c0 + n]
+    slots = (block_table[seq, pos // synth.PAGE].astype(np.int64) * synth.PAGE + pos % synth.PAGE).astype(np.int32)
+    return k, v, torch.from_numpy(slots).to(device)
+
+
 @dataclass
 class MixedStep:
     """One layer of the mixed serving step, ready to run."""
