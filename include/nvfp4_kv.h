@@ -176,8 +176,13 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
  * their slots come from block_table.  The result is the same as
  * nvfp4_kv_quantize_append of those tokens followed by
  * nvfp4_paged_decode_attn_multi: the same cache bytes and the same output.
- * The workgroup that reads a page holding a new token quantizes and stores
- * that token itself before it loads the page, so no workgroup waits on another.
+ * Schedule: when a unit holds at most 4096 pages (max_seq_len <= 65,536) the
+ * step is one launch -- the workgroup that reads a page holding a new token
+ * quantizes and stores that token itself before it loads the page, so no
+ * workgroup waits on another.  Longer units take two launches on `stream`
+ * (the append kernel, with each new token's slot taken from block_table,
+ * then the decode), which measured faster there.  Both give the same bytes
+ * and output.
  *   k_new, v_new : [batch][q_per_seq][num_kv_heads][128] of dtype (the
  *                  query's dtype), 16-byte aligned.  Positions < 0
  *                  (seq_lens[b] < q_per_seq) and out-of-range page indices

@@ -28,12 +28,21 @@ struct AppendTensor {
 
 struct AppendParams {
   AppendTensor t[2];     // [0] = K (token-major tile layout), [1] = V (decode-friendly tile layout)
-  const int32_t* slots;  // [num_tokens]
+  const int32_t* slots;  // [num_tokens], or nullptr: slots of a decode step's new tokens (below)
   int64_t token_stride;
   int32_t num_tokens;
   int32_t H;
   int32_t num_pages;
   int32_t rot_k;         // 1: Hadamard-rotate K rows before quantization
+  // decode-step slots (slots == nullptr): token t = b*step_T + i sits at
+  // position min(seq_lens[b], max_seq_len) - step_T + i (skipped when
+  // negative), in page block_table[b*bt_stride + position/16] (skipped when
+  // outside the cache) -- the positions the fused decode step appends at
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t bt_stride;
+  int32_t step_T;
+  int32_t max_seq_len;
 };
 
 hipError_t launch_quantize_append(const AppendParams& p, nvfp4_dtype_t dtype, hipStream_t stream);

@@ -88,6 +88,15 @@ struct Job {
   int h, b;
 };
 
+// Slot of new token t of a decode step (AppendParams, slots == nullptr), -1 to skip.
+__device__ __forceinline__ int32_t step_slot(const AppendParams& p, int64_t t) {
+  const int b = (int)(t / p.step_T), i = (int)(t - (int64_t)b * p.step_T);
+  const int pos = min(p.seq_lens[b], p.max_seq_len) - p.step_T + i;
+  if (pos < 0) return -1;
+  const int page = p.block_table[(int64_t)b * p.bt_stride + pos / kPageSize];
+  return (unsigned)page < (unsigned)p.num_pages ? page * kPageSize + pos % kPageSize : -1;
+}
+
 // The input load does not wait for the slot: a job past the end, or of a
 // skipped token, loads token 0 (always in range) and is dropped at the store.
 // Both loads are unconditional (no branch around them), so the compiler can
@@ -99,7 +108,7 @@ __device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const Appen
   block_coords(i < n_jobs ? i : 0, p, t, j.h, j.b);
   j.live = i < n_jobs && t >= 0;
   const int64_t tt = j.live ? t : 0;
-  j.slot = p.slots[tt];  // issued first: waiting for it never waits for the inputs
+  j.slot = p.slots ? p.slots[tt] : step_slot(p, tt);  // issued first: waiting for it never waits for the inputs
   j.raw = load_raw<InT>(reinterpret_cast<const InT*>(T.x) + tt * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b);
   return j;
 }

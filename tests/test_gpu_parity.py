@@ -322,16 +322,28 @@ def test_decode_multi_one_token_is_plain_decode():
     ([1, 3, 5], 1, 2, 4, torch.bfloat16),            # sequences shorter than the new tokens
 ])
 def test_decode_step_equals_append_then_decode(lens, H, G, T, qdt):
+    _step_case(lens, H, G, T, qdt, max(lens))
+
+
+@pytest.mark.parametrize("lens,H,G,T", [([33, 16, 17, 1000], 2, 8, 1), ([17, 40, 2], 2, 8, 2), ([1, 3, 5], 1, 2, 4)])
+def test_decode_step_two_launch_schedule(lens, H, G, T):
+    """max_seq_len above 65,536 tokens: the step appends with the append kernel, then decodes."""
+    _step_case(lens, H, G, T, torch.bfloat16, 70000)
+
+
+def _step_case(lens, H, G, T, qdt, msl):
     import nvfp4_quantized_paged_kv_amd as nk
 
-    _say(f"case: decode step lens={lens} H={H} G={G} T={T} q={qdt}")
+    _say(f"case: decode step lens={lens} H={H} G={G} T={T} q={qdt} max_seq_len={msl}")
     B, Hq = len(lens), H * G
     c = build_cache(lens, H, torch.bfloat16, "sparse6", 0.003, False, seed=sum(lens) + 5 * T)
     kn = synth.kv_values(B * T, H, "sparse6", 0.003, 0, qdt, "cpu", 77, T).reshape(B, T, H, 128)
     vn = synth.kv_values(B * T, H, "sparse6", 0.003, 1, qdt, "cpu", 77, T).reshape(B, T, H, 128)
     q = synth.queries(B * T, Hq, qdt, "cpu", 78, T).reshape(B, T, Hq, 128)
-    msl = max(lens)
-    bt = torch.from_numpy(c.bt).cuda()
+    bt_h = c.bt
+    if bt_h.shape[1] * 16 < msl:  # room for max_seq_len (entries past the sequences are never read)
+        bt_h = np.concatenate([bt_h, np.zeros((B, (msl + 15) // 16 - bt_h.shape[1]), np.int32)], 1)
+    bt = torch.from_numpy(np.ascontiguousarray(bt_h)).cuda()
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     # the new tokens' slots (positions len - T + i >= 0)
     pos = [(b, i, lens[b] - T + i) for b in range(B) for i in range(T)]
