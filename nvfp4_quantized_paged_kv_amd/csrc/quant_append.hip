@@ -18,7 +18,9 @@
 // memory system.  Bulk appends of Hadamard-rotated K, whose arithmetic is the
 // limit, run on a grid the device holds at once, each thread walking jobs a
 // grid-wide stride apart and loading the next pair's inputs before it
-// quantizes the current pair.
+// quantizes the current pair.  A decode step that appends with this kernel
+// passes no slot array: each new token's slot comes from the block table at
+// the position the step gives it (step_slot).
 //
 // The block quantizer (exact E4M3 scale, E2M1 codes by the hardware
 // conversion with an exact threshold fallback) is in nvfp4_quant_device.h,
