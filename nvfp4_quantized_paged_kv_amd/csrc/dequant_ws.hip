@@ -74,7 +74,6 @@ __global__ __launch_bounds__(kWsWaves * 64) void dequant_ws_kernel(DequantWsPara
   const uint8_t* codes = p.codes[which];
   const uint8_t* scales = p.scales[which];
   uint8_t* ws = p.ws[which];
-  // four tiles per step: their loads are all in flight before any is written
   struct Tile {
     uint4 c;
     uint32_t sc;
@@ -126,13 +125,28 @@ __global__ __launch_bounds__(kWsWaves * 64) void dequant_ws_kernel(DequantWsPara
       }
     }
   };
-  for (int i = 0; i < kWsTilesPerWave; i += 4) {
+  // two register sets of four tiles, each consumed in place: the next set's
+  // loads are issued before the current set is written (fetch past the last
+  // tile reads tile 0 and put skips it)
+  Tile a0 = fetch(0), a1 = fetch(1), a2 = fetch(2), a3 = fetch(3);
+  for (int i = 0; i < kWsTilesPerWave; i += 8) {
     if (tile0 + (int64_t)i * kWsWaves + wave >= tiles) break;
-    const Tile t0 = fetch(i), t1 = fetch(i + 1), t2 = fetch(i + 2), t3 = fetch(i + 3);
-    put(t0);
-    put(t1);
-    put(t2);
-    put(t3);
+    const Tile b0 = fetch(i + 4), b1 = fetch(i + 5), b2 = fetch(i + 6), b3 = fetch(i + 7);
+    put(a0);
+    put(a1);
+    put(a2);
+    put(a3);
+    if (tile0 + (int64_t)(i + 4) * kWsWaves + wave >= tiles) break;
+    if (i + 8 < kWsTilesPerWave) {
+      a0 = fetch(i + 8);
+      a1 = fetch(i + 9);
+      a2 = fetch(i + 10);
+      a3 = fetch(i + 11);
+    }
+    put(b0);
+    put(b1);
+    put(b2);
+    put(b3);
   }
 }
 
