@@ -324,6 +324,8 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_rows_to_workspace(const void* k_new, const vo
   p.ws[1] = ws_v;
   p.ws_scale[0] = k_ws_scale;
   p.ws_scale[1] = v_ws_scale;
+  p.ws_rcp[0] = 1.0 / (double)k_ws_scale;
+  p.ws_rcp[1] = 1.0 / (double)v_ws_scale;
   p.rows = ws_rows;
   p.token_stride = token_stride_elems;
   p.num_tokens = num_tokens;

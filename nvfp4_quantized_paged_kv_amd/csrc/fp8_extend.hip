@@ -35,10 +35,13 @@ namespace {
 
 // ------------------------------------------------------------------ FP8 rows
 // One thread per 16 consecutive values of one (token, kv head); blockIdx.y
-// picks K or V.  Byte = sign(x) | E4M3 nearest to |x| / ws_scale: the float64
-// quotient of a float32 dividend rounds like the exact real quotient (an E4M3
-// midpoint times the divisor has at most 29 significant bits, so a dividend
-// that is not on it lies at least 2^-30 away, relative).
+// picks K or V.  Byte = sign(x) | E4M3 nearest to |x| / ws_scale.  An E4M3
+// midpoint times the divisor has at most 29 significant bits, so a float32
+// dividend that is not on it lies at least 2^-30 (relative) away.  The
+// quotient is |x| * RN(1/ws_scale) (within 2^-52) plus one correction with
+// the exact residual |x| - q0 * ws_scale (one fma), within about 2^-104 of
+// the exact one: it rounds like the exact quotient, and an exact midpoint
+// comes out exactly (ties to even).
 template <typename InT>
 __global__ __launch_bounds__(256) void fp8_rows_kernel(Fp8RowsParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -48,8 +51,7 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(Fp8RowsParams p) {
   const int64_t th = i >> 3;
   const int h = (int)(th % p.H);
   const int64_t t = th / p.H;
-  const int row = p.rows[t];
-  if (row < 0 || row >= p.ws_capacity) return;
+  const int row = p.rows[t];  // checked at the store: the input loads do not wait for it
   const uint8_t* src = reinterpret_cast<const uint8_t*>(p.x[tensor]) +
                        (t * p.token_stride + (int64_t)h * kHeadDim + grp * 16) * (int64_t)sizeof(InT);
   float v[16];
@@ -74,14 +76,17 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(Fp8RowsParams p) {
       v[4 * k + 3] = __uint_as_float(w.w);
     }
   }
-  const double s = (double)p.ws_scale[tensor];
+  const double s = (double)p.ws_scale[tensor], r = p.ws_rcp[tensor];
   uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const uint32_t mag = e4m3_encode_rne_sat((double)__builtin_fabsf(v[k]) / s);
+    const double a = (double)__builtin_fabsf(v[k]);
+    const double q0 = a * r;
+    const uint32_t mag = e4m3_encode_rne_sat(__builtin_fma(__builtin_fma(-q0, s, a), r, q0));
     const uint32_t byte = mag | ((__float_as_uint(v[k]) >> 24) & 0x80u);
     w[k >> 2] |= byte << (8 * (k & 3));
   }
+  if (row < 0 || row >= p.ws_capacity) return;
   *reinterpret_cast<uint4*>(p.ws[tensor] + ((int64_t)row * p.H + h) * kHeadDim + grp * 16) =
       uint4{w[0], w[1], w[2], w[3]};
 }

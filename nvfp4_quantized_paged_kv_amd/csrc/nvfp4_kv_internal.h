@@ -137,6 +137,7 @@ struct Fp8RowsParams {
   const void* x[2];      // K, V: [num_tokens][H][128], token stride `token_stride` elements
   uint8_t* ws[2];        // [ws_capacity][H][128]
   float ws_scale[2];
+  double ws_rcp[2];      // 1/ws_scale rounded to float64
   const int32_t* rows;   // [num_tokens] workspace row per token (< 0: skip)
   int64_t token_stride;
   int32_t num_tokens;
