@@ -145,6 +145,21 @@ def test_extend_peaked_softmax(q_scale):
     assert err.max() <= ATTN_TOL, err.max()
 
 
+def test_extend_huge_logits_stay_finite():
+    """Logits far above 2^32 (a huge softmax scale): the weights come from the
+    rounded logit, so the largest one is exactly 2^0 and none overflows; the
+    output is a convex combination of V rows and matches the oracle."""
+    _say("case: extend huge logits")
+    rng = np.random.default_rng(67)
+    prefixes, chunks = [90, 0], [33, 20]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, 16, torch.bfloat16, seed=5, sm=1e12)
+    assert np.isfinite(got[rows]).all()
+    err = row_rel_err(got[rows], ref)
+    _say(f"  finite; max row rel err vs oracle {err.max():.2e}")
+    assert err.max() <= ATTN_TOL, err.max()
+
+
 def test_extend_rows_outside_chunks_are_untouched():
     """Tokens past max_chunk_len and query rows after the last chunk are not written."""
     _say("case: extend untouched rows")
