@@ -172,6 +172,19 @@ def test_decode_peaked_softmax(q_scale):
     assert err.max() <= ATTN_TOL, err.max()
 
 
+def test_decode_huge_logits_stay_finite():
+    """Queries scaled by 1e13 (logits far above 2^32): the softmax weights come
+    from the rounded logit, so none overflows; the output stays finite and
+    matches the oracle."""
+    _say("case: decode huge logits")
+    c = build_cache([300, 47, 129], 2, torch.bfloat16, "sparse6", 0.005, False, seed=83)
+    got, ref = decode_both(c, 2 * 8, torch.bfloat16, seed=11, q_scale=1e13)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    _say(f"  finite; max row rel err vs oracle {err.max():.2e}")
+    assert err.max() <= ATTN_TOL, err.max()
+
+
 def test_decode_split_count_invariance():
     """A larger max_seq_len changes the split geometry; both results stay within the parity bound.
 
