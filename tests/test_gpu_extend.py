@@ -117,6 +117,28 @@ def _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, qdt, seed, q_scale=
     return got, rows, ref
 
 
+def test_fp8_rows_ties_non_power_of_two_scale():
+    """Quotients exactly on E4M3 midpoints with a 12-bit workspace scale that is
+    not a power of two (1/scale is inexact): ties go to the even byte."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: fp8 rows ties, scale 1.234375")
+    H, T, s = 2, 4, 1.234375
+    e4 = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    mids = (e4[:-1] + e4[1:]) / 2  # at most 5 significant bits: mid * s is exact in float32
+    x = np.resize(np.concatenate([mids, -mids]) * s, T * H * 128).astype(np.float32).reshape(T, H, 128)
+    assert np.array_equal(x.astype(np.float64) / s, np.resize(np.concatenate([mids, -mids]), T * H * 128).reshape(T, H, 128))
+    rows = np.arange(T, dtype=np.int32)
+    ws_k = torch.zeros((T, H, 128), dtype=torch.uint8, device="cuda")
+    ws_v = torch.zeros_like(ws_k)
+    xt = torch.from_numpy(x).cuda()
+    nk.fp8_rows_to_workspace(xt, xt, torch.from_numpy(rows).cuda(), s, s, ws_k, ws_v)
+    torch.cuda.synchronize()
+    ref = np.zeros((T, H, 128), np.uint8)
+    oracle.fp8_quantize_rows(x, rows, s, ref)
+    assert np.array_equal(ws_k.cpu().numpy(), ref) and np.array_equal(ws_v.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("prefixes,chunks,H,G,qdt", [
     ([0], [100], 2, 4, torch.bfloat16),                 # prefill: the chunk only
     ([0, 37, 300], [1, 50, 33], 2, 8, torch.bfloat16),  # ragged extends, single-token chunk

@@ -92,6 +92,22 @@ def _tie_rows():
     r[48:64] = 3e38
     r[64:80] = np.float32(1.5e-45)  # float32 subnormals
     rows.append((r, 1.0))
+    # a 12-bit global scale that is not a power of two (1/(6g) is inexact):
+    # E4M3 ties of amax/(6g), then E2M1 ties of x/(bs*g) at known scale bytes
+    # (every product below has at most 19 significant bits: exact in float32)
+    g = 1.234375
+    r = np.zeros(128, np.float32)
+    for b, k in enumerate([0, 2, 9, 33, 64, 90, 111, 125]):
+        amax = np.float32((e4[k] + e4[k + 1]) / 2 * 6 * g)
+        r[16 * b] = amax
+        r[16 * b + 1:16 * b + 16] = np.linspace(-amax, amax, 15)
+    rows.append((r, g))
+    r = np.zeros(128, np.float32)
+    for b, k in enumerate([8, 16, 40, 56, 72, 88, 104, 118]):
+        bs0 = e4[k]  # amax = 6 * bs0 * g gives scale byte k exactly
+        r[16 * b:16 * b + 16] = np.array([6 * bs0 * g] + [m * bs0 * g for m in mids] + [-m * bs0 * g for m in mids]
+                                         + [0.0], np.float64)[:16].astype(np.float32)
+    rows.append((r, g))
     return rows
 
 
