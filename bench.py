@@ -112,7 +112,7 @@ def append_b2b(stream, steps, chunks, targets, append, per_head, **kw):
     re-appending the first fill chunk of a layer (the same tokens into the same
     slots, so the cache keeps its bytes), alternating over the layers so that
     no call finds its inputs in the caches.  Returns (us per call, GB/s of
-    algorithmic bytes)."""
+    algorithmic bytes, algorithmic bytes per call)."""
     def launch(i):
         j = i % len(chunks)
         k, v, sl = chunks[j]
@@ -121,12 +121,19 @@ def append_b2b(stream, steps, chunks, targets, append, per_head, **kw):
     k0 = chunks[0][0]
     n, H = k0.shape[0], k0.shape[1]
     b = n * H * (2 * 128 * k0.element_size() + per_head) + 4 * n
-    return s * 1e6, b / s / 1e9
+    return s * 1e6, b / s / 1e9, b
 
 
-def read_traffic(kernel_files, workload: str):
-    """HBM traffic per decode call from a committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source; else None."""
+# The bulk quantize-append kernel's source.
+APPEND_SOURCES = [os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", n)
+                  for n in ("quant_append.hip", "nvfp4_kv_internal.h", "nvfp4_device.h", "nvfp4_quant_device.h")]
+
+
+def read_traffic(kernel_files, workload: str, key: str = "hbm_bytes_per_call",
+                 hash_key: str = "kernel_source_sha256_16"):
+    """HBM traffic per call (decode by default; `key` picks another kernel's
+    figure) from a committed rocprofv3 PMC summary, if it was taken on the
+    current kernel source; else None."""
     prof = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.txt")
     if not os.path.exists(prof):
         return None
@@ -136,10 +143,10 @@ def read_traffic(kernel_files, workload: str):
             if ":" in ln and not ln.startswith("#"):
                 k, v = ln.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != src_hash(kernel_files):
+    if vals.get(hash_key) != src_hash(kernel_files):
         return None
     try:
-        return float(vals["hbm_bytes_per_call"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -326,7 +333,7 @@ def bench_mixed(args, wl, dev):
     # bulk append back to back over the first fill chunk of two layers
     from nvfp4_quantized_paged_kv_amd.workloads import first_chunk
     b2b_layers = list(range(min(L, 2)))
-    bulk_us, bulk_gbs = append_b2b(stream, args.steps,
+    bulk_us, bulk_gbs, _ = append_b2b(stream, args.steps,
                                    [first_chunk(wl, list(wl.lens), l, steps[l].filled.block_table, dev)
                                     for l in b2b_layers],
                                    [steps[l].filled.layer for l in b2b_layers], nk.quantize_append, 144)
@@ -595,8 +602,8 @@ def main():
         if fill not in chunks:
             chunks[fill] = [first_chunk(wl, [fill] * B, l, bts[l], dev) for l in b2b_layers]
         return chunks[fill]
-    app_us, app_gbs = append_b2b(stream, args.steps, chunk_set(ctx - 1), [layers[l] for l in b2b_layers],
-                                 nk.quantize_append, 144)
+    app_us, app_gbs, app_b = append_b2b(stream, args.steps, chunk_set(ctx - 1), [layers[l] for l in b2b_layers],
+                                        nk.quantize_append, 144)
     print("[bench] bulk append timed back to back", file=sys.stderr, flush=True)
 
     # ---- MXFP4, the format the pages compare NVFP4 against (E8M0 scale per 32
@@ -616,7 +623,7 @@ def main():
     for i in range(args.warmup):
         mx_call(i)
     mx_s = back_to_back(stream, args.steps, mx_call)
-    mx_app_us, mx_app_gbs = append_b2b(stream, args.steps, chunk_set(ctx), [mx_layers[l] for l in b2b_layers],
+    mx_app_us, mx_app_gbs, _ = append_b2b(stream, args.steps, chunk_set(ctx), [mx_layers[l] for l in b2b_layers],
                                        nk.mx_quantize_append, 136)
     bytes_mx = B * ctx * H * 136 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
     mxfp4 = {"decode_us": round(mx_s * 1e6, 3), "decode_gbs": round(bytes_mx / mx_s / 1e9, 2),
@@ -645,7 +652,7 @@ def main():
         for i in range(args.warmup):
             rot_call(i)
         rot_s = back_to_back(stream, args.steps, rot_call)
-        rot_app_us, rot_app_gbs = append_b2b(stream, args.steps, chunk_set(ctx), [rot_layers[l] for l in b2b_layers],
+        rot_app_us, rot_app_gbs, _ = append_b2b(stream, args.steps, chunk_set(ctx), [rot_layers[l] for l in b2b_layers],
                                              nk.mx_quantize_append if mx else nk.quantize_append, 136 if mx else 144,
                                              hadamard=True)
         b_rot = bytes_mx if mx else bytes_decode
@@ -689,6 +696,12 @@ def main():
         "quantize_append_bulk_gbs": round(app_gbs, 2),
         "quantize_append_bulk_us": round(app_us, 2),
         "quantize_append_bulk_chunk_tokens": int(chunk_set(ctx - 1)[0][0].shape[0]),
+        "append_roofline": {"bound": "hbm", "achieved": round(app_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(app_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": read_traffic(APPEND_SOURCES, wl.name, "append_hbm_bytes_per_call",
+                                                    "append_source_sha256_16"),
+                            "kernel": "nvfp4_kv_quantize_append (bulk, one chunk per call)",
+                            "algorithmic_bytes_per_call": int(app_b)},
         "quantize_append_bulk_gbs_single_call": round(app_total_b / app_total_s / 1e9, 2),
         "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),
         "fp8_workspace_gbs": round(ws_gbs, 2),
