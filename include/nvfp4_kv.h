@@ -176,7 +176,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
  * their slots come from block_table.  The result is the same as
  * nvfp4_kv_quantize_append of those tokens followed by
  * nvfp4_paged_decode_attn_multi: the same cache bytes and the same output.
- * Schedule: when a unit holds at most 4096 pages (max_seq_len <= 65,536) the
+ * Schedule: when a unit holds at most 16384 pages (max_seq_len <= 262,144) the
  * step is one launch -- the workgroup that reads a page holding a new token
  * quantizes and stores that token itself before it loads the page, so no
  * workgroup waits on another.  Longer units take two launches on `stream`

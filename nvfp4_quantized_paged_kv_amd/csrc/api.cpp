@@ -136,10 +136,12 @@ namespace {
 // A decode step whose units hold more pages than this appends its new tokens
 // with the append kernel and then decodes (two launches); shorter ones append
 // inside the decode kernel.  Measured on MI355X: 8K-token contexts (512 pages)
-// run the step 2.5% faster fused; 128K (8192 pages) run it equally fast either
-// way; a 2M-token context (125,000 pages) runs the fused kernel about 20 us
-// (4%) longer than append + decode.
-constexpr int64_t kStepFusedMaxPages = 4096;
+// run the step 1.4-2.5% faster fused; at 128K (8192 pages) the fused step runs
+// as fast as two launches with a precomputed slot array and about 2% faster
+// than two launches that take the slots from the block table on the device; a
+// 2M-token context (125,000 pages) runs the fused kernel about 20 us (4%)
+// longer than append + decode.
+constexpr int64_t kStepFusedMaxPages = 16384;
 
 nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new, const void* q,
                            nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads,

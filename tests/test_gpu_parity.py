@@ -356,8 +356,8 @@ def test_decode_step_equals_append_then_decode(lens, H, G, T, qdt):
 
 @pytest.mark.parametrize("lens,H,G,T", [([33, 16, 17, 1000], 2, 8, 1), ([17, 40, 2], 2, 8, 2), ([1, 3, 5], 1, 2, 4)])
 def test_decode_step_two_launch_schedule(lens, H, G, T):
-    """max_seq_len above 65,536 tokens: the step appends with the append kernel, then decodes."""
-    _step_case(lens, H, G, T, torch.bfloat16, 70000)
+    """max_seq_len above 262,144 tokens: the step appends with the append kernel, then decodes."""
+    _step_case(lens, H, G, T, torch.bfloat16, 270000)
 
 
 def _step_case(lens, H, G, T, qdt, msl):
