@@ -22,10 +22,11 @@
 //   online softmax in fp32 (exp2 domain), with a lazy max: the running max is
 //         only raised when a page exceeds it by more than 2^8, so P <= 2^8;
 //         row maxima across the 4 token groups use v_permlane16/32_swap
-//   PV    O[16 q x 128] += P[16 x 16 tok] . V_page : 8 x mfma_f32_16x16x16_f16
-//         (the QK^T output lane layout is exactly the PV A-operand layout; the V
-//          tile layout gives lane l the 4 tokens 4*(l/16)..+3 of dims
-//          8*(l%16)..+7 in 16 contiguous bytes; nibbles of two tokens are
+//   PV    O[16 q x 128] += P[16 x 16 tok] . V_page : 8 x mfma_f32_16x16x32_f16
+//         (the QK^T output lane layout is exactly the PV A-operand layout; the
+//          32-wide contraction carries P as an f16 hi + lo pair against the same
+//          V twice; the V tile layout gives lane l the 4 tokens 4*(l/16)..+3 of
+//          dims 8*(l%16)..+7 in 16 contiguous bytes; nibbles of two tokens are
 //          re-paired with bit-field inserts so that one byte = one MFMA k-pair)
 // Dequantization: v_cvt_scalef32_pk_f16_fp4 widens two E2M1 codes (times 2^8),
 // and one v_pk_mul_f16 by (E4M3 scale * 2^-8, taken from the scale byte's bit
@@ -628,7 +629,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   #undef NVFP4_MX_PV_STEP
         return;
       }
-      const half4_t pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+      // P as an f16 hi + lo pair (about 22 bits): with P alone in f16 (11
+      // bits) a row whose output nearly cancels -- outliers of opposite sign
+      // in a few tokens -- could miss 1e-3 relative to the row's largest value
+      const half4_t ph = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+      const half8_t pa = {ph[0], ph[1], ph[2], ph[3], (_Float16)(pr[0] - (float)ph[0]), (_Float16)(pr[1] - (float)ph[1]),
+                          (_Float16)(pr[2] - (float)ph[2]), (_Float16)(pr[3] - (float)ph[3])};
 
       // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3)
       uint32_t vsw = cur.vsw;
@@ -647,10 +653,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const half2_t a1 = fp4x2_to_f16_x256<C>(E23) * vs23;                                   \
       const half2_t b0 = fp4x2_to_f16_x256<C>(O01) * vs01;                                   \
       const half2_t b1 = fp4x2_to_f16_x256<C>(O23) * vs23;                                   \
-      const half4_t ve = {a0[0], a0[1], a1[0], a1[1]};                                       \
-      const half4_t vo = {b0[0], b0[1], b1[0], b1[1]};                                       \
-      acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, ve, acc[2 * C], 0, 0, 0);       \
-      acc[2 * C + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vo, acc[2 * C + 1], 0, 0, 0); \
+      const half8_t ve = {a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};            \
+      const half8_t vo = {b0[0], b0[1], b1[0], b1[1], b0[0], b0[1], b1[0], b1[1]};            \
+      acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, ve, acc[2 * C], 0, 0, 0);      \
+      acc[2 * C + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vo, acc[2 * C + 1], 0, 0, 0); \
     }
       NVFP4_PV_STEP(0)
       NVFP4_PV_STEP(1)

@@ -188,6 +188,21 @@ def test_decode_peaked_softmax(q_scale):
     assert err.max() <= ATTN_TOL, err.max()
 
 
+def test_decode_max_batch():
+    """The largest batch one launch takes (4096 sequences: every slot of the
+    prologue's prefix scan), ragged lengths 0..40 including empty sequences."""
+    _say("case: decode max batch 4096")
+    rng = np.random.default_rng(97)
+    lens = [int(x) for x in rng.integers(0, 41, 4096)]
+    lens[0], lens[-1], lens[2048] = 0, 40, 1
+    c = build_cache(lens, 1, torch.bfloat16, "sparse6", 0.005, False, seed=97)
+    got, ref = decode_both(c, 2, torch.bfloat16, seed=13)
+    err = row_rel_err(got, ref)
+    _say(f"  max row rel err {err.max():.2e}")
+    assert err.max() <= ATTN_TOL, (err.max(), int(np.argmax(err)))
+    assert (got.reshape(4096, 2, 128)[np.array(lens) == 0] == 0).all()
+
+
 def test_decode_huge_logits_stay_finite():
     """Queries scaled by 1e13 (logits far above 2^32): the softmax weights come
     from the rounded logit, so none overflows; the output stays finite and
