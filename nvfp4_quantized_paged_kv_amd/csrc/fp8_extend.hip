@@ -21,7 +21,8 @@
 //                     row block (lane: key 16kb + l%16, dims 32*(l/16)..+31;
 //                     Q in the same permuted dim order, so no shuffles)
 //   online softmax in fp32 (exp2 domain, lazy max as in the decode kernel)
-//   O[token][dim]  += P . V : 8 dim blocks x mfma_f32_16x16x32_f16 (the
+//   O[token][dim]  += P . V : 8 dim blocks x 2 mfma_f32_16x16x32_f16 (P as
+//                     an f16 hi + lo pair, one MFMA each; the
 //                     weights stay where the S^T layout put them: the
 //                     contraction index is mapped onto the 32 keys to match)
 // The FP32 per-tensor workspace scales go on the logits (K) and on the output
@@ -133,8 +134,12 @@ __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
+// Three waves per SIMD for bf16 queries (at most 168 VGPRs; the P hi + lo
+// pair would otherwise take the kernel just past that); the float32-query
+// kernel holds a second Q pair and runs two waves per SIMD either way.
 template <bool QF32>
-__global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 3))) void extend_kernel(
+    ExtendParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kKTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kVTileBytes];
 
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
     }
 
     // ---- online softmax per row block (exp2 domain, lazy max)
-    half4_t pa[2][2];
+    half4_t pa[2][2], pl[2][2];  // P as an f16 hi + lo pair
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float pm =
@@ -349,6 +354,8 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
           pr[i] = __builtin_amdgcn_exp2f(S[kb][rb][i] * tscale[rb] - m_run[rb]);
         l_run[rb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         pa[rb][kb] = half4_t{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+        pl[rb][kb] = half4_t{(_Float16)(pr[0] - (float)pa[rb][kb][0]), (_Float16)(pr[1] - (float)pa[rb][kb][1]),
+                             (_Float16)(pr[2] - (float)pa[rb][kb][2]), (_Float16)(pr[3] - (float)pa[rb][kb][3])};
       }
     }
 
@@ -356,16 +363,23 @@ __global__ __launch_bounds__(512) void extend_kernel(ExtendParams p) {
     // k = 8*eq + j stands for key 4*eq + j (j < 4) of key block 0 and key
     // 16 + 4*eq + j - 4 of key block 1, which is how the S^T layout left the
     // weights in this lane; V is read from the transposed tile in the same order.
-    half8_t pw[2];
+    // P enters as an f16 hi + lo pair (about 22 bits), the lo part first: with P
+    // in f16 alone (11 bits) a row whose output nearly cancels can miss 1e-3 of
+    // its largest value.
+    half8_t pw[2], pwl[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
       pw[rb] = __builtin_shufflevector(pa[rb][0], pa[rb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      pwl[rb] = __builtin_shufflevector(pl[rb][0], pl[rb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const uint8_t* vp = &s_v[buf][(16 * db + er) * kVStride + 8 * eq];
       const uint2 v0 = *reinterpret_cast<const uint2*>(vp);       // f16 keys 4*eq .. +3
       const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 32);  // f16 keys 16 + 4*eq .. +3
       const half8_t b = __builtin_bit_cast(half8_t, uint4{v0.x, v0.y, v1.x, v1.y});
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pwl[rb], b, acc[rb][db], 0, 0, 0);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[rb], b, acc[rb][db], 0, 0, 0);
     }

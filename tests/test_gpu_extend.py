@@ -95,11 +95,12 @@ def _case(rng, prefixes, chunks, H, gap=5):
 
 
 def _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, qdt, seed, q_scale=1.0, sm=0.088, rows=None,
-                 max_chunk=None, extra_q_rows=0):
+                 max_chunk=None, extra_q_rows=0, q=None):
     import nvfp4_quantized_paged_kv_amd as nk
 
     Tq = int(qo[-1]) + extra_q_rows
-    q = synth.queries(Tq, Hq, qdt, "cpu", seed, 7)
+    if q is None:
+        q = synth.queries(Tq, Hq, qdt, "cpu", seed, 7)
     if q_scale != 1.0:
         q = (q.float() * q_scale).to(qdt)
     pl = np.asarray(prefixes, np.int32)
@@ -179,6 +180,39 @@ def test_extend_huge_logits_stay_finite():
     assert np.isfinite(got[rows]).all()
     err = row_rel_err(got[rows], ref)
     _say(f"  finite; max row rel err vs oracle {err.max():.2e}")
+    assert err.max() <= ATTN_TOL, err.max()
+
+
+def test_extend_cancelling_rows():
+    """Rows whose output nearly cancels: in each sequence two prefix keys take
+    almost all the weight (logits 20 and 19.990; every other key sits 40 lower)
+    and have opposite V rows (+1 and -1 in every dim), so every output value is
+    about 0.5% of a V value.  Rounding P to f16 alone (2^-12 relative) would
+    leave about 2.5% of the row's largest value; the bound is 1e-3.  All
+    products and sums of the logits are exact (powers of two)."""
+    _say("case: extend cancelling rows")
+    H, Hq = 2, 16
+    prefixes, chunks = [40, 7], [37, 20]
+    offs = np.array([0, prefixes[0] + chunks[0] + 3], np.int32)
+    cap = int(offs[-1]) + prefixes[1] + chunks[1]
+    rng = np.random.default_rng(71)
+    ws_k = np.full((cap, H, 128), 0xB8, np.uint8)  # K = -1 in every dim
+    mag = rng.integers(0, 0x7F, (cap, H, 128)).astype(np.uint8)  # any finite E4M3 V (0x7F is NaN)
+    ws_v = mag | (rng.integers(0, 2, (cap, H, 128)).astype(np.uint8) << 7)
+    for o in offs:
+        ws_k[o] = 0x38  # key a: K = 1
+        ws_k[o + 1] = 0x38
+        ws_k[o + 1, :, 127] = 0x37  # key b: K = 1 except 0.9375 in one dim
+        ws_v[o] = 0x38  # V = +1
+        ws_v[o + 1] = 0xB8  # V = -1
+    qo = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = torch.ones((int(qo[-1]), Hq, 128), dtype=torch.bfloat16)
+    # logit of key a = 1.25 * 128 * 0.125 = 20
+    got, rows, ref = _extend_both(ws_k, ws_v, 0.125, 1.0 / 64, offs, qo, prefixes, Hq, torch.bfloat16, seed=0,
+                                  sm=1.25, q=q)
+    assert np.abs(ref).max(axis=1).max() < 0.01 / 64  # every row cancels to below 1% of a V value
+    err = row_rel_err(got[rows], ref)
+    _say(f"  max row rel err vs oracle {err.max():.2e}")
     assert err.max() <= ATTN_TOL, err.max()
 
 
