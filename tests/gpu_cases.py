@@ -49,8 +49,9 @@ class Cache:
     g_v: float
 
 
-def build_cache(lens, H, dtype, dist, outlier_frac, g_one, seed, extra_pages=3, device="cuda"):
-    """Quantize-append every sequence's tokens with both implementations."""
+def build_cache(lens, H, dtype, dist, outlier_frac, g_one, seed, extra_pages=3, device="cuda", kv=None):
+    """Quantize-append every sequence's tokens with both implementations
+    (kv: optional per-sequence (k, v) tensors [n, H, 128] in place of synthetic ones)."""
     import nvfp4_quantized_paged_kv_amd as nk
 
     bt, pool = synth.page_tables(lens, sum((n + 15) // 16 for n in lens) + extra_pages, seed=seed)
@@ -58,8 +59,12 @@ def build_cache(lens, H, dtype, dist, outlier_frac, g_one, seed, extra_pages=3, 
     for b, n in enumerate(lens):
         if n == 0:
             continue
-        ks.append(synth.kv_values(n, H, dist, outlier_frac, 0, dtype, "cpu", seed, b))
-        vs.append(synth.kv_values(n, H, dist, outlier_frac, 1, dtype, "cpu", seed, b))
+        if kv is not None:
+            ks.append(kv[b][0].to(dtype))
+            vs.append(kv[b][1].to(dtype))
+        else:
+            ks.append(synth.kv_values(n, H, dist, outlier_frac, 0, dtype, "cpu", seed, b))
+            vs.append(synth.kv_values(n, H, dist, outlier_frac, 1, dtype, "cpu", seed, b))
         slots.append(synth.slots_for(bt[b], 0, n))
     k = torch.cat(ks) if ks else torch.zeros((0, H, 128), dtype=dtype)
     v = torch.cat(vs) if vs else torch.zeros((0, H, 128), dtype=dtype)
@@ -77,11 +82,12 @@ def build_cache(lens, H, dtype, dist, outlier_frac, g_one, seed, extra_pages=3, 
     return Cache(layer, planes, bt, list(lens), g_k, g_v)
 
 
-def decode_both(cache: Cache, Hq, q_dtype, seed, rows=None, max_seq_len=None, q_scale=1.0, device="cuda"):
+def decode_both(cache: Cache, Hq, q_dtype, seed, rows=None, max_seq_len=None, q_scale=1.0, device="cuda", q=None):
     import nvfp4_quantized_paged_kv_amd as nk
 
     B = len(cache.lens)
-    q = synth.queries(B, Hq, q_dtype, "cpu", seed, 1) * q_scale
+    if q is None:
+        q = synth.queries(B, Hq, q_dtype, "cpu", seed, 1) * q_scale
     q = q.to(q_dtype)
     msl = max(max(cache.lens), 1) if max_seq_len is None else max_seq_len
     bt = cache.bt

@@ -216,12 +216,50 @@ def test_decode_huge_logits_stay_finite():
     assert err.max() <= ATTN_TOL, err.max()
 
 
+def _cancelling_kv(lens, H, seed):
+    """Per sequence: K = -1 and random V, except tokens 0 and 1: K = 1 (token
+    1: 0.75 in dim 127), V = +1 and -1.  With g = 1 every K block has the scale
+    0.171875, so K dequantizes to +-1.03125 and dim 127 of token 1 to 0.6875."""
+    gen = torch.Generator().manual_seed(seed)
+    kv = []
+    for n in lens:
+        k = -torch.ones((n, H, 128))
+        v = torch.randn((n, H, 128), generator=gen)
+        k[0] = 1.0
+        k[1] = 1.0
+        k[1, :, 127] = 0.75
+        v[0] = 1.0
+        v[1] = -1.0
+        kv.append((k, v))
+    return kv
+
+
+def test_decode_cancelling_rows():
+    """Rows whose output nearly cancels: with Q = 1.75 (0.25 in dim 127) the
+    logits of tokens 0 and 1 are about 20.4 and 0.0076 apart, every other token
+    sits about 40.8 lower, and V is +1 and -1 there, so each output is about
+    0.4% of a V value.  P in f16 alone (2^-12 relative) could leave up to 3% of
+    the row's largest value; the f16 hi + lo pair keeps it within 1e-3.  All
+    products and sums of the logits are exact in the MFMA."""
+    _say("case: decode cancelling rows")
+    lens, H, Hq = [100, 37, 300], 2, 16
+    c = build_cache(lens, H, torch.bfloat16, None, 0.0, True, seed=89, kv=_cancelling_kv(lens, H, 89))
+    q = torch.full((len(lens), Hq, 128), 1.75)
+    q[:, :, 127] = 0.25
+    got, ref = decode_both(c, Hq, torch.bfloat16, seed=0, q=q)
+    assert np.abs(ref).max(axis=1).max() < 0.01  # every row cancels to below 1% of a V value
+    err = row_rel_err(got, ref)
+    _say(f"  max row rel err vs oracle {err.max():.2e}")
+    assert err.max() <= ATTN_TOL, err.max()
+
+
 def test_decode_split_count_invariance():
     """A larger max_seq_len changes the split geometry; both results stay within the parity bound.
 
-    The softmax weights enter the PV product as f16 relative to a running
-    maximum that depends on how tokens are grouped into splits, so two split
-    geometries differ at the f16 rounding level (~1e-4), not bit for bit."""
+    The softmax weights are taken relative to a running maximum that depends
+    on how tokens are grouped into splits, and enter the PV product as an f16
+    hi + lo pair, so two split geometries differ at the level of that
+    rounding, not bit for bit."""
     _say("case: decode split invariance")
     c = build_cache([1500, 900], 2, torch.bfloat16, "sparse6", 0.005, False, seed=21)
     a, ref = decode_both(c, 16, torch.bfloat16, seed=3)
