@@ -89,8 +89,8 @@ def lib():
     L.nvfp4o_mx_decode_attention.restype = None
     L.nvfp4o_hadamard_rows.argtypes = [_f64p, _i64, _dbl, _f64p]
     L.nvfp4o_hadamard_rows.restype = None
-    L.nvfp4o_page_mode_dequant.argtypes = [_f64p, _i64, _i64, _f64p]
-    L.nvfp4o_page_mode_dequant.restype = None
+    L.nvfp4o_unrounded_block_dequant.argtypes = [_f64p, _i64, _i64, _f64p]
+    L.nvfp4o_unrounded_block_dequant.restype = None
     L.nvfp4o_bytes_per_token_head.argtypes = []
     L.nvfp4o_bytes_per_token_head.restype = _i64
     L.nvfp4o_max_threads.argtypes = []
@@ -346,11 +346,13 @@ def rotate_q(q) -> np.ndarray:
     return hadamard_rows(q, Q_ROT_SCALE)
 
 
-# ------------------------------------------------------ the page experiment
-def page_mode_dequant(x, block: int) -> np.ndarray:
+# ------------------------------------------ the page's two-level comparison
+def unrounded_block_dequant(x, block: int) -> np.ndarray:
+    """Two-level scaling with an unrounded per-block scale amax/6 and no tensor
+    scale (block = x.size: one global scale): the values read back, float64."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     out = np.zeros_like(x)
-    lib().nvfp4o_page_mode_dequant(x, x.size, int(block), out)
+    lib().nvfp4o_unrounded_block_dequant(x, x.size, int(block), out)
     return out
 
 

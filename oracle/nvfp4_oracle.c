@@ -18,8 +18,8 @@
  * Readings where the pages leave a step open (each also listed in the design
  * notes):
  *   R1 ties go to the even code (E2M1) / even byte (E4M3); the page's own
- *      stdlib snap takes the first list entry instead -- kept only in
- *      nvfp4o_page_mode_dequant() to reproduce the page's printed RMSE.
+ *      experiment breaks ties toward the more negative list entry, which
+ *      makes no difference on its Gaussian data (ties have measure zero).
  *   R2 block scale = E4M3 value nearest to amax/(6*g) (the page's script keeps
  *      it unrounded and has no g); saturates at 448, values below the E4M3
  *      grid's half-step round to 0.
@@ -550,33 +550,24 @@ void nvfp4o_hadamard_rows(const double* x, int64_t n_rows, double scale, double*
   }
 }
 
-/* --------------------------------------------------- the page's experiment
- * [MW] §2 stdlib experiment, reproduced operation for operation: per block of
- * `block` values, scale = amax/6 (1.0 when amax <= 1e-12, no rounding, no
- * global scale) and each value becomes snap(v/scale)*scale, where snap picks
- * the first entry of the 16-value list (ordered -6 .. -0.0, 0.0 .. 6) with the
- * smallest |entry - x|.  block = n gives the global-only comparator. */
-void nvfp4o_page_mode_dequant(const double* x, int64_t n, int64_t block, double* out) {
-  static const double grid[16] = {-6.0, -4.0, -3.0, -2.0, -1.5, -1.0, -0.5, -0.0,
-                                  0.0,  0.5,  1.0,  1.5,  2.0,  3.0,  4.0,  6.0};
-  for (int64_t s = 0; s < n; s += block) {
-    int64_t e = s + block < n ? s + block : n;
+/* ------------------------------------------- unrounded two-level scaling
+ * [MW] §2 compares two-level scaling against a single global scale on
+ * Gaussian data with a few large outliers; its comparison keeps the block
+ * scale unrounded and has no tensor scale.  This is that rule, written with
+ * the oracle's own encoder: per block of `block` values, s = amax/6 (a block
+ * of zeros stays zero) and each value v becomes sign(v) * E2M1(c) * s with
+ * c = nvfp4o_e2m1_encode(|v|/s) (nearest magnitude, ties to the even code --
+ * ties have measure zero on such data).  block = n is the global-only
+ * comparator. */
+void nvfp4o_unrounded_block_dequant(const double* x, int64_t n, int64_t block, double* out) {
+  for (int64_t s0 = 0; s0 < n; s0 += block) {
+    const int64_t s1 = s0 + block < n ? s0 + block : n;
     double amax = 0.0;
-    for (int64_t i = s; i < e; ++i)
-      if (fabs(x[i]) > amax) amax = fabs(x[i]);
-    double scale = amax > 1e-12 ? amax / 6.0 : 1.0;
-    for (int64_t i = s; i < e; ++i) {
-      double y = x[i] / scale;
-      int best = 0;
-      double bestd = fabs(grid[0] - y);
-      for (int k = 1; k < 16; ++k) {
-        double d = fabs(grid[k] - y);
-        if (d < bestd) {
-          best = k;
-          bestd = d;
-        }
-      }
-      out[i] = grid[best] * scale;
+    for (int64_t i = s0; i < s1; ++i) amax = fmax(amax, fabs(x[i]));
+    const double s = amax / 6.0;
+    for (int64_t i = s0; i < s1; ++i) {
+      const double mag = s > 0.0 ? nvfp4o_e2m1_value(nvfp4o_e2m1_encode(fabs(x[i]) / s)) * s : 0.0;
+      out[i] = copysign(mag, x[i]);
     }
   }
 }

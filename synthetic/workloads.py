@@ -9,8 +9,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import KVCacheLayer, MxKVCacheLayer, mx_quantize_append, quantize_append
-from . import synth
+from nvfp4_quantized_paged_kv_amd import KVCacheLayer, MxKVCacheLayer, mx_quantize_append, quantize_append
+from synthetic import synth
 
 
 @dataclass

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 
 ATTN_TOL = 1e-3  # row-normalised max relative error of the fp32 decode output
 

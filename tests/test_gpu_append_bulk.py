@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 from tests.gpu_cases import host_f32, planes_equal
 
 pytestmark = pytest.mark.gpu

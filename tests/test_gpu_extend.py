@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 from tests.gpu_cases import ATTN_TOL, build_cache, host_f32, row_rel_err
 
 pytestmark = pytest.mark.gpu

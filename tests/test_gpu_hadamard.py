@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 from tests.gpu_cases import ATTN_TOL, host_f32, row_rel_err
 
 pytestmark = pytest.mark.gpu

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 from tests.gpu_cases import ATTN_TOL, host_f32, row_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -188,7 +188,7 @@ def test_mx_decode_long_split_and_larger_bound():
 def test_mx_full_size_sampled():
     """The bench's MXFP4 decode: the 70B-class batch filled as the bench fills it."""
     import nvfp4_quantized_paged_kv_amd as nk
-    from nvfp4_quantized_paged_kv_amd.workloads import build_layer
+    from synthetic.workloads import build_layer
 
     wl = synth.WORKLOADS["gqa70b_b32_8k"]
     lens = [wl.ctx] * wl.batch

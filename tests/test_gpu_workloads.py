@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 from tests.gpu_cases import ATTN_TOL, row_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +57,7 @@ def _check_units(wl, lens, fl, samples, raw, q, out, g_k, g_v):
 
 def _run(name, samples, layer_idx=0):
     import nvfp4_quantized_paged_kv_amd as nk
-    from nvfp4_quantized_paged_kv_amd.workloads import build_layer
+    from synthetic.workloads import build_layer
 
     wl = synth.WORKLOADS[name]
     lens = [wl.ctx] * wl.batch
@@ -97,7 +97,7 @@ def test_agentic_b1_2m_full_size():
 def test_mixed_64_full_size():
     """Ragged 64-sequence step: append 16/2048 tokens, FP8 workspace of 8 prefixes, decode of 56."""
     import nvfp4_quantized_paged_kv_amd as nk
-    from nvfp4_quantized_paged_kv_amd.workloads import build_mixed_step
+    from synthetic.workloads import build_mixed_step
 
     wl = synth.WORKLOADS["mixed_64"]
     lens = list(wl.lens)

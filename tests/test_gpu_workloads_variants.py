@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 from tests.gpu_cases import ATTN_TOL, row_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +31,7 @@ def _say(*a):
 
 def _fill(fill_len, pool_len, mx=False, hadamard=False):
     """Fill layer 0 of the workload; return (workload, filled layer, raw rows of the sampled units)."""
-    from nvfp4_quantized_paged_kv_amd.workloads import build_layer
+    from synthetic.workloads import build_layer
 
     wl = synth.WORKLOADS[WL]
     lens = [fill_len] * wl.batch

@@ -26,7 +26,7 @@ import scipy.linalg
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 
 
 def _matrix():

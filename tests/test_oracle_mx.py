@@ -26,7 +26,7 @@ import pytest
 import torch
 
 import oracle
-from nvfp4_quantized_paged_kv_amd import synth
+from synthetic import synth
 
 GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
 
@@ -189,6 +189,6 @@ def test_smaller_blocks_lose_less():
     # less error on its data); with the [MW] section-2 quantizer on Gaussian
     # values the 16-value block must at least be better
     x = np.random.default_rng(20261106).normal(0.0, 0.02, 1 << 16)
-    e16 = np.sqrt(np.mean((oracle.page_mode_dequant(x, 16) - x) ** 2))
-    e32 = np.sqrt(np.mean((oracle.page_mode_dequant(x, 32) - x) ** 2))
+    e16 = np.sqrt(np.mean((oracle.unrounded_block_dequant(x, 16) - x) ** 2))
+    e32 = np.sqrt(np.mean((oracle.unrounded_block_dequant(x, 32) - x) ** 2))
     assert e16 < e32

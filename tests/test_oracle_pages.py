@@ -1,16 +1,16 @@
 """Pins of the oracle against the numbers the memory-wall blog prints.
 
-* Section 2: the stdlib two-level-scaling experiment (seeded data, printed RMSE
-  of block+global versus global-only quantization) -- reproduced exactly by the
-  oracle's page-mode quantizer, and the oracle's own rule (E4M3-rounded block
-  scale, FP32 global scale, ties to even) must keep the large advantage.
+* Section 2: the two-level-scaling experiment (seeded Gaussian data with a few
+  outliers, printed RMSE of block+global versus global-only quantization) --
+  reproduced exactly by the oracle's unrounded two-level rule, and the oracle's
+  own rule (E4M3-rounded block scale, FP32 global scale, ties to even) must
+  keep the large advantage.
 * Section 1: the KV-cache accounting table, computed from the oracle's own
   cache layout size (bytes per token and head).
 """
 import math
 import os
 import random
-import statistics
 
 import numpy as np
 import pytest
@@ -30,24 +30,28 @@ def _kv(path):
 
 
 def _page_data(cfg):
-    """The page's data recipe, with Python's own random module and seed."""
-    random.seed(int(cfg["seed"][0]))
+    """The section-2 data, as the page describes it: one Mersenne-Twister stream
+    (Python's `random`) seeded with the page's seed gives `n` normal draws of
+    standard deviation `sigma`, then `outliers` uniform positions, each set to
+    `outlier_value` (a position drawn twice is set once)."""
+    rng = random.Random(int(cfg["seed"][0]))
     n, sigma = int(cfg["n"][0]), float(cfg["sigma"][0])
-    values = [random.gauss(0, sigma) for _ in range(n)]
+    x = np.array([rng.gauss(0.0, sigma) for _ in range(n)], dtype=np.float64)
     for _ in range(int(cfg["outliers"][0])):
-        values[random.randrange(len(values))] = float(cfg["outlier_value"][0])
-    return values
+        x[rng.randrange(n)] = float(cfg["outlier_value"][0])
+    return x
 
 
 def _rmse(a, b):
-    return statistics.fmean((x - y) ** 2 for x, y in zip(a, b)) ** 0.5
+    d = np.asarray(a, np.float64) - np.asarray(b, np.float64)
+    return float(np.sqrt(np.mean(d * d)))
 
 
 def test_page_rmse_reproduced_exactly(golden_dir):
     cfg = _kv(os.path.join(golden_dir, "mw_rmse.txt"))
     values = _page_data(cfg)
-    blk = oracle.page_mode_dequant(values, int(cfg["block"][0]))
-    glb = oracle.page_mode_dequant(values, len(values))
+    blk = oracle.unrounded_block_dequant(values, int(cfg["block"][0]))
+    glb = oracle.unrounded_block_dequant(values, len(values))
     assert f"{_rmse(values, blk):.6f}" == cfg["rmse_block_global"][0]
     assert f"{_rmse(values, glb):.6f}" == cfg["rmse_global_only"][0]
 
@@ -64,7 +68,7 @@ def test_two_level_rule_beats_global_only(golden_dir, gmode):
     deq = oracle.dequantize_rows(codes, scales, g).reshape(-1)
     xd = x.astype(np.float64)
     ours = _rmse(xd, deq)
-    glb = _rmse(xd, oracle.page_mode_dequant(xd, xd.size))
+    glb = _rmse(xd, oracle.unrounded_block_dequant(xd, xd.size))
     assert ours * 4.0 < glb, (ours, glb)
     # and it is within a few percent of the page's own unrounded-scale block result
     assert ours < 1.05 * float(cfg["rmse_block_global"][0])
