@@ -1,24 +1,28 @@
 """Benchmark of the NVFP4 paged-KV hot path on one MI355X.
 
-Default workload: 70B-class GQA decode, one layer per step -- batch 32, 64 query
-heads / 8 KV heads, head_dim 128, 8192-token contexts, 16-token pages, bf16
-K/V ~ N(0, 0.02) with 2 of 128 K channels scaled x50, FP32 global scales
-amax/(6*448).  Four layer caches are filled (bulk quantize-append, timed) and
-the timed step rotates over them so consecutive steps never re-read a cache
-that could sit in the 256 MB Infinity Cache.  One step = append the batch's new
-token (one per sequence) + decode attention over the 8192-token caches, as one
+Default workload: agentic single-session decode -- batch 1, 96 query heads /
+8 KV heads, head_dim 128, a 2,000,000-token context resident as NVFP4 pages in
+random page order, bf16 K/V ~ N(0, 0.02) with 0.2% of entries set to +-6.0,
+FP32 global scales amax/(6*448).  Eight layer caches (2.3 GB of pages each)
+are filled by bulk quantize-append and the timed step rotates over them, so a
+step never finds its layer in the 256 MB Infinity Cache.  One step = append
+the sequence's new token + decode attention over the whole context, as one
 call of the library's decode step (the same step as two explicit calls is
-reported beside it).
+reported beside it).  `--workload` selects the other shapes (70B-class batch
+32 at 8K, batch 8 at 128K, the mixed serving step, the tiny case).
 
-Printed: one JSON line.  `value` is decode-step effective HBM bandwidth
-(algorithmic bytes of append + decode per step / step wall time); the same line
-carries the bulk quantize-append GB/s (a fill chunk re-appended back to back,
-alternating over two layers; the single-call figure of the fill beside it),
-the FP8 workspace dequant GB/s, the
-roofline of the dominant kernel (decode attention, timed with HIP events on the
-launch stream), the MXFP4 comparison format's append and decode on the same
-tokens, both formats with Hadamard-rotated K, and the CPU oracle timed on a
-bounded sample.
+Timing.  `value` and `ms_per_step` come from the median of several windows of
+exactly --steps step calls, each window bracketed by torch.cuda.synchronize()
+on both sides and timed by the wall clock (min and max beside it).  Kernel
+rooflines use HIP events on the launch stream around calls queued back to
+back (median of several windows, each led by untimed calls so that the GPU is
+already busy with the same work when the first event is taken).
+
+Printed: one JSON line -- decode-step effective HBM GB/s (algorithmic bytes of
+append + decode per step / step time), the decode kernel's roofline, the bulk
+quantize-append GB/s and its roofline, the FP8 workspace dequant, multi-token
+decode, the MXFP4 comparison format and Hadamard-rotated K on the same tokens,
+and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -37,24 +41,26 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0  # dense f16 / bf16 MFMA
 METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s) + quantize-append GB/s"
-# GPU spin (torch.cuda._sleep, clock cycles, about 0.1 ms) queued ahead of a
-# per-kernel event pair: the host-side call (10-20 us) is hidden behind it.
-# Kept short: after a long near-idle spin the GPU runs the next kernels slower
-# while its clocks ramp back up.
-SLEEP_CYCLES = 1 << 18
-# Back-to-back windows: calls queued (untimed) ahead of each timed window, and windows per measurement
-LEAD_CALLS = 16
-WINDOWS = 3
+# Windows of the headline step timing (each exactly --steps calls between two synchronizations)
+STEP_WINDOWS = 7
+# Back-to-back kernel timing: untimed calls queued ahead of each timed window, and windows per figure
+LEAD_CALLS = 8
+B2B_WINDOWS = 5
+# Layer caches larger than this are already far beyond the 256 MB Infinity Cache in pairs:
+# the comparison formats (MXFP4, rotated K) rotate over two of them instead of every layer
+BIG_LAYER_BYTES = 1 << 30
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa70b_b32_8k",
-                    choices=["gqa70b_b32_8k", "long_b8_128k", "agentic_b1_2m", "mixed_64", "tiny"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="agentic_b1_2m",
+                    choices=["agentic_b1_2m", "gqa70b_b32_8k", "long_b8_128k", "mixed_64", "tiny"])
     ap.add_argument("--layers", type=int, default=0, help="override the number of rotated layer caches")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the step, the decode and the bulk append (no MXFP4 / rotated / workspace)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate", action="store_true",
@@ -72,22 +78,56 @@ def src_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
+_CSRC = os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc")
 # The decode kernel's source: the kernel file and the headers it includes.
-DECODE_SOURCES = [os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", n)
+DECODE_SOURCES = [os.path.join(_CSRC, n)
                   for n in ("decode_attn.hip", "nvfp4_kv_internal.h", "nvfp4_device.h", "nvfp4_quant_device.h")]
+# The bulk quantize-append kernel's source.
+APPEND_SOURCES = [os.path.join(_CSRC, n)
+                  for n in ("quant_append.hip", "nvfp4_kv_internal.h", "nvfp4_device.h", "nvfp4_quant_device.h")]
 
 
-def back_to_back(stream, n, launch):
+def spread(xs, scale=1.0, nd=3):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64) * scale
+    return {"n": int(a.size), "median": round(float(np.median(a)), nd), "min": round(float(a.min()), nd),
+            "max": round(float(a.max()), nd)}
+
+
+def sync_windows(launch, steps: int, windows: int):
+    """The headline timing: `windows` windows of exactly `steps` calls, each
+    bracketed by torch.cuda.synchronize() on both sides.  Returns the wall
+    seconds per call of every window and the HIP-event seconds per call (events
+    on the launch stream, recorded at the window's first and last call)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    wall, ev = [], []
+    for w in range(windows):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            launch(w * steps + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall.append((time.perf_counter() - t0) / steps)
+        ev.append(e0.elapsed_time(e1) / 1e3 / steps)
+    return wall, ev
+
+
+def back_to_back(stream, n, launch, windows=B2B_WINDOWS, spread_out=None):
     """Per-call GPU time of n calls queued back to back between one event pair
-    on `stream`: the median over WINDOWS windows.  Each window is led by
+    on `stream`: the median over `windows` windows.  Each window is led by
     LEAD_CALLS untimed calls, so the GPU is already busy with the same work
     (no idle gap, no clock ramp) when the first event is taken and the host
     queues the timed calls while earlier ones run.  Warns on stderr if the host
-    took longer to queue a window than the GPU took to run it."""
+    took longer to queue a window than the GPU took to run it.  spread_out, if
+    a list, receives every window's per-call seconds."""
     import numpy as np
     import torch
     per_call = []
-    for w in range(WINDOWS):
+    for w in range(windows):
         torch.cuda.synchronize()
         for i in range(LEAD_CALLS):
             launch(i)
@@ -104,6 +144,8 @@ def back_to_back(stream, n, launch):
             print(f"[bench] warning: queueing {n} calls took {host_s * 1e3:.2f} ms, longer than their "
                   f"{gpu_s * 1e3:.2f} ms on the GPU; the back-to-back time includes host gaps", file=sys.stderr)
         per_call.append(gpu_s / n)
+    if spread_out is not None:
+        spread_out.extend(per_call)
     return float(np.median(per_call))
 
 
@@ -124,26 +166,26 @@ def append_b2b(stream, steps, chunks, targets, append, per_head, **kw):
     return s * 1e6, b / s / 1e9, b
 
 
-# The bulk quantize-append kernel's source.
-APPEND_SOURCES = [os.path.join(ROOT, "nvfp4_quantized_paged_kv_amd", "csrc", n)
-                  for n in ("quant_append.hip", "nvfp4_kv_internal.h", "nvfp4_device.h", "nvfp4_quant_device.h")]
+def read_profile(workload: str):
+    """key: value lines of the committed rocprofv3 HBM-counter summary of a workload."""
+    prof = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.txt")
+    vals = {}
+    if os.path.exists(prof):
+        with open(prof) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith("#"):
+                    k, v = ln.split(":", 1)
+                    vals[k.strip()] = v.strip()
+    return vals
 
 
 def read_traffic(kernel_files, workload: str, key: str = "hbm_bytes_per_call",
                  hash_key: str = "kernel_source_sha256_16"):
     """HBM traffic per call (decode by default; `key` picks another kernel's
-    figure) from a committed rocprofv3 PMC summary, if it was taken on the
+    figure) from the committed rocprofv3 PMC summary, if it was taken on the
     current kernel source; else None."""
-    prof = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.txt")
-    if not os.path.exists(prof):
-        return None
-    vals = {}
-    with open(prof) as f:
-        for ln in f:
-            if ":" in ln and not ln.startswith("#"):
-                k, v = ln.split(":", 1)
-                vals[k.strip()] = v.strip()
-    if vals.get(hash_key) != src_hash(kernel_files):
+    vals = read_profile(workload)
+    if not vals or vals.get(hash_key) != src_hash(kernel_files):
         return None
     try:
         return float(vals[key])
@@ -153,13 +195,14 @@ def read_traffic(kernel_files, workload: str, key: str = "hbm_bytes_per_call",
 
 def cpu_baseline(wl, target_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
-    whole sequences (all KV heads, the full context) generated on the host,
-    quantized and attended by the oracle; rate in the metric's unit."""
+    sequences of up to 8192 tokens (all KV heads) generated on the host with the
+    workload's value distribution, quantized and attended by the oracle; rate in
+    the metric's unit (decode GB/s over the same algorithmic bytes as the GPU)."""
     import numpy as np
     import torch
 
     import oracle
-    from nvfp4_quantized_paged_kv_amd import synth
+    from synthetic import synth
 
     H, ctx = wl.kv_heads, min(wl.ctx, 8192)
     in_b = 2 if wl.in_dtype == torch.bfloat16 else 4
@@ -169,7 +212,7 @@ def cpu_baseline(wl, target_s: float):
     t_q = 0.0
     q_bytes = 0
     seqs = 0
-    while t_dec + t_q < target_s and seqs < wl.batch:
+    while t_dec + t_q < target_s and seqs < max(wl.batch, 64):
         k = synth.kv_values(ctx, H, wl.dist, wl.outlier_frac, 0, wl.in_dtype, "cpu", 900 + seqs)
         v = synth.kv_values(ctx, H, wl.dist, wl.outlier_frac, 1, wl.in_dtype, "cpu", 900 + seqs)
         g_k = 1.0 if wl.global_one else synth.global_scale(float(k.float().abs().max()))
@@ -195,9 +238,9 @@ def cpu_baseline(wl, target_s: float):
         "unit": "GB/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": f"{seqs} sequence(s) x {ctx} tokens x {H} kv heads x {wl.q_heads} q heads: "
-                  f"oracle decode {t_dec:.2f} s; oracle quantize {t_q:.2f} s "
-                  f"({q_bytes / t_q / 1e9:.4f} GB/s)",
+        "sample": f"{seqs} sequence(s) x {ctx} tokens x {H} kv heads x {wl.q_heads} q heads "
+                  f"(the workload's value distribution): oracle decode {t_dec:.2f} s; oracle quantize "
+                  f"{t_q:.2f} s ({q_bytes / t_q / 1e9:.4f} GB/s)",
         "quantize_gbps": round(q_bytes / t_q / 1e9, 4),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
@@ -248,7 +291,7 @@ def bench_mixed(args, wl, dev):
     import torch
 
     import nvfp4_quantized_paged_kv_amd as nk
-    from nvfp4_quantized_paged_kv_amd.workloads import build_mixed_step
+    from synthetic.workloads import build_mixed_step, first_chunk
     warm_kernels(wl, dev)
 
     L = args.layers or wl.layers
@@ -280,78 +323,54 @@ def bench_mixed(args, wl, dev):
     b_dec = dec_tokens * H * 144 + dec_pages * 4 + n_dec * Hq * 128 * (in_b + 4)
     sm = 1 / math.sqrt(128)
 
-    def step(l, ev=None):
-        # with ev: each kernel sits between its own event pair, preceded by a GPU
-        # sleep that covers the host-side call, so the pair brackets only the kernel
-        st = steps[l]
-        if ev is not None:
-            torch.cuda._sleep(SLEEP_CYCLES)
-            ev[0].record(stream)
+    def app_call(i):
+        st = steps[i % L]
         nk.quantize_append(st.filled.layer, st.new_k, st.new_v, st.new_slots)
-        if ev is not None:
-            ev[1].record(stream)
-            torch.cuda._sleep(SLEEP_CYCLES)
-            ev[2].record(stream)
+
+    def ws_call(i):
+        st = steps[i % L]
         nk.dequant_to_fp8_workspace(st.filled.layer, st.ext_table, st.ext_prefix, st.ext_offsets, st.max_prefix,
                                     6 * st.filled.layer.k_global, 6 * st.filled.layer.v_global, ws_k, ws_v)
-        if ev is not None:
-            ev[3].record(stream)
-            torch.cuda._sleep(SLEEP_CYCLES)
-            ev[4].record(stream)
-        nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
-                             workspace=dws)
-        if ev is not None:
-            ev[5].record(stream)
 
-    for i in range(args.warmup):
-        step(i % L)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % L)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i % L, evs[i])
-    torch.cuda.synchronize()
-    app = np.array([e[0].elapsed_time(e[1]) for e in evs]) / 1e3
-    wsd = np.array([e[2].elapsed_time(e[3]) for e in evs]) / 1e3
-    dec = np.array([e[4].elapsed_time(e[5]) for e in evs]) / 1e3
-    # decode calls back to back between one event pair (the roofline's per-launch duration)
     def dec_call(i):
         st = steps[i % L]
         nk.paged_decode_attn(st.filled.layer, st.dec_q, st.dec_table, st.dec_lens, st.max_dec_len, sm, out=out,
                              workspace=dws)
-    dec_b2b = back_to_back(stream, args.steps, dec_call)
-    # the step's append back to back (each call rewrites its layer's new tokens: the same bytes)
-    def app_call(i):
-        st = steps[i % L]
-        nk.quantize_append(st.filled.layer, st.new_k, st.new_v, st.new_slots)
+
+    def step(i):
+        app_call(i)
+        ws_call(i)
+        dec_call(i)
+
+    for l in range(L):  # set-up: touch every layer once
+        step(l)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    wall, ev = sync_windows(step, args.steps, STEP_WINDOWS)
+    per_step = float(np.median(wall))
+    step_b2b = back_to_back(stream, args.steps, step)
+    dec_spread = []
+    dec_b2b = back_to_back(stream, args.steps, dec_call, spread_out=dec_spread)
     app_b2b = back_to_back(stream, args.steps, app_call)
+    ws_b2b = back_to_back(stream, args.steps, ws_call)
     # bulk append back to back over the first fill chunk of two layers
-    from nvfp4_quantized_paged_kv_amd.workloads import first_chunk
     b2b_layers = list(range(min(L, 2)))
     bulk_us, bulk_gbs, _ = append_b2b(stream, args.steps,
-                                   [first_chunk(wl, list(wl.lens), l, steps[l].filled.block_table, dev)
-                                    for l in b2b_layers],
-                                   [steps[l].filled.layer for l in b2b_layers], nk.quantize_append, 144)
+                                      [first_chunk(wl, list(wl.lens), l, steps[l].filled.block_table, dev)
+                                       for l in b2b_layers],
+                                      [steps[l].filled.layer for l in b2b_layers], nk.quantize_append, 144)
 
     # ---- extend chunks: their K/V as FP8 rows after each prefix, then causal
     # attention of the chunk queries over [prefix | chunk] in the workspace
     ext_out = torch.empty((s0.ext_q.shape[0], Hq, 128), dtype=torch.float32, device=dev)
     scales = lambda st: (6 * st.filled.layer.k_global, 6 * st.filled.layer.v_global)
-    rows_ms = []
-    for i in range(max(5, min(args.steps, 20))):
+
+    def rows_call(i):
         st = steps[i % L]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(SLEEP_CYCLES)
-        e0.record(stream)
         nk.fp8_rows_to_workspace(st.new_k, st.new_v, st.ext_rows, *scales(st), ws_k, ws_v)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rows_ms.append(e0.elapsed_time(e1))
+    rows_s = back_to_back(stream, args.steps, rows_call)
     t_ext = int(s0.ext_q.shape[0])
     b_rows = t_ext * H * 128 * (2 * in_b + 2) + 4 * t_new
 
@@ -359,7 +378,7 @@ def bench_mixed(args, wl, dev):
         st = steps[i % L]
         nk.fp8_extend_attn(st.ext_q, st.ext_q_offsets, st.ext_offsets[:-1], st.ext_prefix, st.ext_chunk, ws_k, ws_v,
                            *scales(st), sm, out=ext_out)
-    ext_s = back_to_back(stream, max(4, args.steps // 10), ext_call)
+    ext_s = back_to_back(stream, max(4, args.steps // 5), ext_call, windows=3)
     C = s0.ext_chunk
     pairs = sum(C * int(p) + C * (C + 1) // 2 for p in s0.ext_prefix.cpu().numpy())  # (query token, key) pairs
     ext_flops = pairs * Hq * 4 * 128  # QK^T and PV: 2 x 128 multiply-adds per (query row, key)
@@ -368,24 +387,26 @@ def bench_mixed(args, wl, dev):
     b_step = b_app + b_ws + b_dec
     achieved = b_dec / dec_b2b / 1e9
     return {
-        "value": round(b_step / (wall / args.steps) / 1e9, 2),
-        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "value": round(b_step / per_step / 1e9, 2),
+        "ms_per_step": round(per_step * 1e3, 5),
+        "ms_per_step_windows": spread(wall, 1e3, 5),
+        "ms_per_step_events_windows": spread(ev, 1e3, 5),
+        "step_us_b2b": round(step_b2b * 1e6, 3),
         "config": {"workload": wl.name, "sequences": len(s0.lens), "decode_sequences": int(n_dec),
                    "extend_sequences": int(n_ext), "q_heads": Hq, "kv_heads": H, "head_dim": 128, "page_size": 16,
                    "layers_rotated": L, "new_tokens": int(t_new), "decode_tokens": dec_tokens,
                    "workspace_tokens": ws_prefix, "workspace_rows": ws_cap,
                    "step": "append 16/2048 tokens + FP8 workspace dequant of 8 prefixes + decode of 56, one layer"},
-        "pct_of_peak": round(100 * b_step / (wall / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
+        "pct_of_peak": round(100 * b_step / per_step / 1e9 / PEAK_HBM_GBS, 2),
         "decode_attn_gbs_events": round(achieved, 2),
         "decode_attn_us": round(dec_b2b * 1e6, 3),
-        "decode_attn_us_per_call_events": round(dec.mean() * 1e6, 3),
+        "decode_attn_us_windows": spread(dec_spread, 1e6),
         "append_step_gbs": round(b_app / app_b2b / 1e9, 2),
         "append_step_us": round(app_b2b * 1e6, 3),
-        "append_step_us_per_call_events": round(app.mean() * 1e6, 3),
-        "fp8_workspace_gbs": round(b_ws / wsd.mean() / 1e9, 2),
-        "fp8_workspace_us": round(wsd.mean() * 1e6, 3),
-        "fp8_rows_us": round(float(np.median(rows_ms)) * 1e3, 3),
-        "fp8_rows_gbs": round(b_rows / (float(np.median(rows_ms)) / 1e3) / 1e9, 2),
+        "fp8_workspace_gbs": round(b_ws / ws_b2b / 1e9, 2),
+        "fp8_workspace_us": round(ws_b2b * 1e6, 3),
+        "fp8_rows_us": round(rows_s * 1e6, 3),
+        "fp8_rows_gbs": round(b_rows / rows_s / 1e9, 2),
         "extend_attn_us": round(ext_s * 1e6, 2),
         "extend_attn_tflops": round(ext_tf, 2),
         "extend_roofline": {"bound": "mfma", "achieved": round(ext_tf, 2), "peak": PEAK_F16_TFLOPS,
@@ -402,58 +423,25 @@ def bench_mixed(args, wl, dev):
     }
 
 
-def calibration_kernel():
-    """A plain elementwise kernel of known traffic: y = x + 1 over 2^28 float32."""
-    import torch
-
-    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    y = torch.empty_like(x)
-    for _ in range(3):
-        torch.add(x, 1.0, out=y)
-    torch.cuda.synchronize()
-
-
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "requested_gpus": args.gpus}))
-        sys.exit(2)
-
+def bench_uniform(args, wl, dev):
+    """Equal-length batches (the tiny, 70B-class, 128K and 2M-token workloads)."""
     import numpy as np
     import torch
 
     import nvfp4_quantized_paged_kv_amd as nk
-    from nvfp4_quantized_paged_kv_amd import synth
+    from synthetic import synth
+    from synthetic.workloads import build_layer, first_chunk
 
-    assert torch.cuda.is_available(), "bench needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = synth.WORKLOADS[args.workload]
-    if wl.lens:
-        res = bench_mixed(args, wl, dev)
-        result = {"metric": METRIC, "value": res.pop("value"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-                  "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
-                  "scaling": "weak", "vs_baseline": None,
-                  "dtype": "nvfp4 cache; bf16 in; f16 MFMA, fp32 accumulate",
-                  "data": "synthetic (seeded torch generators)"}
-        result.update(res)
-        if args.calibrate:
-            calibration_kernel()
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-        print(json.dumps(result), flush=True)
-        return
     L = args.layers or wl.layers
     B, Hq, H, ctx = wl.batch, wl.q_heads, wl.kv_heads, wl.ctx
     pages_per_seq = (ctx + 15) // 16
+    layer_bytes = B * pages_per_seq * H * 2304
+    L_x = min(L, 2) if layer_bytes >= BIG_LAYER_BYTES else L  # layers of the comparison formats
     stream = torch.cuda.current_stream()
     print(f"[bench] workload {wl.name}: B={B} Hq={Hq} H={H} ctx={ctx} layers={L}", file=sys.stderr, flush=True)
 
     # ---- build L layer caches (bulk quantize-append of ctx-1 tokens per sequence, timed)
-    from nvfp4_quantized_paged_kv_amd.workloads import build_layer
     warm_kernels(wl, dev)
-
     layers, tables, newk, newv, slots_new, qs, bts = [], [], [], [], [], [], []
     append_ms, append_bytes = [], []
     for l in range(L):
@@ -482,119 +470,49 @@ def main():
     bytes_decode = B * ctx * H * 144 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
     bytes_step = bytes_append_step + bytes_decode
 
-    def step(l, ev=None):
-        # with ev: each kernel sits between its own event pair, preceded by a GPU
-        # sleep that covers the host-side call, so the pair brackets only the kernel
-        if ev is not None:
-            torch.cuda._sleep(SLEEP_CYCLES)
-            ev[0].record(stream)
-        nk.quantize_append(layers[l], newk[l], newv[l], slots_new[l])
-        if ev is not None:
-            ev[1].record(stream)
-            torch.cuda._sleep(SLEEP_CYCLES)
-            ev[2].record(stream)
-        nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for i in range(args.warmup):
-        step(i % L)
-    torch.cuda.synchronize()
-
-    # ---- the same step in one launch: the decode kernel appends the new token itself
+    # the step as one library call: nvfp4_paged_decode_step appends the new
+    # token inside the decode kernel, or launches the append kernel first, by shape
     kn_f = [newk[l].reshape(B, 1, H, 128) for l in range(L)]
     vn_f = [newv[l].reshape(B, 1, H, 128) for l in range(L)]
     q_f = [qs[l].reshape(B, 1, Hq, 128) for l in range(L)]
     out_f = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device=dev)
 
-    def lib_step(l):
+    def lib_step(i):
+        l = i % L
         nk.paged_decode_step(layers[l], kn_f[l], vn_f[l], q_f[l], tables[l], seq_lens, ctx, sm, out=out_f,
                              workspace=workspace)
 
-    for i in range(args.warmup):
-        lib_step(i % L)
-    torch.cuda.synchronize()
+    def app_call(i):
+        l = i % L
+        nk.quantize_append(layers[l], newk[l], newv[l], slots_new[l])
 
-    # ---- timed region: K steps, wall clock, of the library's decode step
-    # (nvfp4_paged_decode_step: the value; it appends inside the decode kernel
-    # or launches the append kernel first, by the shape), then the same step
-    # as two explicit calls (quantize-append, decode) beside it
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        lib_step(i % L)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % L)
-    torch.cuda.synchronize()
-    wall_two = time.perf_counter() - t0
-
-    # ---- same steps again with HIP events on the launch stream (per-call durations)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i % L, evs[i])
-    torch.cuda.synchronize()
-    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-
-    # ---- decode calls back to back between one event pair (the roofline's
-    # per-launch duration: no per-call event or dispatch overhead inside it)
     def dec_call(i):
         l = i % L
         nk.paged_decode_attn(layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
-    dec_avg_s = back_to_back(stream, args.steps, dec_call)
-    step_s = back_to_back(stream, args.steps, lambda i: lib_step(i % L))
 
-    # ---- multi-token decode: T = 16 / G new tokens per sequence (the last T of
-    # the context) fill the 16-row MFMA tile in the same pass over the cache
-    multi = None
-    T_m = 16 // (Hq // H)
-    if T_m >= 2:
-        q_m = [synth.queries(B * T_m, Hq, wl.in_dtype, dev, 6, l).reshape(B, T_m, Hq, 128) for l in range(L)]
-        out_m = torch.empty((B, T_m, Hq, 128), dtype=torch.float32, device=dev)
-        ws_m = torch.zeros(nk.decode_multi_workspace_bytes(B, T_m, Hq, H, ctx), dtype=torch.uint8, device=dev)
+    def two_step(i):  # the same step as two explicit calls
+        app_call(i)
+        dec_call(i)
 
-        def multi_call(i):
-            l = i % L
-            nk.paged_decode_attn_multi(layers[l], q_m[l], tables[l], seq_lens, ctx, sm, out=out_m, workspace=ws_m)
-        multi_s = back_to_back(stream, args.steps, multi_call)
-        b_multi = B * ctx * H * 144 + B * pages_per_seq * 4 + B * T_m * Hq * 128 * (in_b + 4)
-        multi = {"q_per_seq": T_m, "us": round(multi_s * 1e6, 3), "gbs": round(b_multi / multi_s / 1e9, 2),
-                 "query_tokens_per_s": round(B * T_m / multi_s, 1),
-                 "time_vs_one_token": round(multi_s / dec_avg_s, 4)}
+    for l in range(L):  # set-up: touch every layer once
+        lib_step(l)
+    torch.cuda.synchronize()
+
+    # ---- warm-up, then the timed region: windows of exactly --steps step calls
+    for i in range(args.warmup):
+        lib_step(i)
+    torch.cuda.synchronize()
+    wall, ev = sync_windows(lib_step, args.steps, STEP_WINDOWS)
+    per_step = float(np.median(wall))
+    wall_two, _ = sync_windows(two_step, args.steps, 3)
+    print("[bench] step timed", file=sys.stderr, flush=True)
+
+    # ---- kernels back to back (the rooflines' per-launch durations)
+    dec_spread = []
+    dec_avg_s = back_to_back(stream, args.steps, dec_call, spread_out=dec_spread)
+    step_s = back_to_back(stream, args.steps, lib_step)
+    app_s = back_to_back(stream, args.steps, app_call)
     achieved = bytes_decode / dec_avg_s / 1e9
-
-    # ---- FP8 workspace dequant on the same cache: 8 sequences' full prefixes (extend path)
-    n_ext = min(8, B)
-    prefix = torch.full((n_ext,), ctx, dtype=torch.int32, device=dev)
-    offs = torch.arange(0, (n_ext + 1) * ctx, ctx, dtype=torch.int32, device=dev)
-    ws_k = torch.empty((n_ext * ctx, H, 128), dtype=torch.uint8, device=dev)
-    ws_v = torch.empty_like(ws_k)
-    ws_ms = []
-    for i in range(max(5, min(args.steps, 20))):
-        l = i % L
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        tab = tables[l][:n_ext].contiguous()
-        torch.cuda._sleep(SLEEP_CYCLES)
-        e0.record(stream)
-        nk.dequant_to_fp8_workspace(layers[l], tab, prefix, offs, ctx,
-                                    6 * layers[l].k_global, 6 * layers[l].v_global, ws_k, ws_v)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ws_ms.append(e0.elapsed_time(e1))
-    ws_bytes_alg = n_ext * ctx * H * (144 + 256) + n_ext * pages_per_seq * 4
-    ws_gbs = ws_bytes_alg / (float(np.median(ws_ms)) / 1e3) / 1e9
-
-    app_total_b = float(sum(append_bytes))
-    app_total_s = float(sum(append_ms)) / 1e3
-    traffic = read_traffic(DECODE_SOURCES, wl.name)
-    # bulk append back to back over the first fill chunk of two layers
-    from nvfp4_quantized_paged_kv_amd.workloads import first_chunk
     b2b_layers = list(range(min(L, 2)))
     chunks = {}
 
@@ -604,95 +522,26 @@ def main():
         return chunks[fill]
     app_us, app_gbs, app_b = append_b2b(stream, args.steps, chunk_set(ctx - 1), [layers[l] for l in b2b_layers],
                                         nk.quantize_append, 144)
-    print("[bench] bulk append timed back to back", file=sys.stderr, flush=True)
-
-    # ---- MXFP4, the format the pages compare NVFP4 against (E8M0 scale per 32
-    # values, 17/32 byte per value): the same tokens, slots and queries in
-    # MXFP4 layers; bulk append and decode timed as above
-    mx_layers, mx_app_ms, mx_app_b = [], [], []
-    for l in range(L):
-        fl = build_layer(wl, [ctx] * B, [ctx] * B, l, dev, timed=True, mx=True)
-        mx_layers.append(fl.layer)
-        mx_app_ms += fl.append_ms
-        mx_app_b += fl.append_bytes
-    print("[bench] MXFP4 layers filled", file=sys.stderr, flush=True)
-
-    def mx_call(i):
-        l = i % L
-        nk.mx_paged_decode_attn(mx_layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
-    for i in range(args.warmup):
-        mx_call(i)
-    mx_s = back_to_back(stream, args.steps, mx_call)
-    mx_app_us, mx_app_gbs, _ = append_b2b(stream, args.steps, chunk_set(ctx), [mx_layers[l] for l in b2b_layers],
-                                       nk.mx_quantize_append, 136)
-    bytes_mx = B * ctx * H * 136 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
-    mxfp4 = {"decode_us": round(mx_s * 1e6, 3), "decode_gbs": round(bytes_mx / mx_s / 1e9, 2),
-             "decode_frac": round(bytes_mx / mx_s / 1e9 / PEAK_HBM_GBS, 4),
-             "algorithmic_bytes_per_call": int(bytes_mx),
-             "decode_time_vs_nvfp4": round(mx_s / dec_avg_s, 4),
-             "quantize_append_bulk_gbs": round(mx_app_gbs, 2), "quantize_append_bulk_us": round(mx_app_us, 2),
-             "quantize_append_bulk_gbs_single_call":
-                 round(float(sum(mx_app_b)) / (float(sum(mx_app_ms)) / 1e3) / 1e9, 2)}
-    # ---- Hadamard-rotated K (both formats): the same tokens stored with K
-    # rotated by the append kernel; the decode rotates Q in its prologue and
-    # takes Q as a hi + lo pair (twice the QK^T MFMAs)
-    hadamard = {}
-    for fmt, mx in (("nvfp4", False), ("mxfp4", True)):
-        rot_layers, rot_ms, rot_b = [], [], []
-        for l in range(L):
-            fl = build_layer(wl, [ctx] * B, [ctx] * B, l, dev, timed=True, mx=mx, hadamard=True)
-            rot_layers.append(fl.layer)
-            rot_ms += fl.append_ms
-            rot_b += fl.append_bytes
-        dec = nk.mx_paged_decode_attn if mx else nk.paged_decode_attn
-
-        def rot_call(i):
-            l = i % L
-            dec(rot_layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace, hadamard=True)
-        for i in range(args.warmup):
-            rot_call(i)
-        rot_s = back_to_back(stream, args.steps, rot_call)
-        rot_app_us, rot_app_gbs, _ = append_b2b(stream, args.steps, chunk_set(ctx), [rot_layers[l] for l in b2b_layers],
-                                             nk.mx_quantize_append if mx else nk.quantize_append, 136 if mx else 144,
-                                             hadamard=True)
-        b_rot = bytes_mx if mx else bytes_decode
-        plain_s = mx_s if mx else dec_avg_s
-        hadamard[fmt] = {"decode_us": round(rot_s * 1e6, 3), "decode_gbs": round(b_rot / rot_s / 1e9, 2),
-                         "decode_time_vs_unrotated": round(rot_s / plain_s, 4),
-                         "quantize_append_bulk_gbs": round(rot_app_gbs, 2),
-                         "quantize_append_bulk_us": round(rot_app_us, 2),
-                         "quantize_append_bulk_gbs_single_call":
-                             round(float(sum(rot_b)) / (float(sum(rot_ms)) / 1e3) / 1e9, 2)}
-        del rot_layers
-    print("[bench] Hadamard-rotated layers timed", file=sys.stderr, flush=True)
-    del mx_layers
+    print("[bench] decode and bulk append timed back to back", file=sys.stderr, flush=True)
+    app_total_b = float(sum(append_bytes))
+    app_total_s = float(sum(append_ms)) / 1e3
 
     result = {
-        "metric": METRIC,
-        "value": round(bytes_step / (wall / args.steps) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "nvfp4 cache; bf16 in; f16 MFMA, fp32 accumulate" if wl.in_dtype == torch.bfloat16
-                 else "nvfp4 cache; f32 in; f16 MFMA, fp32 accumulate",
-        "data": "synthetic (seeded torch generators)",
+        "value": round(bytes_step / per_step / 1e9, 2),
+        "ms_per_step": round(per_step * 1e3, 5),
+        "ms_per_step_windows": spread(wall, 1e3, 5),
+        "ms_per_step_events_windows": spread(ev, 1e3, 5),
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
                    "context": ctx, "page_size": 16, "layers_rotated": L,
                    "step": "nvfp4_paged_decode_step: append 1 token/seq + decode attention, one layer"},
-        "pct_of_peak": round(100 * bytes_step / (wall / args.steps) / 1e9 / PEAK_HBM_GBS, 2),
+        "pct_of_peak": round(100 * bytes_step / per_step / 1e9 / PEAK_HBM_GBS, 2),
+        "step_us_b2b": round(step_s * 1e6, 3),
+        "step_append_then_decode": {"ms_per_step": round(float(np.median(wall_two)) * 1e3, 5),
+                                    "value": round(bytes_step / float(np.median(wall_two)) / 1e9, 2)},
         "decode_attn_gbs_events": round(achieved, 2),
         "decode_attn_us": round(dec_avg_s * 1e6, 3),
-        "decode_attn_us_per_call_events": round(float(dec_ms.mean()) * 1e3, 3),
-        "decode_multi_token": multi,
-        "step_us_b2b": round(step_s * 1e6, 3),
-        "step_append_then_decode": {"ms_per_step": round(wall_two * 1e3 / args.steps, 5),
-                                    "value": round(bytes_step / (wall_two / args.steps) / 1e9, 2)},
-        "append_step_us": round(float(app_ms.mean()) * 1e3, 3),
+        "decode_attn_us_windows": spread(dec_spread, 1e6),
+        "append_step_us": round(app_s * 1e6, 3),
         "quantize_append_bulk_gbs": round(app_gbs, 2),
         "quantize_append_bulk_us": round(app_us, 2),
         "quantize_append_bulk_chunk_tokens": int(chunk_set(ctx - 1)[0][0].shape[0]),
@@ -704,17 +553,158 @@ def main():
                             "algorithmic_bytes_per_call": int(app_b)},
         "quantize_append_bulk_gbs_single_call": round(app_total_b / app_total_s / 1e9, 2),
         "quantize_append_bulk_tokens": int(B * (ctx - 1) * L),
-        "fp8_workspace_gbs": round(ws_gbs, 2),
-        "fp8_workspace_tokens": int(n_ext * ctx),
-        "mxfp4": mxfp4,
-        "hadamard_k": hadamard,
         "bytes_per_step": int(bytes_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": read_traffic(DECODE_SOURCES, wl.name),
                      "kernel": "nvfp4_paged_decode_attn (decode_kernel)",
                      "algorithmic_bytes_per_call": int(bytes_decode)},
     }
+    if args.no_extras:
+        return result
+
+    # ---- multi-token decode: T = 16 / G new tokens per sequence (the last T of
+    # the context) fill the 16-row MFMA tile in the same pass over the cache
+    T_m = 16 // (Hq // H)
+    if T_m >= 2:
+        q_m = [synth.queries(B * T_m, Hq, wl.in_dtype, dev, 6, l).reshape(B, T_m, Hq, 128) for l in range(L)]
+        out_m = torch.empty((B, T_m, Hq, 128), dtype=torch.float32, device=dev)
+        ws_m = torch.zeros(nk.decode_multi_workspace_bytes(B, T_m, Hq, H, ctx), dtype=torch.uint8, device=dev)
+
+        def multi_call(i):
+            l = i % L
+            nk.paged_decode_attn_multi(layers[l], q_m[l], tables[l], seq_lens, ctx, sm, out=out_m, workspace=ws_m)
+        multi_s = back_to_back(stream, args.steps, multi_call)
+        b_multi = B * ctx * H * 144 + B * pages_per_seq * 4 + B * T_m * Hq * 128 * (in_b + 4)
+        result["decode_multi_token"] = {"q_per_seq": T_m, "us": round(multi_s * 1e6, 3),
+                                        "gbs": round(b_multi / multi_s / 1e9, 2),
+                                        "query_tokens_per_s": round(B * T_m / multi_s, 1),
+                                        "time_vs_one_token": round(multi_s / dec_avg_s, 4)}
+
+    # ---- FP8 workspace dequant on the same cache: up to 8 sequences' full prefixes (extend path)
+    n_ext = min(8, B)
+    prefix = torch.full((n_ext,), ctx, dtype=torch.int32, device=dev)
+    offs = torch.arange(0, (n_ext + 1) * ctx, ctx, dtype=torch.int32, device=dev)
+    ws_k = torch.empty((n_ext * ctx, H, 128), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty_like(ws_k)
+    tabs = [tables[l][:n_ext].contiguous() for l in range(L)]
+
+    def ws_call(i):
+        l = i % L
+        nk.dequant_to_fp8_workspace(layers[l], tabs[l], prefix, offs, ctx, 6 * layers[l].k_global,
+                                    6 * layers[l].v_global, ws_k, ws_v)
+    ws_s = back_to_back(stream, max(4, args.steps // 2), ws_call)
+    ws_bytes_alg = n_ext * ctx * H * (144 + 256) + n_ext * pages_per_seq * 4
+    result["fp8_workspace_gbs"] = round(ws_bytes_alg / ws_s / 1e9, 2)
+    result["fp8_workspace_us"] = round(ws_s * 1e6, 3)
+    result["fp8_workspace_tokens"] = int(n_ext * ctx)
+    del ws_k, ws_v
+
+    # ---- MXFP4, the format the pages compare NVFP4 against (E8M0 scale per 32
+    # values, 17/32 byte per value): the same tokens, slots and queries in
+    # MXFP4 layers; bulk append and decode timed as above
+    mx_layers, mx_app_ms, mx_app_b = [], [], []
+    for l in range(L_x):
+        fl = build_layer(wl, [ctx] * B, [ctx] * B, l, dev, timed=True, mx=True)
+        mx_layers.append(fl.layer)
+        mx_app_ms += fl.append_ms
+        mx_app_b += fl.append_bytes
+    print("[bench] MXFP4 layers filled", file=sys.stderr, flush=True)
+
+    def mx_call(i):
+        l = i % L_x
+        nk.mx_paged_decode_attn(mx_layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace)
+    for i in range(max(args.warmup, L_x)):
+        mx_call(i)
+    mx_s = back_to_back(stream, args.steps, mx_call)
+    mx_app_us, mx_app_gbs, _ = append_b2b(stream, args.steps, chunk_set(ctx), [mx_layers[l] for l in b2b_layers],
+                                          nk.mx_quantize_append, 136)
+    bytes_mx = B * ctx * H * 136 + B * pages_per_seq * 4 + B * Hq * 128 * in_b + B * Hq * 128 * 4
+    result["mxfp4"] = {"layers_rotated": L_x, "decode_us": round(mx_s * 1e6, 3),
+                       "decode_gbs": round(bytes_mx / mx_s / 1e9, 2),
+                       "decode_frac": round(bytes_mx / mx_s / 1e9 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes_per_call": int(bytes_mx),
+                       "decode_time_vs_nvfp4": round(mx_s / dec_avg_s, 4),
+                       "quantize_append_bulk_gbs": round(mx_app_gbs, 2),
+                       "quantize_append_bulk_us": round(mx_app_us, 2),
+                       "quantize_append_bulk_gbs_single_call":
+                           round(float(sum(mx_app_b)) / (float(sum(mx_app_ms)) / 1e3) / 1e9, 2)}
+    del mx_layers
+    # ---- Hadamard-rotated K (both formats): the same tokens stored with K
+    # rotated by the append kernel; the decode rotates Q in its prologue and
+    # takes Q as a hi + lo pair (twice the QK^T MFMAs)
+    hadamard = {}
+    for fmt, mx in (("nvfp4", False), ("mxfp4", True)):
+        rot_layers, rot_ms, rot_b = [], [], []
+        for l in range(L_x):
+            fl = build_layer(wl, [ctx] * B, [ctx] * B, l, dev, timed=True, mx=mx, hadamard=True)
+            rot_layers.append(fl.layer)
+            rot_ms += fl.append_ms
+            rot_b += fl.append_bytes
+        dec = nk.mx_paged_decode_attn if mx else nk.paged_decode_attn
+
+        def rot_call(i):
+            l = i % L_x
+            dec(rot_layers[l], qs[l], tables[l], seq_lens, ctx, sm, out=out, workspace=workspace, hadamard=True)
+        for i in range(max(args.warmup, L_x)):
+            rot_call(i)
+        rot_s = back_to_back(stream, args.steps, rot_call)
+        rot_app_us, rot_app_gbs, _ = append_b2b(stream, args.steps, chunk_set(ctx),
+                                                [rot_layers[l] for l in b2b_layers],
+                                                nk.mx_quantize_append if mx else nk.quantize_append,
+                                                136 if mx else 144, hadamard=True)
+        b_rot = bytes_mx if mx else bytes_decode
+        plain_s = mx_s if mx else dec_avg_s
+        hadamard[fmt] = {"layers_rotated": L_x, "decode_us": round(rot_s * 1e6, 3),
+                         "decode_gbs": round(b_rot / rot_s / 1e9, 2),
+                         "decode_time_vs_unrotated": round(rot_s / plain_s, 4),
+                         "quantize_append_bulk_gbs": round(rot_app_gbs, 2),
+                         "quantize_append_bulk_us": round(rot_app_us, 2),
+                         "quantize_append_bulk_gbs_single_call":
+                             round(float(sum(rot_b)) / (float(sum(rot_ms)) / 1e3) / 1e9, 2)}
+        del rot_layers
+    result["hadamard_k"] = hadamard
+    print("[bench] Hadamard-rotated layers timed", file=sys.stderr, flush=True)
+    return result
+
+
+def calibration_kernel():
+    """A plain elementwise kernel of known traffic: y = x + 1 over 2^28 float32."""
+    import torch
+
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.add(x, 1.0, out=y)
+    torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+
+    import nvfp4_quantized_paged_kv_amd  # noqa: F401  (fails loudly if the HIP library is not built)
+    from synthetic import synth
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    res = bench_mixed(args, wl, dev) if wl.lens else bench_uniform(args, wl, dev)
+    in_dtype = "bf16" if wl.in_dtype == torch.bfloat16 else "f32"
+    result = {"metric": METRIC, "value": res.pop("value"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None,
+              "dtype": f"nvfp4 cache; {in_dtype} in; f16 MFMA, fp32 accumulate",
+              "data": "synthetic (seeded torch generators)"}
+    result.update(res)
     if args.calibrate:
         calibration_kernel()
     if not args.no_cpu_baseline:

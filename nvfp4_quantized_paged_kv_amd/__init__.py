@@ -160,6 +160,16 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+def _zeros_on(nbytes: int, device, stream) -> torch.Tensor:
+    """A zero-filled byte buffer whose fill is queued on `stream` (torch's
+    current stream when None), so a kernel launched there sees the zeros."""
+    if stream is None:
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(s):
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def _ptr(t: torch.Tensor | None):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -242,10 +252,13 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_
     return int(lib.nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len))
 
 
-def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int, device="cuda") -> torch.Tensor:
-    """A zero-filled decode workspace (the library keeps it zeroed between calls)."""
+def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int, device="cuda",
+                     stream=None) -> torch.Tensor:
+    """A zero-filled decode workspace (the library keeps it zeroed between calls),
+    filled on `stream` (torch's current stream when None).  Allocate it once and
+    pass it to every call on that stream."""
     need = max(decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len), 256)
-    return torch.zeros(need, dtype=torch.uint8, device=device)
+    return _zeros_on(need, device, stream)
 
 
 def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
@@ -254,7 +267,7 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
     """Decode attention of q [B, Hq, 128] (bf16/f32) over the cache; returns f32 [B, Hq, 128].
 
     hadamard: the cache holds rotated K (quantize_append(..., hadamard=True)); q is rotated alike."""
-    out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace)
+    out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace, stream)
     c = layer.c_struct()
     name = "nvfp4_paged_decode_attn_hadamard" if hadamard else "nvfp4_paged_decode_attn"
     st = getattr(lib, name)(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],
@@ -264,8 +277,9 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
     return out
 
 
-def _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace):
-    """Validate one-token decode arguments; allocate out / workspace when not given."""
+def _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace, stream):
+    """Validate one-token decode arguments; allocate out / workspace when not given
+    (a fresh workspace is zero-filled on the call's stream)."""
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
     B, Hq, _ = q.shape
@@ -279,7 +293,7 @@ def _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace):
         raise ValueError("out must be a contiguous float32 [B, Hq, 128] tensor")
     need = decode_workspace_bytes(B, Hq, layer.num_kv_heads, max_seq_len)
     if workspace is None and need > 0:
-        workspace = decode_workspace(B, Hq, layer.num_kv_heads, max_seq_len, q.device)
+        workspace = decode_workspace(B, Hq, layer.num_kv_heads, max_seq_len, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return out, workspace, ws_bytes
 
@@ -306,7 +320,7 @@ def paged_decode_attn_multi(layer: KVCacheLayer, q: torch.Tensor, block_table: t
         raise ValueError("out must be a contiguous float32 [B, T, Hq, 128] tensor")
     need = decode_multi_workspace_bytes(B, T, Hq, layer.num_kv_heads, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _zeros_on(max(need, 256), q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = layer.c_struct()
     st = lib.nvfp4_paged_decode_attn_multi(ctypes.byref(c), _ptr(q), _dtype_code(q), B, T, Hq, _ptr(block_table),
@@ -338,7 +352,7 @@ def paged_decode_step(layer: KVCacheLayer, k_new: torch.Tensor, v_new: torch.Ten
         raise ValueError("out must be a contiguous float32 [B, T, Hq, 128] tensor")
     need = decode_multi_workspace_bytes(B, T, Hq, layer.num_kv_heads, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _zeros_on(max(need, 256), q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = layer.c_struct()
     st = lib.nvfp4_paged_decode_step(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(q), _dtype_code(q), B, T, Hq,
@@ -471,7 +485,7 @@ def mx_paged_decode_attn(layer: MxKVCacheLayer, q: torch.Tensor, block_table: to
                          max_seq_len: int, sm_scale: float, out: torch.Tensor | None = None,
                          workspace: torch.Tensor | None = None, stream=None, hadamard: bool = False) -> torch.Tensor:
     """Decode attention of q [B, Hq, 128] over MXFP4 pages; returns f32 [B, Hq, 128]."""
-    out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace)
+    out, workspace, ws_bytes = _decode_args(layer, q, block_table, seq_lens, max_seq_len, out, workspace, stream)
     c = layer.c_struct()
     name = "mxfp4_paged_decode_attn_hadamard" if hadamard else "mxfp4_paged_decode_attn"
     st = getattr(lib, name)(ctypes.byref(c), _ptr(q), _dtype_code(q), q.shape[0], q.shape[1],

@@ -745,7 +745,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       wait_vmem();  // this wave's partial stores are complete before the arrival is counted
       __syncthreads();
       if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(p.counters + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // release: the workgroup's partial stores (ordered before this by the
+        // barrier) are visible at agent scope before the count moves; acquire:
+        // the last arriver's loads below see every other workgroup's partials
+        const int old = __hip_atomic_fetch_add(p.counters + u, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s_flag = old == w_last - w_first;
       }
       __syncthreads();
