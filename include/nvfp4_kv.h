@@ -22,7 +22,9 @@
  *     asynchronously on it; results are visible after the caller's stream sync.
  *   - Arguments are validated on the host before any HIP call; a failed check
  *     returns a status and enqueues nothing.  A launch failure returns
- *     NVFP4_ERR_HIP.  Functions are stateless and thread-safe.
+ *     NVFP4_ERR_HIP.  Functions are stateless and thread-safe, except
+ *     nvfp4_paged_decode_attn_noalloc, which uses a device scratch array the
+ *     library holds per GPU (see there).
  *   - Supported shapes: head_dim 128 and page_size 16 only (others return
  *     NVFP4_ERR_UNSUPPORTED); at most 16 query heads per KV head.
  *   - Device-side index data (slot_mapping, block_table, seq_lens, prefix_lens,
@@ -140,6 +142,30 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
                                                  int32_t block_table_stride, const int32_t* seq_lens,
                                                  int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                                                  size_t workspace_bytes, void* stream);
+
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): nvfp4_paged_decode_attn with its workspace taken from the
+ * library's own device scratch instead of a caller buffer.  The call
+ * allocates and frees nothing.
+ * Scratch: one 8 MiB device array per GPU, held until the process ends --
+ * 64 KiB of arrival counters (one int32 per (sequence, kv head)), then the
+ * split partials.  The first call on a device looks the array up and clears
+ * the counters with a fill kernel on `stream`; every call leaves them at zero
+ * again.  Every call on a GPU shares that GPU's scratch and finds the last
+ * call's partials in it: calls on one GPU must be ordered (one stream, or
+ * synchronized); calls that overlap race.
+ * Limit: batch * num_kv_heads <= 16384, and the partials must fit:
+ *   nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, num_kv_heads,
+ *   max_seq_len) - 256 * ceil(batch * num_kv_heads / 64) <= 8 MiB - 64 KiB
+ * (e.g. up to 218 sequences of 8 kv heads at 8 query heads per kv head, any
+ * context length).  Larger calls return NVFP4_ERR_WORKSPACE_TOO_SMALL before
+ * any HIP call.  Other arguments, results and errors as nvfp4_paged_decode_attn. */
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_noalloc(const nvfp4_kv_layer_t* layer, const void* q,
+                                                         nvfp4_dtype_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                                         const int32_t* block_table, int32_t block_table_stride,
+                                                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                                         float* out, void* stream);
 
 /* Decode of several new query tokens per sequence (multi-token or
  * speculative decoding).  It is the decode data flow of blog section 3 with q_per_seq query tokens

@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "nvfp4_kv_quantize_append",
     "nvfp4_paged_decode_workspace_bytes",
     "nvfp4_paged_decode_attn",
+    "nvfp4_paged_decode_attn_noalloc",
     "nvfp4_paged_decode_multi_workspace_bytes",
     "nvfp4_paged_decode_attn_multi",
     "nvfp4_paged_decode_step",
@@ -106,6 +107,8 @@ def _load():
     L.nvfp4_paged_decode_workspace_bytes.restype = sz
     L.nvfp4_paged_decode_attn.argtypes = [lp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
     L.nvfp4_paged_decode_attn.restype = ctypes.c_int
+    L.nvfp4_paged_decode_attn_noalloc.argtypes = [lp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, f32, vp, vp]
+    L.nvfp4_paged_decode_attn_noalloc.restype = ctypes.c_int
     L.nvfp4_paged_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.nvfp4_paged_decode_multi_workspace_bytes.restype = sz
     L.nvfp4_paged_decode_attn_multi.argtypes = [lp, vp, ctypes.c_int, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz,
@@ -274,6 +277,29 @@ def paged_decode_attn(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.T
                             _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
                             float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, name)
+    return out
+
+
+def paged_decode_attn_noalloc(layer: KVCacheLayer, q: torch.Tensor, block_table: torch.Tensor,
+                              seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float, out: torch.Tensor,
+                              stream=None) -> torch.Tensor:
+    """paged_decode_attn with the library's own device scratch as its workspace:
+    nothing is allocated (out [B, Hq, 128] float32 is the caller's).  Calls on
+    one GPU share that scratch and must be ordered."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    B, Hq, _ = q.shape
+    _dev_i32(block_table, "block_table")
+    _dev_i32(seq_lens, "seq_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table must be [B, stride] and seq_lens [B]")
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be a contiguous float32 [B, Hq, 128] tensor")
+    c = layer.c_struct()
+    st = lib.nvfp4_paged_decode_attn_noalloc(ctypes.byref(c), _ptr(q), _dtype_code(q), B, Hq, _ptr(block_table),
+                                             block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                                             float(sm_scale), _ptr(out), _stream(stream))
+    _check(st, "nvfp4_paged_decode_attn_noalloc")
     return out
 
 

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "decode_noalloc.h"
 #include "nvfp4_kv.h"
 #include "nvfp4_kv_internal.h"
 
@@ -147,7 +148,7 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
                            nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
                            const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                            int32_t max_seq_len, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                           void* stream, bool mx = false, bool rot_q = false) {
+                           void* stream, bool mx = false, bool rot_q = false, bool use_scratch = false) {
   const nvfp4_status_t st = check_layer(layer);
   if (st != NVFP4_OK) return st;
   if (!dtype_ok(q_dtype) || batch < 0 || q_per_seq < 1 || num_q_heads <= 0 || max_seq_len < 0)
@@ -167,10 +168,27 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
   if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return NVFP4_ERR_UNSUPPORTED;
   const int32_t R = (int32_t)(G * q_per_seq);
   const DecodeGeometry geo = decode_geometry(batch, R, layer->num_kv_heads, max_seq_len);
-  if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
-  if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (use_scratch) {
+    // the library's own scratch: fixed counter region, partials after it
+    const int64_t units = (int64_t)batch * layer->num_kv_heads;
+    if (units * 4 > (int64_t)kNoAllocCounterBytes ||
+        geo.workspace_bytes - geo.counters_bytes > kNoAllocScratchBytes - kNoAllocCounterBytes)
+      return NVFP4_ERR_WORKSPACE_TOO_SMALL;
+  } else {
+    if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARGUMENT;
+  }
   const double qk = (double)sm_scale * (double)layer->k_global * 1.4426950408889634;  // log2(e)
   if (!std::isfinite(qk)) return NVFP4_ERR_INVALID_ARGUMENT;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (use_scratch) {  // every argument is checked above; the first HIP call comes here
+    void* sp = nullptr;
+    const hipError_t e = noalloc_scratch(&sp, hs);
+    if (e != hipSuccess) return from_hip(e);
+    workspace = sp;
+  }
+  const uint8_t* ws_base = static_cast<uint8_t*>(workspace);
+  const size_t part_offset = use_scratch ? kNoAllocCounterBytes : geo.counters_bytes;
   DecodeParams p;
   p.k_codes = layer->k_codes;
   p.k_scales = layer->k_scales;
@@ -180,7 +198,7 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.counters = static_cast<int32_t*>(workspace);
-  p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + geo.counters_bytes);
+  p.part = reinterpret_cast<float*>(const_cast<uint8_t*>(ws_base) + part_offset);
   p.out = out;
   p.num_pages = layer->num_pages;
   p.H = layer->num_kv_heads;
@@ -199,7 +217,6 @@ nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, con
   p.v_new = v_new;
   p.mx = mx ? 1 : 0;
   p.rot_q = rot_q ? 1 : 0;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (k_new && ((int64_t)max_seq_len + kPageSize - 1) / kPageSize > kStepFusedMaxPages) {
     // every argument is checked above: append the step's new tokens, then decode
     AppendParams a;
@@ -234,6 +251,15 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn(const nvfp4_kv_layer_t* layer, 
                                                  size_t workspace_bytes, void* stream) {
   return decode_impl(layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
                      seq_lens, max_seq_len, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_noalloc(const nvfp4_kv_layer_t* layer, const void* q,
+                                                         nvfp4_dtype_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                                         const int32_t* block_table, int32_t block_table_stride,
+                                                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                                         float* out, void* stream) {
+  return decode_impl(layer, nullptr, nullptr, q, q_dtype, batch, 1, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, sm_scale, out, nullptr, 0, stream, false, false, true);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_hadamard(const nvfp4_kv_layer_t* layer, const void* q,

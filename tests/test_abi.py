@@ -308,3 +308,34 @@ def test_hadamard_entry_points_check_like_their_plain_twins():
         need = nk.decode_workspace_bytes(1, 64, 8, 1 << 20)
         assert dec(B=1, msl=1 << 20, bts=1 << 16, wsb=need - 1) == 3
 
+
+
+def _decode_noalloc(nk, layer, q=FAKE, qdt=1, B=2, Hq=64, bt=FAKE, bts=4, sl=FAKE, msl=64, sm=0.088, out=FAKE):
+    return nk.lib.nvfp4_paged_decode_attn_noalloc(ctypes.byref(layer), ctypes.c_void_p(q), qdt, B, Hq,
+                                                  ctypes.c_void_p(bt), bts, ctypes.c_void_p(sl), msl, sm,
+                                                  ctypes.c_void_p(out), None)
+
+
+def test_noalloc_decode_checks_and_limit():
+    """The allocation-free decode checks its arguments like nvfp4_paged_decode_attn
+    and rejects calls whose partials exceed its 8 MiB scratch, all before any HIP call."""
+    nk = _lib()
+    L = _layer(nk)
+    assert _decode_noalloc(nk, L, Hq=60) == 1
+    assert _decode_noalloc(nk, L, Hq=8 * 17) == 2
+    assert _decode_noalloc(nk, L, qdt=3) == 1
+    assert _decode_noalloc(nk, L, B=0, q=0, bt=0, sl=0, out=0) == 0  # empty batch: nothing enqueued
+    assert _decode_noalloc(nk, L, q=0) == 1
+    assert _decode_noalloc(nk, L, out=0) == 1
+    assert _decode_noalloc(nk, L, bts=3) == 1
+    assert _decode_noalloc(nk, L, sm=float("inf")) == 1
+    assert _decode_noalloc(nk, L, q=FAKE + 2) == 2
+
+    # the limit: partials = workspace bytes past the counters <= 8 MiB - 64 KiB
+    def partial_bytes(B, Hq, msl):
+        return nk.decode_workspace_bytes(B, Hq, 8, msl) - (B * 8 * 4 + 255) // 256 * 256
+    limit = (8 << 20) - (64 << 10)
+    ok_b = max(b for b in range(1, 1024) if partial_bytes(b, 64, 8192) <= limit)
+    assert ok_b >= 200  # about 218 sequences of 8 kv heads at 8 q heads per kv head
+    assert _decode_noalloc(nk, L, B=ok_b + 1, Hq=64, msl=8192, bts=512) == 3
+    assert _decode_noalloc(nk, L, B=4096, Hq=128, msl=64, bts=4) == 3  # too many units for the counters
