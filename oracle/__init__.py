@@ -58,6 +58,10 @@ def lib():
     L.nvfp4o_quantize_rows.restype = None
     L.nvfp4o_dequantize_rows.argtypes = [_u8p, _u8p, _i64, _flt, _f64p]
     L.nvfp4o_dequantize_rows.restype = None
+    L.nvfp4o_mla_quantize_rows.argtypes = [_f32p, _i64, _flt, _u8p, _u8p]
+    L.nvfp4o_mla_quantize_rows.restype = None
+    L.nvfp4o_mla_sparse_decode.argtypes = [_u8p, _u8p, _i64, _flt, _f32p, _i64, _int, _i32p, _int, _flt, _f64p]
+    L.nvfp4o_mla_sparse_decode.restype = None
     L.nvfp4o_scatter_rows.argtypes = [_u8p, _u8p, _i64, _int, _i32p, _int, _u8p, _u8p]
     L.nvfp4o_scatter_rows.restype = None
     L.nvfp4o_gather_rows.argtypes = [_u8p, _u8p, _i64, _int, _i32p, _int, _u8p, _u8p]
@@ -344,6 +348,69 @@ def rotate_k(k) -> np.ndarray:
 def rotate_q(q) -> np.ndarray:
     """Queries as the rotated decode uses them: H q / 8 (float64)."""
     return hadamard_rows(q, Q_ROT_SCALE)
+
+
+# ---------------------------------------------------- Sparse-MLA latent cache
+MLA_D = 576          # latent (512) + rotary key (64) values per token row
+MLA_DV = 512         # values the output sums (the latent part)
+MLA_CODE_BYTES = MLA_D // 2
+MLA_SCALE_BYTES = MLA_D // 16
+
+
+class MlaPlanes:
+    """The oracle's latent cache: codes [num_slots][288], scales [num_slots][36]."""
+
+    def __init__(self, num_slots: int):
+        self.num_slots = int(num_slots)
+        self.codes = np.zeros((self.num_slots, MLA_CODE_BYTES), np.uint8)
+        self.scales = np.zeros((self.num_slots, MLA_SCALE_BYTES), np.uint8)
+
+
+def mla_quantize_rows(x, g: float):
+    """Latent rows float32 [n, 576] -> (codes [n, 288], scales [n, 36])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.ndim == 2 and x.shape[1] == MLA_D
+    n = x.shape[0]
+    codes = np.zeros((n, MLA_CODE_BYTES), np.uint8)
+    scales = np.zeros((n, MLA_SCALE_BYTES), np.uint8)
+    lib().nvfp4o_mla_quantize_rows(x, n, float(np.float32(g)), codes, scales)
+    return codes, scales
+
+
+def mla_quantize_append(planes: MlaPlanes, x, slots, g: float) -> None:
+    """Quantize rows x [n, 576] into their slots (slots outside the cache are skipped)."""
+    codes, scales = mla_quantize_rows(x, g)
+    slots = np.asarray(slots, np.int64)
+    ok = (slots >= 0) & (slots < planes.num_slots)
+    planes.codes[slots[ok]] = codes[ok]
+    planes.scales[slots[ok]] = scales[ok]
+
+
+def mla_dequantize_rows(codes, scales, g: float) -> np.ndarray:
+    """codes [n, 288], scales [n, 36] -> float64 [n, 576] through the GQA row
+    dequantizer (a 576-row is 36 independent 16-value blocks)."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    n = codes.shape[0]
+    pc = np.zeros((n, 320), np.uint8)
+    psc = np.zeros((n, 40), np.uint8)
+    pc[:, :MLA_CODE_BYTES] = codes
+    psc[:, :MLA_SCALE_BYTES] = scales
+    out = dequantize_rows(pc.reshape(n * 5, 64), psc.reshape(n * 5, 8), g).reshape(n, 640)
+    return out[:, :MLA_D]
+
+
+def mla_sparse_decode(planes: MlaPlanes, g: float, q, indices, sm_scale: float) -> np.ndarray:
+    """q float32 [T, Hq, 576], indices int32 [T, topk] (cache slots) -> float64 [T, Hq, 512]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    T, Hq, D = q.shape
+    assert D == MLA_D
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    assert idx.ndim == 2 and idx.shape[0] == T
+    out = np.zeros((T, Hq, MLA_DV), np.float64)
+    lib().nvfp4o_mla_sparse_decode(planes.codes, planes.scales, planes.num_slots, float(np.float32(g)), q, T, Hq,
+                                   idx, idx.shape[1], float(np.float32(sm_scale)), out)
+    return out
 
 
 # ------------------------------------------ the page's two-level comparison

@@ -124,31 +124,31 @@ int nvfp4o_e2m1_encode(double y) {
  *   scales: n_rows x 8 bytes, byte b = E4M3 scale of values 16b..16b+15 (R6)
  * Per block: amax = max|x|, bs = E4M3(amax/(6g)) (R2), each code = sign(x) |
  * E2M1(|x|/(bs*g)) (R1, R3, R5), zero scale -> magnitude 0 (R8). */
+/* One 16-value block: its E4M3 scale byte and its 16 codes, ORed into the 8
+ * code bytes cb (which start at zero). */
+static void quantize_block16(const float* xb, double gd, uint8_t* cb, uint8_t* sb) {
+  double amax = 0.0;
+  for (int i = 0; i < 16; ++i) {
+    double a = fabs((double)xb[i]);
+    if (a > amax) amax = a;
+  }
+  int sbyte = nvfp4o_e4m3_encode(amax / (6.0 * gd));
+  double bs = nvfp4o_e4m3_value(sbyte);
+  *sb = (uint8_t)sbyte;
+  for (int i = 0; i < 16; ++i) {
+    double v = (double)xb[i];
+    int mag = (bs == 0.0) ? 0 : nvfp4o_e2m1_encode(fabs(v) / (bs * gd));
+    int code = (signbit(v) ? 8 : 0) | mag;
+    cb[i / 2] |= (uint8_t)(code << (4 * (i & 1)));
+  }
+}
+
 void nvfp4o_quantize_rows(const float* x, int64_t n_rows, float g, uint8_t* codes, uint8_t* scales) {
   const double gd = (double)g;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n_rows; ++r) {
-    const float* xr = x + r * 128;
-    uint8_t* cr = codes + r * 64;
-    uint8_t* sr = scales + r * 8;
-    memset(cr, 0, 64);
-    for (int b = 0; b < 8; ++b) {
-      double amax = 0.0;
-      for (int i = 0; i < 16; ++i) {
-        double a = fabs((double)xr[16 * b + i]);
-        if (a > amax) amax = a;
-      }
-      int sb = nvfp4o_e4m3_encode(amax / (6.0 * gd));
-      double bs = nvfp4o_e4m3_value(sb);
-      sr[b] = (uint8_t)sb;
-      for (int i = 0; i < 16; ++i) {
-        int d = 16 * b + i;
-        double v = (double)xr[d];
-        int mag = (bs == 0.0) ? 0 : nvfp4o_e2m1_encode(fabs(v) / (bs * gd));
-        int code = (signbit(v) ? 8 : 0) | mag;
-        cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
-      }
-    }
+    memset(codes + r * 64, 0, 64);
+    for (int b = 0; b < 8; ++b) quantize_block16(x + r * 128 + 16 * b, gd, codes + r * 64 + 8 * b, scales + r * 8 + b);
   }
 }
 
@@ -547,6 +547,86 @@ void nvfp4o_hadamard_rows(const double* x, int64_t n_rows, double scale, double*
       for (int j = 0; j < 128; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -xr[j] : xr[j];
       out[r * 128 + i] = scale * acc;
     }
+  }
+}
+
+/* ------------------------------------------------- Sparse-MLA latent cache
+ * [MW] §6 closing note: the serving engine's NVFP4 KV cache supports GQA and
+ * Sparse MLA models.  The pages say nothing more; the readings (also in the
+ * design notes):
+ *   M1 an MLA cache holds one latent row per token, shared by every query
+ *      head: 512 latent values followed by 64 rotary-key values (the
+ *      DeepSeek-V3-class shape).  Scores use all 576 values; the output is the
+ *      softmax-weighted sum of the first 512 (decode with the key and value
+ *      up-projections absorbed into the query and the output projection).
+ *   M2 the row is stored as NVFP4 with the GQA cache's rule: 36 blocks of 16
+ *      consecutive values, E4M3 scale per block, one FP32 global scale g per
+ *      layer (readings R1..R8 apply block by block).
+ *   M3 "sparse": each query token attends only to a given list of cached
+ *      tokens (its top-k selection, made outside this path).  List entries
+ *      are cache slots; an entry outside [0, num_slots) is skipped; an entry
+ *      listed twice counts twice.
+ *   M4 layout: codes [num_slots][288] (byte j = values 2j, 2j+1, low nibble
+ *      first), scales [num_slots][36] (byte b = E4M3 scale of values
+ *      16b..16b+15); a slot is page * page_size + offset for any page size. */
+
+#define MLA_D 576
+#define MLA_DV 512
+
+/* Latent rows [n_rows][576] -> codes [n_rows][288], scales [n_rows][36] (M2, M4). */
+void nvfp4o_mla_quantize_rows(const float* x, int64_t n_rows, float g, uint8_t* codes, uint8_t* scales) {
+  const double gd = (double)g;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    memset(codes + r * (MLA_D / 2), 0, MLA_D / 2);
+    for (int b = 0; b < MLA_D / 16; ++b)
+      quantize_block16(x + r * MLA_D + 16 * b, gd, codes + r * (MLA_D / 2) + 8 * b, scales + r * (MLA_D / 16) + b);
+  }
+}
+
+/* Value d of the latent row in slot s: E2M1 * E4M3 * g, exact in float64. */
+static double mla_value(const uint8_t* pc, const uint8_t* ps, int64_t s, int d, double g) {
+  int code = (pc[s * (MLA_D / 2) + d / 2] >> (4 * (d & 1))) & 15;
+  return nvfp4o_e2m1_value(code) * nvfp4o_e4m3_value(ps[s * (MLA_D / 16) + d / 16]) * g;
+}
+
+/* Sparse MLA decode (M1, M3): for query token t < T and head h < Hq, with the
+ * valid entries j of indices[t][0..topk):
+ *   s_j = sm_scale * sum_{d<576} q[t][h][d] * K_hat[slot_j][d]
+ *   out[t][h][d] = sum_j softmax(s)_j * K_hat[slot_j][d],  d < 512
+ * in float64; no valid entry gives zeros.  q: [T][Hq][576], out: [T][Hq][512]. */
+void nvfp4o_mla_sparse_decode(const uint8_t* pc, const uint8_t* ps, int64_t num_slots, float g, const float* q,
+                              int64_t T, int Hq, const int32_t* indices, int topk, float sm_scale, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t th = 0; th < T * Hq; ++th) {
+    const int64_t t = th / Hq;
+    const float* qr = q + th * MLA_D;
+    double* o = out + th * MLA_DV;
+    for (int d = 0; d < MLA_DV; ++d) o[d] = 0.0;
+    double* sc = (double*)malloc((size_t)(topk > 0 ? topk : 1) * sizeof(double));
+    double m = -INFINITY;
+    int any = 0;
+    for (int j = 0; j < topk; ++j) {
+      const int64_t s = indices[t * topk + j];
+      if (s < 0 || s >= num_slots) continue;
+      double acc = 0.0;
+      for (int d = 0; d < MLA_D; ++d) acc += (double)qr[d] * mla_value(pc, ps, s, d, (double)g);
+      sc[j] = (double)sm_scale * acc;
+      if (sc[j] > m) m = sc[j];
+      any = 1;
+    }
+    if (any) {
+      double l = 0.0;
+      for (int j = 0; j < topk; ++j) {
+        const int64_t s = indices[t * topk + j];
+        if (s < 0 || s >= num_slots) continue;
+        const double w = exp(sc[j] - m);
+        l += w;
+        for (int d = 0; d < MLA_DV; ++d) o[d] += w * mla_value(pc, ps, s, d, (double)g);
+      }
+      for (int d = 0; d < MLA_DV; ++d) o[d] /= l;
+    }
+    free(sc);
   }
 }
 
