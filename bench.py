@@ -665,7 +665,71 @@ def bench_uniform(args, wl, dev):
         del rot_layers
     result["hadamard_k"] = hadamard
     print("[bench] Hadamard-rotated layers timed", file=sys.stderr, flush=True)
+    result["sparse_mla"] = bench_mla(args, dev)
     return result
+
+
+def bench_mla(args, dev):
+    """Sparse MLA over the NVFP4 latent cache at a DeepSeek-V3.2-class decode
+    shape (128 query tokens, one per sequence; latent rows of 512 + 64 values;
+    top-2048 of each sequence's 32,768 cached tokens; 64-token pages in random
+    order; 4 layer caches rotated, so the touched rows exceed the 256 MB
+    Infinity Cache): bulk quantize-append, and the sparse decode at 128 and at
+    16 heads per query token (the second: one tensor-parallel shard of 8)."""
+    import torch
+
+    import nvfp4_quantized_paged_kv_amd as nk
+    from synthetic import synth
+    from synthetic.workloads import MLA_CHUNK, MLA_OUTLIERS, MLA_SHAPE, build_mla_layer, mla_slots
+
+    sh = MLA_SHAPE
+    T, ctx, topk, page, L = sh["T"], sh["ctx"], sh["topk"], sh["page"], sh["layers"]
+    n_slots = T * ctx
+    stream = torch.cuda.current_stream()
+    filled = [build_mla_layer(l, dev, timed=True) for l in range(L)]
+    print("[bench] sparse-MLA layers filled", file=sys.stderr, flush=True)
+    sm = 1 / math.sqrt(192)
+    res = {"workload": f"sparse MLA decode: {T} query tokens, 576/512 latent rows, top-{topk} of {ctx}-token "
+                       f"contexts, {page}-token pages, {L} rotated layers"}
+    # bulk append: the first fill chunk re-appended into its own slots, back to back, alternating over two layers
+    rows_b = [synth.mla_rows(MLA_CHUNK, MLA_OUTLIERS, torch.bfloat16, dev, 60, l, 0) for l in range(2)]
+    tok = torch.arange(0, MLA_CHUNK, device=dev)
+    slots_b = [mla_slots(filled[l].block_table, tok, ctx, page) for l in range(2)]
+    app_s = back_to_back(stream, args.steps, lambda i: nk.mla_quantize_append(filled[i % 2].layer, rows_b[i % 2],
+                                                                              slots_b[i % 2]))
+    per_tok = 576 * 2 + 324 + 4
+    app_gbs = MLA_CHUNK * per_tok / app_s / 1e9
+    res["append_us"] = round(app_s * 1e6, 2)
+    res["append_roofline"] = {"bound": "hbm", "achieved": round(app_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(app_gbs / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes_per_call": int(MLA_CHUNK * per_tok), "tokens_per_call": MLA_CHUNK}
+    app_ms = [m for f in filled for m in f.append_ms]
+    res["append_gbs_single_call"] = round(n_slots * L * per_tok / (sum(app_ms) / 1e3) / 1e9, 2)
+    for Hq in (128, 16):
+        qs = [synth.mla_queries(T, Hq, torch.bfloat16, dev, 63, l) for l in range(L)]
+        out = torch.empty((T, Hq, 512), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(nk.mla_sparse_decode_workspace_bytes(T, Hq, topk), 256), dtype=torch.uint8, device=dev)
+
+        def call(i):
+            l = i % L
+            nk.mla_sparse_decode(filled[l].layer, qs[l], filled[l].indices, sm, out=out, workspace=ws)
+        for i in range(max(args.warmup, L)):
+            call(i)
+        spread_s = []
+        dec_s = back_to_back(stream, args.steps, call, spread_out=spread_s)
+        flops = T * Hq * topk * 2 * (576 + 512)
+        byts = T * topk * (324 + 4) + T * Hq * (576 * 2 + 512 * 4)
+        tf = flops / dec_s / 1e12
+        gbs = byts / dec_s / 1e9
+        res[f"decode_heads{Hq}"] = {
+            "us": round(dec_s * 1e6, 3), "us_windows": spread(spread_s, 1e6),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_F16_TFLOPS, 4), "flops_per_call": int(flops)},
+            "hbm": {"achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_call": int(byts)},
+            "workspace_bytes": int(ws.numel())}
+    print("[bench] sparse-MLA decode timed", file=sys.stderr, flush=True)
+    return res
 
 
 def calibration_kernel():

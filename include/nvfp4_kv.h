@@ -391,6 +391,69 @@ NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn_hadamard(const mxfp4_kv_layer_t
                                                           float* out, void* workspace, size_t workspace_bytes,
                                                           void* stream);
 
+/* ------------------------------------------------- Sparse-MLA latent cache
+ * grer.cn blog "NVFP4 KV cache and the memory wall", section 6 (closing
+ * note): the serving engine's NVFP4 KV cache supports GQA and Sparse MLA
+ * models.  An MLA cache holds one latent row per token, shared by every query
+ * head: 512 latent values followed by 64 rotary-key values.  Rows are stored
+ * as NVFP4 with the rule of nvfp4_kv_quantize_append applied to 36 blocks of
+ * 16 consecutive values (one E4M3 scale per block, one FP32 global scale per
+ * layer): 324 bytes per token, 9/16 byte per value.
+ * Layout (slot s = page * page_size + offset, for any page size):
+ *   codes  [num_slots][288] u8: byte j of a row holds values 2j (low nibble)
+ *          and 2j+1 (high nibble).
+ *   scales [num_slots][36]  u8: byte b = E4M3 scale of values 16b .. 16b+15.
+ * A value reads back as E2M1(code) * E4M3(scale) * global_scale. */
+typedef struct nvfp4_mla_layer {
+  uint8_t* codes;      /* 16-byte aligned */
+  uint8_t* scales;     /* 4-byte aligned */
+  int32_t num_slots;
+  int32_t latent_dim;  /* must be 512 */
+  int32_t rope_dim;    /* must be 64 */
+  float global_scale;  /* finite, 2^-100 <= g <= 2^100 */
+} nvfp4_mla_layer_t;
+
+/* Quantize-on-append of latent rows (blog section 3, first data flow, for the
+ * MLA cache): row t < num_tokens of kv_new ([num_tokens][576] of dtype,
+ * token_stride_elems >= 576 apart, 16-byte aligned base and stride, finite
+ * values) goes to slot slot_mapping[t]; slots < 0 or >= num_slots are
+ * skipped; the rounding is that of nvfp4_kv_quantize_append, block by block.
+ * num_tokens == 0 is a no-op.  Supported: num_tokens * 18 < 2^31 * 256. */
+NVFP4_API nvfp4_status_t nvfp4_mla_quantize_append(const nvfp4_mla_layer_t* layer, const void* kv_new,
+                                                   nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                   const int32_t* slot_mapping, void* stream);
+
+/* Bytes of device workspace nvfp4_mla_sparse_decode needs (host sizes): the
+ * partial results of lists that the call splits over several workgroups (it
+ * does so when few query tokens would leave CUs idle).  0 when no list is
+ * split (the call then takes no workspace), for num_q_tokens == 0, and for
+ * sizes the call rejects. */
+NVFP4_API size_t nvfp4_mla_sparse_decode_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads, int32_t topk);
+
+/* Sparse MLA decode over the NVFP4 latent cache (blog section 3, third data
+ * flow, dequantizing inside the kernel; section 6: Sparse MLA).  For query
+ * token t < num_q_tokens and head h < num_q_heads, over the entries j <
+ * topk of indices[t][0..topk) that are cache slots (entries < 0 or >=
+ * num_slots are skipped; an entry listed twice counts twice):
+ *   s_j = sm_scale * sum_{d<576} q[t][h][d] * K_hat[slot_j][d]
+ *   out[t][h][d] = sum_j softmax(s)_j * K_hat[slot_j][d],  d < 512 (fp32 accumulate)
+ * A token with no valid entry gets zeros.  Dequantized values are exact in f16;
+ * the products run on f16 MFMA, P as an f16 hi + lo pair.
+ *   q       : [num_q_tokens][num_q_heads][576] bf16 (q_dtype must be BF16), 16-byte aligned.
+ *   indices : [num_q_tokens][topk] int32 cache slots.
+ *   out     : [num_q_tokens][num_q_heads][512] float32.
+ *   workspace: >= nvfp4_mla_sparse_decode_workspace_bytes(...) bytes, 256-byte
+ *            aligned, when that is not 0 (else ignored; may be NULL): the
+ *            partial results of split lists, written and merged by the call (a
+ *            second launch on `stream`); no initial contents needed; calls
+ *            that share it must be ordered on one stream.
+ *   Supported: num_q_heads a multiple of 16, and of 64 above 64; topk <= 2^20;
+ *   q_dtype BF16.  Others return NVFP4_ERR_UNSUPPORTED. */
+NVFP4_API nvfp4_status_t nvfp4_mla_sparse_decode(const nvfp4_mla_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t num_q_tokens, int32_t num_q_heads, const int32_t* indices,
+                                                 int32_t topk, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream);
+
 /* Static string for a status code. */
 NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 

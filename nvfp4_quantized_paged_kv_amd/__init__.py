@@ -52,6 +52,9 @@ EXPORTED_SYMBOLS = (
     "nvfp4_paged_decode_attn_hadamard",
     "mxfp4_kv_quantize_append_hadamard",
     "mxfp4_paged_decode_attn_hadamard",
+    "nvfp4_mla_quantize_append",
+    "nvfp4_mla_sparse_decode_workspace_bytes",
+    "nvfp4_mla_sparse_decode",
     "nvfp4_status_string",
 )
 
@@ -85,6 +88,19 @@ class CMxLayer(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
+    ]
+
+
+class CMlaLayer(ctypes.Structure):
+    """Mirror of ``nvfp4_mla_layer_t``."""
+
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32),
+        ("latent_dim", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("global_scale", ctypes.c_float),
     ]
 
 
@@ -138,6 +154,13 @@ def _load():
     for f in ("nvfp4_kv_quantize_append_hadamard", "nvfp4_paged_decode_attn_hadamard",
               "mxfp4_kv_quantize_append_hadamard", "mxfp4_paged_decode_attn_hadamard"):
         getattr(L, f).restype = ctypes.c_int
+    mlp = ctypes.POINTER(CMlaLayer)
+    L.nvfp4_mla_quantize_append.argtypes = [mlp, vp, ctypes.c_int, i32, i64, vp, vp]
+    L.nvfp4_mla_quantize_append.restype = ctypes.c_int
+    L.nvfp4_mla_sparse_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    L.nvfp4_mla_sparse_decode_workspace_bytes.restype = sz
+    L.nvfp4_mla_sparse_decode.argtypes = [mlp, vp, ctypes.c_int, i32, i32, vp, i32, f32, vp, vp, sz, vp]
+    L.nvfp4_mla_sparse_decode.restype = ctypes.c_int
     L.nvfp4_status_string.argtypes = [ctypes.c_int]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     return L
@@ -518,4 +541,77 @@ def mx_paged_decode_attn(layer: MxKVCacheLayer, q: torch.Tensor, block_table: to
                             _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
                             float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, name)
+    return out
+
+
+# --------------------------------------------------- Sparse-MLA latent cache
+MLA_DIM = 576            # latent (512) + rotary key (64) values per token row
+MLA_LATENT = 512
+MLA_ROW_CODE_BYTES = 288
+MLA_ROW_SCALE_BYTES = 36
+
+
+@dataclass
+class MlaCacheLayer:
+    """One layer's NVFP4 latent cache: codes [num_slots, 288] and scales [num_slots, 36] (device)."""
+
+    codes: torch.Tensor
+    scales: torch.Tensor
+    num_slots: int
+    global_scale: float
+
+    @staticmethod
+    def allocate(num_slots: int, global_scale: float, device="cuda") -> "MlaCacheLayer":
+        n = int(num_slots)
+        return MlaCacheLayer(torch.zeros((n, MLA_ROW_CODE_BYTES), dtype=torch.uint8, device=device),
+                             torch.zeros((n, MLA_ROW_SCALE_BYTES), dtype=torch.uint8, device=device),
+                             n, float(global_scale))
+
+    def c_struct(self) -> CMlaLayer:
+        return CMlaLayer(self.codes.data_ptr(), self.scales.data_ptr(), self.num_slots, MLA_LATENT,
+                         MLA_DIM - MLA_LATENT, self.global_scale)
+
+
+def mla_quantize_append(layer: MlaCacheLayer, kv: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Quantize latent rows kv [T, 576] (bf16/f32, token-strided) into their slots."""
+    if kv.dim() != 2 or kv.shape[1] != MLA_DIM or kv.stride(1) != 1:
+        raise ValueError("kv must be [T, 576] with contiguous rows")
+    _dev_i32(slot_mapping, "slot_mapping")
+    if slot_mapping.numel() != kv.shape[0]:
+        raise ValueError("slot_mapping must have one entry per token")
+    c = layer.c_struct()
+    T = kv.shape[0]
+    st = lib.nvfp4_mla_quantize_append(ctypes.byref(c), _ptr(kv), _dtype_code(kv), T,
+                                       kv.stride(0) if T > 0 else MLA_DIM, _ptr(slot_mapping), _stream(stream))
+    _check(st, "nvfp4_mla_quantize_append")
+
+
+def mla_sparse_decode_workspace_bytes(num_q_tokens: int, num_q_heads: int, topk: int) -> int:
+    return int(lib.nvfp4_mla_sparse_decode_workspace_bytes(num_q_tokens, num_q_heads, topk))
+
+
+def mla_sparse_decode(layer: MlaCacheLayer, q: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Sparse MLA decode of q [T, Hq, 576] (bf16) over the cache slots indices [T, topk];
+    returns f32 [T, Hq, 512]."""
+    if q.dim() != 3 or q.shape[2] != MLA_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [T, Hq, 576] tensor")
+    T, Hq, _ = q.shape
+    _dev_i32(indices, "indices")
+    if indices.dim() != 2 or indices.shape[0] != T:
+        raise ValueError("indices must be [T, topk]")
+    if out is None:
+        out = torch.empty((T, Hq, MLA_LATENT), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (T, Hq, MLA_LATENT):
+        raise ValueError("out must be a contiguous float32 [T, Hq, 512] tensor")
+    need = mla_sparse_decode_workspace_bytes(T, Hq, indices.shape[1])
+    if workspace is None and need > 0:  # partials of split lists: no initial contents needed
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = layer.c_struct()
+    st = lib.nvfp4_mla_sparse_decode(ctypes.byref(c), _ptr(q), _dtype_code(q), T, Hq, _ptr(indices),
+                                     indices.shape[1], float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+    _check(st, "nvfp4_mla_sparse_decode")
     return out

@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "decode_noalloc.h"
+#include "mla_internal.h"
 #include "nvfp4_kv.h"
 #include "nvfp4_kv_internal.h"
 
@@ -483,6 +484,103 @@ NVFP4_API nvfp4_status_t mxfp4_paged_decode_attn_hadamard(const mxfp4_kv_layer_t
                                                           void* stream) {
   return mx_decode_impl(layer, q, q_dtype, batch, num_q_heads, block_table, block_table_stride, seq_lens, max_seq_len,
                         sm_scale, out, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------ Sparse-MLA latent cache
+
+namespace {
+
+nvfp4_status_t check_mla_layer(const nvfp4_mla_layer_t* L) {
+  if (L == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (L->latent_dim != kMlaLatent || L->rope_dim != kMlaDim - kMlaLatent) return NVFP4_ERR_UNSUPPORTED;
+  if (!L->codes || !L->scales || L->num_slots <= 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(L->codes, 16) || !aligned(L->scales, 4)) return NVFP4_ERR_UNSUPPORTED;
+  if (!scale_ok(L->global_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t nvfp4_mla_quantize_append(const nvfp4_mla_layer_t* layer, const void* kv_new,
+                                                   nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
+                                                   const int32_t* slot_mapping, void* stream) {
+  const nvfp4_status_t st = check_mla_layer(layer);
+  if (st != NVFP4_OK) return st;
+  if (!dtype_ok(dtype) || num_tokens < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return NVFP4_OK;
+  if (!kv_new || !slot_mapping) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (token_stride_elems < kMlaDim) return NVFP4_ERR_INVALID_ARGUMENT;
+  const int64_t esize = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(kv_new, 16) || (token_stride_elems * esize) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  MlaAppendParams p;
+  p.x = kv_new;
+  p.codes = layer->codes;
+  p.scales = layer->scales;
+  p.slots = slot_mapping;
+  p.token_stride = token_stride_elems;
+  p.num_tokens = num_tokens;
+  p.num_slots = layer->num_slots;
+  p.g = layer->global_scale;
+  p.r6 = 1.0 / (6.0 * (double)layer->global_scale);
+  return from_hip(launch_mla_append(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+static bool mla_shape_ok(int32_t num_q_tokens, int32_t num_q_heads, int32_t topk) {
+  if (num_q_tokens < 0 || num_q_heads <= 0 || topk < 0) return false;
+  if (num_q_heads % 16 != 0 || (num_q_heads > 64 && num_q_heads % 64 != 0)) return false;
+  if (topk > (1 << 20)) return false;
+  return true;
+}
+
+NVFP4_API size_t nvfp4_mla_sparse_decode_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads, int32_t topk) {
+  if (!mla_shape_ok(num_q_tokens, num_q_heads, topk) || num_q_tokens == 0) return 0;
+  const MlaGeometry geo = mla_geometry(num_q_tokens, num_q_heads, topk);
+  if (geo.waves == 0 || (int64_t)num_q_tokens * geo.HB * geo.splits >= ((int64_t)1 << 31)) return 0;
+  return geo.workspace_bytes;
+}
+
+NVFP4_API nvfp4_status_t nvfp4_mla_sparse_decode(const nvfp4_mla_layer_t* layer, const void* q, nvfp4_dtype_t q_dtype,
+                                                 int32_t num_q_tokens, int32_t num_q_heads, const int32_t* indices,
+                                                 int32_t topk, float sm_scale, float* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  const nvfp4_status_t st = check_mla_layer(layer);
+  if (st != NVFP4_OK) return st;
+  if (!dtype_ok(q_dtype) || num_q_tokens < 0 || num_q_heads <= 0 || topk < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (q_dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_UNSUPPORTED;
+  if (!mla_shape_ok(num_q_tokens, num_q_heads, topk)) return NVFP4_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return NVFP4_ERR_INVALID_ARGUMENT;
+  const double qk = (double)sm_scale * (double)layer->global_scale * 1.4426950408889634;  // log2(e)
+  if (!std::isfinite(qk) || !std::isfinite((float)qk)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_q_tokens == 0) return NVFP4_OK;
+  if (!q || !out || (topk > 0 && !indices)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16)) return NVFP4_ERR_UNSUPPORTED;
+  const MlaGeometry geo = mla_geometry(num_q_tokens, num_q_heads, topk);
+  if (geo.waves == 0 || (int64_t)num_q_tokens * geo.HB * geo.splits >= ((int64_t)1 << 31)) return NVFP4_ERR_UNSUPPORTED;
+  if (geo.workspace_bytes > 0) {  // some list is split: the shares' partials
+    if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARGUMENT;
+  }
+  MlaDecodeParams p;
+  p.codes = layer->codes;
+  p.scales = layer->scales;
+  p.q = q;
+  p.indices = indices;
+  p.out = out;
+  p.part = static_cast<float*>(workspace);
+  p.num_slots = layer->num_slots;
+  p.T = num_q_tokens;
+  p.Hq = num_q_heads;
+  p.topk = topk;
+  p.HB = geo.HB;
+  p.splits = geo.splits;
+  p.per_split = geo.per_split;
+  p.qk_scale_log2 = (float)qk;
+  p.v_scale = layer->global_scale;
+  return from_hip(launch_mla_decode(p, geo.waves, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -180,3 +180,50 @@ def slots_for(bt_row: np.ndarray, start: int, n: int) -> np.ndarray:
     """Slots of tokens start..start+n-1 of one sequence."""
     t = np.arange(start, start + n, dtype=np.int64)
     return (bt_row[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+
+
+# ------------------------------------------------------- Sparse-MLA latent cache
+# Stand-in for a DeepSeek-V3.2-class sparse-MLA decode: every token caches one
+# latent row (512 latent + 64 rotary-key values) shared by all query heads; each
+# query token attends to a top-k list of positions of its own sequence (the
+# selection itself is made outside this path: here a seeded uniform draw of
+# distinct positions).  Values follow the pages' cache distribution.
+MLA_DIM = 576
+MLA_LATENT = 512
+
+
+def mla_rows(n_tokens: int, outlier_frac: float, dtype: torch.dtype, device, *seed_parts: int) -> torch.Tensor:
+    """Latent rows [n_tokens, 576] in `dtype`: N(0, 0.02) with a fraction of +-6.0 entries."""
+    g = generator(device, *seed_parts, 55)
+    x = torch.randn((n_tokens, MLA_DIM), generator=g, device=device, dtype=torch.float32) * 0.02
+    if outlier_frac > 0:
+        u = torch.rand((n_tokens, MLA_DIM), generator=g, device=device)
+        sign = torch.where(torch.rand((n_tokens, MLA_DIM), generator=g, device=device) < 0.5, -6.0, 6.0)
+        x = torch.where(u < outlier_frac, sign, x)
+    return x.to(dtype)
+
+
+def mla_queries(T: int, Hq: int, dtype: torch.dtype, device, *seed_parts: int) -> torch.Tensor:
+    """Absorbed queries [T, Hq, 576] ~ N(0, 1)."""
+    g = generator(device, *seed_parts, 56)
+    return torch.randn((T, Hq, MLA_DIM), generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def mla_topk_positions(T: int, lens, topk: int, device, *seed_parts: int) -> torch.Tensor:
+    """Per query token t: min(topk, lens[t]) distinct positions of [0, lens[t]) in random order,
+    padded with -1 to topk entries; int64 [T, topk]."""
+    g = generator(device, *seed_parts, 57)
+    out = torch.full((T, topk), -1, dtype=torch.int64, device=device)
+    for t in range(T):
+        n = int(lens[t])
+        k = min(topk, n)
+        if k > 0:
+            out[t, :k] = torch.randperm(n, generator=g, device=device)[:k]
+    return out
+
+
+def slots_of_positions(pos: torch.Tensor, block_table: torch.Tensor, page: int) -> torch.Tensor:
+    """Cache slots of positions pos [T, k] (-1 stays -1) through block_table [T, width] of `page`-token pages."""
+    p = pos.clamp(min=0)
+    pages = torch.gather(block_table.to(torch.int64), 1, p // page)
+    return torch.where(pos >= 0, pages * page + p % page, torch.full_like(pos, -1)).to(torch.int32)

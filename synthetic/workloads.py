@@ -136,3 +136,65 @@ def build_mixed_step(wl: synth.Workload, layer_idx: int, device="cuda", on_chunk
         ext_q=synth.queries(ext.size * chunk, wl.q_heads, wl.in_dtype, device, 5, layer_idx),
         ext_q_offsets=torch.from_numpy((np.arange(ext.size + 1) * chunk).astype(np.int32)).to(device),
         max_dec_len=int(dec_lens.max()), max_prefix=int(prefix.max()), ext_chunk=chunk)
+
+
+# ------------------------------------------------------- Sparse-MLA latent cache
+# DeepSeek-V3.2-class sparse-MLA decode: T query tokens (one per sequence),
+# each sequence holds ctx cached tokens in `page`-token pages of a seeded random
+# permutation; each query token attends to topk distinct positions of its own
+# sequence.
+MLA_SHAPE = dict(T=128, Hq=128, ctx=32768, topk=2048, page=64, layers=4)
+MLA_CHUNK = 1 << 17
+MLA_OUTLIERS = 0.002
+
+
+@dataclass
+class MlaFilled:
+    layer: object               # nvfp4_quantized_paged_kv_amd.MlaCacheLayer
+    block_table: torch.Tensor   # [T, ctx / page] int64 page indices
+    indices: torch.Tensor       # [T, topk] int32 cache slots of each query token's list
+    append_ms: list             # per-chunk append durations (HIP events), if timed
+
+
+def mla_slots(bt: torch.Tensor, tok: torch.Tensor, ctx: int, page: int) -> torch.Tensor:
+    """Cache slots of flattened token indices tok (sequence tok // ctx, position tok % ctx)."""
+    pos = tok % ctx
+    return (bt[tok // ctx, pos // page] * page + pos % page).to(torch.int32)
+
+
+def build_mla_layer(layer_idx: int, device="cuda", shape=None, on_chunk=None, timed: bool = False) -> MlaFilled:
+    """Fill one layer's latent cache by bulk quantize-append of seeded rows,
+    chunk by chunk in (sequence, position) order.  on_chunk(c0, rows) sees every
+    generated chunk (rows [n, 576] bf16 of tokens c0 .. c0+n-1)."""
+    from nvfp4_quantized_paged_kv_amd import MlaCacheLayer, mla_quantize_append
+
+    sh = dict(MLA_SHAPE if shape is None else shape)
+    T, ctx, topk, page = sh["T"], sh["ctx"], sh["topk"], sh["page"]
+    n_slots = T * ctx
+    amax = 0.0
+    for c0 in range(0, n_slots, MLA_CHUNK):
+        rows = synth.mla_rows(min(MLA_CHUNK, n_slots - c0), MLA_OUTLIERS, torch.bfloat16, device, 60, layer_idx, c0)
+        amax = max(amax, float(rows.float().abs().max()))
+    layer = MlaCacheLayer.allocate(n_slots, synth.global_scale(amax), device)
+    perm = np.random.default_rng(synth.seed_of(layer_idx, 61)).permutation(n_slots // page).astype(np.int64)
+    bt = torch.from_numpy(perm).to(device).reshape(T, ctx // page)
+    stream = torch.cuda.current_stream()
+    ms = []
+    for c0 in range(0, n_slots, MLA_CHUNK):
+        n = min(MLA_CHUNK, n_slots - c0)
+        rows = synth.mla_rows(n, MLA_OUTLIERS, torch.bfloat16, device, 60, layer_idx, c0)
+        slots = mla_slots(bt, torch.arange(c0, c0 + n, device=device), ctx, page)
+        if timed:
+            torch.cuda._sleep(1 << 20)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        mla_quantize_append(layer, rows, slots)
+        if timed:
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        if on_chunk is not None:
+            on_chunk(c0, rows)
+    pos = synth.mla_topk_positions(T, [ctx] * T, topk, device, 62, layer_idx)
+    idx = synth.slots_of_positions(pos, bt, page)
+    return MlaFilled(layer, bt, idx, ms)

@@ -339,3 +339,51 @@ def test_noalloc_decode_checks_and_limit():
     assert ok_b >= 200  # about 218 sequences of 8 kv heads at 8 q heads per kv head
     assert _decode_noalloc(nk, L, B=ok_b + 1, Hq=64, msl=8192, bts=512) == 3
     assert _decode_noalloc(nk, L, B=4096, Hq=128, msl=64, bts=4) == 3  # too many units for the counters
+
+
+def _mla_layer(nk, **kw):
+    d = dict(codes=FAKE, scales=FAKE + 0x100000, num_slots=100, latent_dim=512, rope_dim=64, global_scale=0.01)
+    d.update(kw)
+    return nk.CMlaLayer(**d)
+
+
+def _mla_decode(nk, layer, q=FAKE, qdt=1, T=2, Hq=64, idx=FAKE, topk=32, sm=0.07, out=FAKE, ws=FAKE, wsb=1 << 30):
+    return nk.lib.nvfp4_mla_sparse_decode(ctypes.byref(layer), ctypes.c_void_p(q), qdt, T, Hq, ctypes.c_void_p(idx),
+                                          topk, sm, ctypes.c_void_p(out), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_mla_checks():
+    """The Sparse-MLA entry points check their arguments before any HIP call."""
+    nk = _lib()
+    L = _mla_layer(nk)
+    app = lambda layer, x=FAKE, dt=1, T=4, stride=576, sl=FAKE: nk.lib.nvfp4_mla_quantize_append(
+        ctypes.byref(layer), ctypes.c_void_p(x), dt, T, stride, ctypes.c_void_p(sl), None)
+    assert app(_mla_layer(nk, latent_dim=256)) == 2
+    assert app(_mla_layer(nk, rope_dim=0)) == 2
+    assert app(_mla_layer(nk, codes=0)) == 1
+    assert app(_mla_layer(nk, codes=FAKE + 8)) == 2
+    assert app(_mla_layer(nk, num_slots=0)) == 1
+    assert app(_mla_layer(nk, global_scale=float("nan"))) == 1
+    assert app(L, T=0, x=0, sl=0) == 0
+    assert app(L, T=-1) == 1
+    assert app(L, stride=575) == 1
+    assert app(L, x=FAKE + 4) == 2
+    assert app(L, stride=580, dt=1) == 2          # 1160-byte rows: not a multiple of 16 bytes
+    assert app(L, sl=0) == 1
+    assert _mla_decode(nk, L, qdt=0) == 2         # float32 queries: not supported
+    assert _mla_decode(nk, L, qdt=5) == 1
+    assert _mla_decode(nk, L, Hq=40) == 2         # not a multiple of 16
+    assert _mla_decode(nk, L, Hq=96) == 2         # above 64: a multiple of 64
+    assert _mla_decode(nk, L, topk=(1 << 20) + 1) == 2
+    assert _mla_decode(nk, L, T=-1) == 1
+    assert _mla_decode(nk, L, T=0, q=0, idx=0, out=0) == 0
+    assert _mla_decode(nk, L, q=0) == 1
+    assert _mla_decode(nk, L, idx=0) == 1
+    assert _mla_decode(nk, L, q=FAKE + 8) == 2
+    assert _mla_decode(nk, L, sm=float("inf")) == 1
+    need = nk.mla_sparse_decode_workspace_bytes(2, 64, 2048)  # few tokens: lists split, partials needed
+    assert need > 256 and _mla_decode(nk, L, topk=2048, wsb=need - 1) == 3
+    assert _mla_decode(nk, L, topk=2048, ws=FAKE + 16) == 1
+    assert _mla_decode(nk, L, topk=2048, ws=0, wsb=need) == 1
+    assert nk.mla_sparse_decode_workspace_bytes(0, 64, 2048) == 0
+    assert nk.mla_sparse_decode_workspace_bytes(512, 128, 2048) == 0  # 1024 (token, head block) units: no split
