@@ -199,6 +199,13 @@ struct PageRegs {
 // loop does no per-lane address arithmetic; reads past the descriptor's range
 // return 0.
 constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer resource word 3 for raw dword access
+// Cache policy of the page loads: every page is read once per call, so the
+// loads are non-temporal (gfx950 buffer-load aux bit 1, nt): streaming reads
+// that do not displace reused data measured clearly faster than default loads.
+#ifndef NVFP4_PAGE_LOAD_AUX
+#define NVFP4_PAGE_LOAD_AUX 2
+#endif
+constexpr int kPageAux = NVFP4_PAGE_LOAD_AUX;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t offset, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + offset), 0, bytes, kBufferFlags);
@@ -238,22 +245,22 @@ __device__ __forceinline__ PageRegs load_page(const DecodeParams& p, const Plane
   if (kPlane) {
     const uint32_t tile = (uint32_t)(ok ? page : 0) * (uint32_t)p.H + (uint32_t)h;
     const int so_c = (int)(tile * kTileCodeBytes), so_s = (int)(tile * kScaleBytes);
-    d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.kc, lo.kc, so_c, 0));
-    d.ksw = kMX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(pr.ks, lo.ks, so_s, 0)
-                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pr.ks, lo.ks, so_s, 0);
-    d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.vc, lo.vc, so_c, 0));
-    d.vsw = __builtin_amdgcn_raw_buffer_load_b32(pr.vs, lo.vs, so_s, 0);
+    d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.kc, lo.kc, so_c, kPageAux));
+    d.ksw = kMX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(pr.ks, lo.ks, so_s, kPageAux)
+                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pr.ks, lo.ks, so_s, kPageAux);
+    d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr.vc, lo.vc, so_c, kPageAux));
+    d.vsw = __builtin_amdgcn_raw_buffer_load_b32(pr.vs, lo.vs, so_s, kPageAux);
   } else {
     const int64_t tile = (int64_t)(ok ? page : 0) * p.H + h;
     const auto kc = tile_rsrc(p.k_codes, tile * kTileCodeBytes, kTileCodeBytes);
     const auto ks = tile_rsrc(p.k_scales, tile * kScaleBytes, kScaleBytes);
     const auto vc = tile_rsrc(p.v_codes, tile * kTileCodeBytes, kTileCodeBytes);
     const auto vs = tile_rsrc(p.v_scales, tile * kScaleBytes, kScaleBytes);
-    d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, lo.kc, 0, 0));
-    d.ksw = kMX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ks, lo.ks, 0, 0)
-                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks, lo.ks, 0, 0);
-    d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, lo.vc, 0, 0));
-    d.vsw = __builtin_amdgcn_raw_buffer_load_b32(vs, lo.vs, 0, 0);
+    d.kw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, lo.kc, 0, kPageAux));
+    d.ksw = kMX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ks, lo.ks, 0, kPageAux)
+                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks, lo.ks, 0, kPageAux);
+    d.vw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, lo.vc, 0, kPageAux));
+    d.vsw = __builtin_amdgcn_raw_buffer_load_b32(vs, lo.vs, 0, kPageAux);
   }
   return d;
 }

@@ -16,21 +16,22 @@
 // is 16 code bytes at 16c and 2 scale bytes at 2c.
 //
 // Decode work: one workgroup per (query token, 16*WAVES query heads, share of
-// the list); wave w owns 16 heads.  Per tile of 16 list entries the workgroup
-// gathers the rows (one thread per 32-value chunk: 16-byte code load, 2-byte
-// scale load), dequantizes them once into LDS as f16 (e2m1 * bs is exact in
-// f16), double-buffered, and every wave computes from that copy:
-//   S^T[16 entries x 16 heads] = K . Q^T : 18 x mfma_f32_16x16x32_f16
+// the list); wave w owns 16 heads.  Per tile of 32 list entries the workgroup
+// gathers the rows (one thread per (entry, 32-value chunk): 16-byte code load,
+// 2-byte scale load), dequantizes them once into LDS as f16 (e2m1 * bs is
+// exact in f16), double-buffered, and every wave computes from that copy:
+//   S^T[2 x 16 entries x 16 heads] = K . Q^T : 2 x 18 mfma_f32_16x16x32_f16
 //     (A = staged rows, lane (entry l%16, dims 32c + 8*(l/16) .. +7), one
 //      16-byte LDS read; B = Q in registers, f16 after an exact power-of-two
 //      prescale)
 //   online softmax in fp32 (log2 domain, lazy running max, as the GQA decode)
-//   O[16 heads x 512] += P . V : 32 x mfma_f32_16x16x32_f16, P as an f16
-//     hi + lo pair filling the k = 32 operand against V duplicated; the V
-//     operand -- entries 4*(l/16) .. +3 at one dim -- comes from the same
-//     row-major copy with one transposing LDS read (ds_read_b64_tr_b16: within
-//     each 16-lane group, lane p receives element p%4 of the 8-byte chunks that
-//     lanes p/4 + 4k address, k = 0..3)
+//   O[16 heads x 512] += P . V : 2 x 32 mfma_f32_16x16x32_f16; the k = 32
+//     operand holds 8 of the tile's entries per 16-lane group (4 of each
+//     half), P enters as an f16 hi + lo pair, one MFMA each; the V operand
+//     -- those entries at one dim -- comes from the same row-major copy with
+//     two transposing LDS reads (ds_read_b64_tr_b16: within each 16-lane
+//     group, lane p receives element p%4 of the 8-byte chunks that lanes
+//     p/4 + 4k address, k = 0..3)
 // The global scale enters the logits and the final output.  When few query
 // tokens leave CUs idle, each list is split into shares over several
 // workgroups; each share stores its (max, sum, O) in the workspace and a merge
