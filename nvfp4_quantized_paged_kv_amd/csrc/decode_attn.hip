@@ -449,6 +449,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int len_v = __builtin_amdgcn_raw_buffer_load_b32(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p.seq_lens), 0, 4 * B, kBufferFlags), 4 * b, 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // all of them in flight before Q is used
+    // Q, both page-index registers and the length complete (they were issued
+    // together; the first page's loads need the indices anyway): the page loop
+    // then reads page indices without waiting.  Otherwise the compiler cannot
+    // tell at the loop head that the index loads are done and drains every
+    // load in flight before each page's index read.
+    wait_vmem();
 
     const LaneOffsets lo = kMX ? LaneOffsets{er * 64 + eq * 16, er * 4 + eq, el * 16, (er >> 2) * 16 + eq * 4}
                                : LaneOffsets{er * 64 + eq * 16, er * 8 + eq * 2, el * 16, (er >> 1) * 16 + eq * 4};
@@ -543,8 +549,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           if (kSplitQ) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[c], S, 0, 0, 0);
         }
       } else {
-        const half2_t ks0 = e4m3_pair_to_f16_scaled(cur.ksw & 0xFFu, cur.ksw & 0xFFu);
-        const half2_t ks1 = e4m3_pair_to_f16_scaled(cur.ksw >> 8, cur.ksw >> 8);
+        // the scale byte b as the f16 pair (b << 7, b << 7): one 24-bit multiply by 0x00800080 each
+        const half2_t ks0 = __builtin_bit_cast(half2_t, (cur.ksw & 0xFFu) * 0x00800080u);
+        const half2_t ks1 = __builtin_bit_cast(half2_t, ((cur.ksw >> 8) & 0xFFu) * 0x00800080u);
   #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const half2_t sc = c < 2 ? ks0 : ks1;
@@ -575,8 +582,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int i = 0; i < 4; ++i)
           if (4 * q4 + i >= vlim) S[i] = -__builtin_inff();
       }
-      const float pm = vmax_over_groups(vmax(vmax3(S[0], S[1], S[2]), S[3])) * tscale;  // -inf: all masked
-      if (__any(pm > m_lim)) {
+      // The lane's own 4 scores decide whether any head's maximum passes its
+      // lazy bound; only then is the maximum over the 4 token groups taken
+      // (tscale >= 0 and rounding are monotone, so the maximum of the scaled
+      // scores is the scaled maximum; -inf: all masked).
+      const float lm = vmax(vmax3(S[0], S[1], S[2]), S[3]) * tscale;
+      if (__any(lm > m_lim)) {
+        const float pm = vmax_over_groups(lm);
         const float m_new = fmaxf(m_run, pm);
         const float f = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= f;
@@ -638,12 +650,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
       // P as an f16 hi + lo pair (about 22 bits): with P alone in f16 (11
       // bits) a row whose output nearly cancels -- outliers of opposite sign
-      // in a few tokens -- could miss 1e-3 relative to the row's largest value
-      const half4_t ph = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-      const half8_t pa = {ph[0], ph[1], ph[2], ph[3], (_Float16)(pr[0] - (float)ph[0]), (_Float16)(pr[1] - (float)ph[1]),
-                          (_Float16)(pr[2] - (float)ph[2]), (_Float16)(pr[3] - (float)ph[3])};
+      // in a few tokens -- could miss 1e-3 relative to the row's largest value.
+      // hi = p cut to 11 significant bits (exact in f16 for p >= 2^-14), lo = the rest.
+      float hf[4];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) hf[i] = __uint_as_float(__float_as_uint(pr[i]) & 0xFFFFE000u);
+      const half4_t ph = {(_Float16)hf[0], (_Float16)hf[1], (_Float16)hf[2], (_Float16)hf[3]};
+      const half4_t pl = {(_Float16)(pr[0] - hf[0]), (_Float16)(pr[1] - hf[1]), (_Float16)(pr[2] - hf[2]),
+                          (_Float16)(pr[3] - hf[3])};
 
-      // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3)
+      // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3).
+      // 16x16x16 MFMAs, one for P hi and one for P lo against the same V
+      // operand: no register copies of V (a 16x16x32 MFMA taking the pair
+      // would need V twice in its operand).
       uint32_t vsw = cur.vsw;
       if (rem < kPageSize) {
         const int nv = min(max(rem - 4 * q4, 0), 4);
@@ -660,10 +679,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const half2_t a1 = fp4x2_to_f16_x256<C>(E23) * vs23;                                   \
       const half2_t b0 = fp4x2_to_f16_x256<C>(O01) * vs01;                                   \
       const half2_t b1 = fp4x2_to_f16_x256<C>(O23) * vs23;                                   \
-      const half8_t ve = {a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};            \
-      const half8_t vo = {b0[0], b0[1], b1[0], b1[1], b0[0], b0[1], b1[0], b1[1]};            \
-      acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, ve, acc[2 * C], 0, 0, 0);      \
-      acc[2 * C + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vo, acc[2 * C + 1], 0, 0, 0); \
+      const half4_t ve = {a0[0], a0[1], a1[0], a1[1]};                                       \
+      const half4_t vo = {b0[0], b0[1], b1[0], b1[1]};                                       \
+      acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, ve, acc[2 * C], 0, 0, 0);        \
+      acc[2 * C + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vo, acc[2 * C + 1], 0, 0, 0); \
+      acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, ve, acc[2 * C], 0, 0, 0);        \
+      acc[2 * C + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vo, acc[2 * C + 1], 0, 0, 0); \
     }
       NVFP4_PV_STEP(0)
       NVFP4_PV_STEP(1)
@@ -700,6 +721,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       rs_bt = chunk_rsrc(c1);
       pidx0 = __builtin_amdgcn_raw_buffer_load_b32(rs_bt, 4 * (c0 + wave + kWaves * el), 0, 0);
       pidx1 = __builtin_amdgcn_raw_buffer_load_b32(rs_bt, 4 * (c0 + wave + kWaves * (el + 64)), 0, 0);
+      wait_vmem();  // both index registers complete before the page loop (see the segment's first chunk)
       if (n_mine > 0) A = load_mine(0);
     }
 
