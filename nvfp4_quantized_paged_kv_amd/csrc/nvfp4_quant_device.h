@@ -31,15 +31,6 @@ __device__ __forceinline__ float threshold_f32(float a, float g, bool odd) {
   return down ? pred : hi;
 }
 
-// Values 2Q and 2Q+1, times c_lo and times c_hi, to E2M1 codes in byte Q%4 of
-// word Q/4 of lo and hi (low nibble = value 2Q).
-template <int Q>
-__device__ __forceinline__ void cvt_pair(uint32_t (&lo)[2], uint32_t (&hi)[2], const float (&x)[16], float c_lo,
-                                         float c_hi) {
-  lo[Q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[Q >> 2], x[2 * Q] * c_lo, x[2 * Q + 1] * c_lo, 1.0f, Q & 3);
-  hi[Q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[Q >> 2], x[2 * Q] * c_hi, x[2 * Q + 1] * c_hi, 1.0f, Q & 3);
-}
-
 template <typename InT>
 __device__ __forceinline__ void load_block(const InT* src, float (&x)[16]);
 
@@ -121,6 +112,117 @@ __device__ __forceinline__ void hadamard_rotate_k(float (&x)[N], int b) {
   for (int i = 0; i < N; ++i) x[i] = (float)(d[i] * 0.0625);
 }
 
+// E4M3 scale byte of a block whose largest magnitude is amax: the E4M3 value
+// nearest to amax/(6g).  r6 = 1/(6g) rounded to float64 (computed once per
+// call by the caller).
+__device__ __forceinline__ uint32_t block_scale_byte(float amax, float g, double r6) {
+  // amax/(6g) without a division: q0 = amax*r6 is within 2^-52 (relative) of
+  // the quotient, and one correction with the exact residual amax - q0*6g
+  // (one fma; 6g is exact in float64) brings it within about 2^-104.  An
+  // exact quotient that is an E4M3 midpoint (5 significant bits) then comes
+  // out exactly, and any other quotient lies at least 2^-31 (relative) from
+  // every midpoint (amax has 24 significant bits, 6*g*midpoint at most 31),
+  // so the E4M3 rounding below sees the same side as for the exact quotient.
+  const double a = (double)amax, g6 = 6.0 * (double)g;
+  const double q0 = a * r6;
+  return e4m3_encode_rne_sat(__builtin_fma(__builtin_fma(-q0, g6, a), r6, q0));
+}
+
+// Value k (lane-varying) of the 8 values x[8i .. 8i+7]: a select tree over the bits of k.
+template <int N>
+__device__ __forceinline__ float pick8(const float (&x)[N], int i, int k) {
+  const float a0 = (k & 1) ? x[8 * i + 1] : x[8 * i], a1 = (k & 1) ? x[8 * i + 3] : x[8 * i + 2];
+  const float a2 = (k & 1) ? x[8 * i + 5] : x[8 * i + 4], a3 = (k & 1) ? x[8 * i + 7] : x[8 * i + 6];
+  const float b0 = (k & 2) ? a1 : a0, b1 = (k & 2) ? a3 : a2;
+  return (k & 4) ? b1 : b0;
+}
+
+// 4 * the midpoint between E2M1 magnitudes m and m + 1 (m = 0..6): 1, 3, 5, 7, 10, 14, 20.
+__device__ __forceinline__ uint32_t e2m1_mid_x4(uint32_t m) {
+  return __builtin_amdgcn_perm(0x00140E0Au, 0x07050301u, 0x0C0C0C00u | m);
+}
+
+// E2M1 codes of N values (N a multiple of 8) of a block with scale bs = E4M3
+// value of its scale byte: packed[i] holds values 8i .. 8i+7, low nibble =
+// even value.  Each value's code is decided on its own, so a block may be
+// split over lanes.  Fast path: the two bracketing conversions; where they
+// agree the code is exact.  Where they differ (the value lies within about
+// 2^-20 of a rounding midpoint: common when g comes from bf16 data), the
+// lower code's magnitude m or m + 1 is right, and the exact threshold between
+// them decides (ties to the even magnitude).  Zero and extreme scales take the
+// threshold path for every value.
+template <int N>
+__device__ __forceinline__ void encode_codes(const float (&x)[N], float bs, float g, uint32_t (&packed)[N / 8]) {
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) packed[i] = 0u;
+  // the fast path needs bs*g (rounded) to be a normal float32 whose reciprocal
+  // is normal too
+  const float bsg = bs * g;
+  if (bsg >= 0x1p-125f && bsg <= 0x1p125f) {
+    // r is within 1 ulp (2^-23) of 1/bsg and bsg within 2^-24 of bs*g, so the
+    // margins of 2^-20 keep c_lo below and c_hi above 1/(bs*g) by more than
+    // 0.74 * 2^-20 after rounding
+    const float r = __builtin_amdgcn_rcpf(bsg);
+    const float c_lo = r * (1.0f - 0x1p-20f), c_hi = r * (1.0f + 0x1p-20f);
+    uint32_t hi[N / 8];
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) hi[i] = 0u;
+#pragma unroll
+    for (int q = 0; q < N / 2; ++q) {
+      switch (q & 3) {  // the byte select of the conversion is an immediate
+        case 0:
+          packed[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed[q >> 2], x[2 * q] * c_lo, x[2 * q + 1] * c_lo, 1.0f, 0);
+          hi[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[q >> 2], x[2 * q] * c_hi, x[2 * q + 1] * c_hi, 1.0f, 0);
+          break;
+        case 1:
+          packed[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed[q >> 2], x[2 * q] * c_lo, x[2 * q + 1] * c_lo, 1.0f, 1);
+          hi[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[q >> 2], x[2 * q] * c_hi, x[2 * q + 1] * c_hi, 1.0f, 1);
+          break;
+        case 2:
+          packed[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed[q >> 2], x[2 * q] * c_lo, x[2 * q + 1] * c_lo, 1.0f, 2);
+          hi[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[q >> 2], x[2 * q] * c_hi, x[2 * q + 1] * c_hi, 1.0f, 2);
+          break;
+        default:
+          packed[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed[q >> 2], x[2 * q] * c_lo, x[2 * q + 1] * c_lo, 1.0f, 3);
+          hi[q >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[q >> 2], x[2 * q] * c_hi, x[2 * q + 1] * c_hi, 1.0f, 3);
+          break;
+      }
+    }
+    // c_hi / c_lo < 1 + 2^-19, so the two products straddle at most one
+    // midpoint: where the codes differ, hi's magnitude is lo's plus one (same sign)
+    const float bs4 = 0.25f * bs;
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const uint32_t d = packed[i] ^ hi[i];
+      uint32_t m = (d | (d >> 1) | (d >> 2) | (d >> 3)) & 0x11111111u;  // bit 4j: value 8i + j differs
+      while (m != 0u) {
+        const int pos = __builtin_ctz(m);
+        m &= m - 1u;
+        const uint32_t mag = (packed[i] >> pos) & 7u;
+        // 4*mid and bs/4 have at most 5 and 4 significant bits: the product is exact
+        const float u = threshold_f32((float)e2m1_mid_x4(mag) * bs4, g, (mag & 1u) != 0u);
+        if (fabsf(pick8<N>(x, i, pos >> 2)) > u) packed[i] += 1u << pos;
+      }
+    }
+    return;
+  }
+  float u[7];
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+  for (int k = 0; k < 7; ++k) u[k] = bs == 0.0f ? __builtin_inff() : threshold_f32(mids[k] * bs, g, (k & 1) != 0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float ax = fabsf(x[k]);
+    const bool c2 = ax > u[3];
+    const bool c1 = ax > (c2 ? u[5] : u[1]);
+    const float t0 = c2 ? (c1 ? u[6] : u[4]) : (c1 ? u[2] : u[0]);
+    const bool c0 = ax > t0;
+    const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
+    const uint32_t code = mag | ((__float_as_uint(x[k]) >> 28) & 8u);
+    packed[k >> 3] |= code << (4 * (k & 7));
+  }
+}
+
 // One quantized block: 16 E2M1 codes (low nibble = even value) and the E4M3 scale byte.
 struct QuantBlock {
   uint32_t packed[2];
@@ -132,63 +234,9 @@ __device__ __forceinline__ QuantBlock quantize_block16(const float (&x)[16], flo
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
-
   QuantBlock q;
-  {
-    // amax/(6g) without a division: q0 = amax*r6 is within 2^-52 (relative) of
-    // the quotient, and one correction with the exact residual amax - q0*6g
-    // (one fma; 6g is exact in float64) brings it within about 2^-104.  An
-    // exact quotient that is an E4M3 midpoint (5 significant bits) then comes
-    // out exactly, and any other quotient lies at least 2^-31 (relative) from
-    // every midpoint (amax has 24 significant bits, 6*g*midpoint at most 31),
-    // so the E4M3 rounding below sees the same side as for the exact quotient.
-    const double a = (double)amax, g6 = 6.0 * (double)g;
-    const double q0 = a * r6;
-    q.sb = e4m3_encode_rne_sat(__builtin_fma(__builtin_fma(-q0, g6, a), r6, q0));
-  }
-  const float bs = e4m3_value(q.sb);
-
-  q.packed[0] = q.packed[1] = 0u;
-  // the fast path needs bs*g (rounded) to be a normal float32 whose reciprocal
-  // is normal too; a zero scale (every code is its sign) and extreme global
-  // scales take the threshold path
-  const float bsg = bs * g;
-  bool exact_path = !(bsg >= 0x1p-125f && bsg <= 0x1p125f);
-  if (!exact_path) {
-    // r is within 1 ulp (2^-23) of 1/bsg and bsg within 2^-24 of bs*g, so the
-    // margins of 2^-20 keep c_lo below and c_hi above 1/(bs*g) by more than
-    // 0.74 * 2^-20 after rounding
-    const float r = __builtin_amdgcn_rcpf(bsg);
-    const float c_lo = r * (1.0f - 0x1p-20f), c_hi = r * (1.0f + 0x1p-20f);
-    uint32_t hi[2] = {0u, 0u};
-    cvt_pair<0>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<1>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<2>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<3>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<4>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<5>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<6>(q.packed, hi, x, c_lo, c_hi);
-    cvt_pair<7>(q.packed, hi, x, c_lo, c_hi);
-    exact_path = (q.packed[0] != hi[0]) | (q.packed[1] != hi[1]);
-  }
-  if (exact_path) {
-    float u[7];
-    const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-#pragma unroll
-    for (int k = 0; k < 7; ++k) u[k] = bs == 0.0f ? __builtin_inff() : threshold_f32(mids[k] * bs, g, (k & 1) != 0);
-    q.packed[0] = q.packed[1] = 0u;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float ax = fabsf(x[k]);
-      const bool c2 = ax > u[3];
-      const bool c1 = ax > (c2 ? u[5] : u[1]);
-      const float t0 = c2 ? (c1 ? u[6] : u[4]) : (c1 ? u[2] : u[0]);
-      const bool c0 = ax > t0;
-      const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
-      const uint32_t code = mag | ((__float_as_uint(x[k]) >> 28) & 8u);
-      q.packed[k >> 3] |= code << (4 * (k & 7));
-    }
-  }
+  q.sb = block_scale_byte(amax, g, r6);
+  encode_codes<16>(x, e4m3_value(q.sb), g, q.packed);
   return q;
 }
 
