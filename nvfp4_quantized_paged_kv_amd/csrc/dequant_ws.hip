@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kWsWaves * 64) void dequant_ws_kernel(DequantWsPara
   if (tile0 >= tiles) return;
 
   {  // this thread's table entry: E4M3 bytes of |e2m1_m| * bs * g / s_ws, m = 0..7
-    const double num = (double)e4m3_value(threadIdx.x) * (double)p.g[which];  // exact: 4 + 24 bits
+    const double num = (double)e4m3_value(threadIdx.x & 0x7Fu) * (double)p.g[which];  // exact: 4 + 24 bits; sign bit ignored
     const double ws = (double)p.ws_scale[which];
     const double y05 = (num * 0.5) / ws;
     const double y15 = (num * 1.5) / ws;

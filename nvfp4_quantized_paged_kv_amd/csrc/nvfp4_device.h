@@ -33,10 +33,11 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne_sat(double r) {
   return (uint32_t)((E + 7) << 3) + m - 8u;                        // m == 16 carries into the exponent
 }
 
-// Exact float value of a non-negative finite E4M3 byte.
+// Exact float value of an E4M3 byte without its sign bit (b < 0x80; 0x7F
+// reads as 480): the f16 bit pattern b << 7 holds the value times 2^-8,
+// subnormals included (see below).
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const int e = (int)(b >> 3) & 15, m = (int)(b & 7);
-  return e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8 + m), e - 10);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(b << 7)) * 256.0f;
 }
 
 // Two E4M3 bytes (each < 0x80) to packed f16 holding value * 2^-8: the f16 bit

@@ -43,7 +43,10 @@ __device__ __forceinline__ void quantize_store(const float (&x)[16], const Appen
 __device__ __forceinline__ void block_coords(int64_t i, const AppendParams& p, int64_t& t, int& h, int& b) {
   const int tq = (int)(i & 3), tg = (int)((i >> 5) & 3);
   b = (int)((i >> 2) & 7);
-  const uint32_t gh = (uint32_t)(i >> 7);  // group of 16 tokens * H + kv head (< 2^31, checked by the host)
+  // group of 16 tokens * H + kv head (< 2^31, checked by the host); the 64
+  // jobs of a wave share it (jobs come in aligned runs of 128), so the
+  // division below runs on the scalar unit
+  const uint32_t gh = __builtin_amdgcn_readfirstlane((uint32_t)(i >> 7));
   h = (int)(gh % (uint32_t)p.H);
   t = 16 * (int64_t)(gh / (uint32_t)p.H) + 4 * tg + tq;
   if (t >= p.num_tokens) t = -1;
