@@ -128,11 +128,17 @@ __device__ __forceinline__ uint32_t block_scale_byte(float amax, float g, double
   return e4m3_encode_rne_sat(__builtin_fma(__builtin_fma(-q0, g6, a), r6, q0));
 }
 
-// Value k (lane-varying) of the 8 values x[8i .. 8i+7]: a select tree over the bits of k.
+// Value k (lane-varying) of the 8 values x[8i .. 8i+7]: a select tree over the
+// bits of k.  The values pass through an empty asm first, so the selects act
+// on registers: selects between elements of x would otherwise be folded into
+// an indexed load, which moves the whole array out of registers (into LDS or
+// scratch memory) in every kernel that quantizes blocks.
 template <int N>
 __device__ __forceinline__ float pick8(const float (&x)[N], int i, int k) {
-  const float a0 = (k & 1) ? x[8 * i + 1] : x[8 * i], a1 = (k & 1) ? x[8 * i + 3] : x[8 * i + 2];
-  const float a2 = (k & 1) ? x[8 * i + 5] : x[8 * i + 4], a3 = (k & 1) ? x[8 * i + 7] : x[8 * i + 6];
+  float v0 = x[8 * i], v1 = x[8 * i + 1], v2 = x[8 * i + 2], v3 = x[8 * i + 3];
+  float v4 = x[8 * i + 4], v5 = x[8 * i + 5], v6 = x[8 * i + 6], v7 = x[8 * i + 7];
+  asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7));
+  const float a0 = (k & 1) ? v1 : v0, a1 = (k & 1) ? v3 : v2, a2 = (k & 1) ? v5 : v4, a3 = (k & 1) ? v7 : v6;
   const float b0 = (k & 2) ? a1 : a0, b1 = (k & 2) ? a3 : a2;
   return (k & 4) ? b1 : b0;
 }
