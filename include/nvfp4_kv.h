@@ -58,7 +58,17 @@ extern "C" {
 #define NVFP4_API
 #endif
 
-typedef enum nvfp4_status {
+/* The status and dtype enums are int-sized in C.  Seen from C++ they get int
+ * as their fixed underlying type, so every int a C caller passes (an unknown
+ * status for nvfp4_status_string, a bad dtype that the checks reject) is a
+ * valid value of the type rather than undefined behaviour. */
+#ifdef __cplusplus
+#define NVFP4_ENUM_BASE : int
+#else
+#define NVFP4_ENUM_BASE
+#endif
+
+typedef enum nvfp4_status NVFP4_ENUM_BASE {
   NVFP4_OK = 0,
   NVFP4_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad scale, inconsistent sizes */
   NVFP4_ERR_UNSUPPORTED = 2,      /* head_dim != 128, page_size != 16, >16 q heads per kv head, alignment */
@@ -66,7 +76,7 @@ typedef enum nvfp4_status {
   NVFP4_ERR_HIP = 4               /* a HIP launch reported an error */
 } nvfp4_status_t;
 
-typedef enum nvfp4_dtype {
+typedef enum nvfp4_dtype NVFP4_ENUM_BASE {
   NVFP4_DTYPE_F32 = 0,
   NVFP4_DTYPE_BF16 = 1
 } nvfp4_dtype_t;

@@ -17,7 +17,8 @@ from dataclasses import dataclass
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libnvfp4kv.so")
+# NVFP4KV_LIBRARY: another build of the same sources (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("NVFP4KV_LIBRARY") or os.path.join(_PKG_DIR, "libnvfp4kv.so")
 
 HEAD_DIM = 128
 PAGE_SIZE = 16

@@ -36,18 +36,25 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# Host code (the C ABI's argument checks, launch set-up) under AddressSanitizer
+# and UBSan; device code is compiled as always.  The sanitizer runtime is not
+# linked: the process that loads this build preloads it.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB_PATH) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if "not a recognized feature" not in ln]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -16,7 +16,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libnvfp4_oracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "libnvfp4_oracle.so")
+# NVFP4_ORACLE_LIBRARY: another build of the same source (the tests' sanitizer build)
+_LIB_PATH = os.environ.get("NVFP4_ORACLE_LIBRARY") or _DEFAULT_LIB
 _lib = None
 
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
@@ -33,10 +35,21 @@ _dbl = ctypes.c_double
 def build() -> str:
     """Compile the oracle with gcc (strict IEEE: no contraction, no fast-math)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
-           "-shared", "-fPIC", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+           "-shared", "-fPIC", _SRC, "-o", _DEFAULT_LIB + ".tmp", "-lm"]
     subprocess.check_call(cmd)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(_DEFAULT_LIB + ".tmp", _DEFAULT_LIB)
+    return _DEFAULT_LIB
+
+
+def build_sanitized(out: str, clang: str) -> str:
+    """The same source under AddressSanitizer and UBSan (clang, no OpenMP), for
+    the host sanitizer test; the runtime is preloaded by the process that loads it."""
+    cmd = [clang, "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared", "-fPIC", _SRC,
+           "-o", out + ".tmp", "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def lib():
@@ -44,6 +57,8 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
+        if _LIB_PATH != _DEFAULT_LIB:
+            raise ImportError(f"NVFP4_ORACLE_LIBRARY={_LIB_PATH} does not exist")
         build()
     L = ctypes.CDLL(_LIB_PATH)
     L.nvfp4o_e2m1_value.argtypes = [_int]
