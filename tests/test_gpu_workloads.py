@@ -87,11 +87,16 @@ def test_gqa70b_b32_8k_full_size():
 
 
 def test_long_b8_128k_full_size():
-    _run("long_b8_128k", [(5, 6)])
+    """Four of the 64 units, the first and the last among them; with 64 units
+    over 256 workgroups every unit's pages are shared by several workgroups,
+    so each checked output went through the in-kernel merge."""
+    _run("long_b8_128k", [(0, 0), (3, 4), (5, 6), (7, 7)])
 
 
 def test_agentic_b1_2m_full_size():
-    _run("agentic_b1_2m", [(0, 2)])
+    """All 8 kv heads of the 2,000,000-token sequence: every code and scale byte
+    of the layer and all 96 query heads' outputs."""
+    _run("agentic_b1_2m", [(0, h) for h in range(8)])
 
 
 def test_mixed_64_full_size():
