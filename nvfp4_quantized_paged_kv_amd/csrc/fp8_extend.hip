@@ -329,11 +329,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
     half4_t pa[2][2], pl[2][2];  // P as an f16 hi + lo pair
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const float pm =
-          vmax_over_groups(vmax(vmax(vmax(S[0][rb][0], S[0][rb][1]), vmax(S[0][rb][2], S[0][rb][3])),
-                                vmax(vmax(S[1][rb][0], S[1][rb][1]), vmax(S[1][rb][2], S[1][rb][3])))) *
-          tscale[rb];
-      if (__any(pm > m_lim[rb])) {
+      // the lane's own 8 scores decide whether any row's maximum passes its
+      // lazy bound; only then is the maximum over the 4 key groups taken
+      // (tscale >= 0 and rounding are monotone: the maximum of the scaled
+      // scores is the scaled maximum)
+      const float lm = vmax(vmax(vmax(S[0][rb][0], S[0][rb][1]), vmax(S[0][rb][2], S[0][rb][3])),
+                            vmax(vmax(S[1][rb][0], S[1][rb][1]), vmax(S[1][rb][2], S[1][rb][3]))) *
+                       tscale[rb];
+      if (__any(lm > m_lim[rb])) {
+        const float pm = vmax_over_groups(lm);
         const float m_new = fmaxf(m_run[rb], pm);
         const float f = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         l_run[rb] *= f;
@@ -353,9 +357,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
         for (int i = 0; i < 4; ++i)  // the rounded product, as in pm: t - m_run <= kExtLazyMax for any logit
           pr[i] = __builtin_amdgcn_exp2f(S[kb][rb][i] * tscale[rb] - m_run[rb]);
         l_run[rb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        pa[rb][kb] = half4_t{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-        pl[rb][kb] = half4_t{(_Float16)(pr[0] - (float)pa[rb][kb][0]), (_Float16)(pr[1] - (float)pa[rb][kb][1]),
-                             (_Float16)(pr[2] - (float)pa[rb][kb][2]), (_Float16)(pr[3] - (float)pa[rb][kb][3])};
+        // hi = p cut to 11 significant bits (exact in f16 for p >= 2^-14), lo = the rest
+        float hf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hf[i] = __uint_as_float(__float_as_uint(pr[i]) & 0xFFFFE000u);
+        pa[rb][kb] = half4_t{(_Float16)hf[0], (_Float16)hf[1], (_Float16)hf[2], (_Float16)hf[3]};
+        pl[rb][kb] = half4_t{(_Float16)(pr[0] - hf[0]), (_Float16)(pr[1] - hf[1]), (_Float16)(pr[2] - hf[2]),
+                             (_Float16)(pr[3] - hf[3])};
       }
     }
 
