@@ -308,6 +308,38 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn(const void* q, nvfp4_dtype_t q_dt
                                                float k_ws_scale, float v_ws_scale, float sm_scale, float* out,
                                                void* stream);
 
+/* The same attention with each chunk tile's keys divided among several
+ * workgroups when the chunks alone are too few tiles to fill the GPU (short
+ * extend chunks over long cached prefixes, as in speculative verification or
+ * a small last prefill chunk).  Each workgroup keeps an unnormalised partial
+ * output with its row maximum and row sum in `workspace`; a second kernel on
+ * the same stream merges them (the usual log-sum-exp combination of softmax
+ * pieces).  The result equals nvfp4_fp8_extend_attn's up to fp32 rounding
+ * order.  Arguments are those of nvfp4_fp8_extend_attn plus:
+ *   max_prefix_len : host bound on the prefixes P_i, used only to choose the
+ *                    split (a larger P_i is still computed correctly).
+ *   workspace      : device memory of at least
+ *                    nvfp4_fp8_extend_attn_split_workspace_bytes(...) bytes,
+ *                    16-byte aligned, owned by the caller, contents ignored
+ *                    and overwritten; may be NULL when that size is 0 (no
+ *                    split chosen: the call is then nvfp4_fp8_extend_attn).
+ * Errors: those of nvfp4_fp8_extend_attn; INVALID_ARGUMENT for
+ * max_prefix_len < 0 or a NULL workspace that is needed,
+ * WORKSPACE_TOO_SMALL for workspace_bytes below the size, UNSUPPORTED for a
+ * misaligned workspace.  Calls that share a workspace must not overlap. */
+NVFP4_API size_t nvfp4_fp8_extend_attn_split_workspace_bytes(nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                                              int32_t num_seqs, int32_t max_chunk_len,
+                                                              int32_t max_prefix_len);
+NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_split(const void* q, nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                                     const int32_t* q_offsets, const int32_t* ws_offsets,
+                                                     const int32_t* prefix_lens, int32_t max_chunk_len,
+                                                     int32_t max_prefix_len, const uint8_t* ws_k, const uint8_t* ws_v,
+                                                     int32_t ws_capacity_tokens, float k_ws_scale, float v_ws_scale,
+                                                     float sm_scale, float* out, void* workspace,
+                                                     size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ MXFP4
  * The 4-bit format the NVFP4 pages compare against (nmedialink.com, accuracy
  * section and Fig. 6: NVFP4 KV caches score above MXFP4 ones, credited to the

@@ -47,6 +47,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_dequant_to_fp8_workspace",
     "nvfp4_fp8_rows_to_workspace",
     "nvfp4_fp8_extend_attn",
+    "nvfp4_fp8_extend_attn_split_workspace_bytes",
+    "nvfp4_fp8_extend_attn_split",
     "mxfp4_kv_quantize_append",
     "mxfp4_paged_decode_attn",
     "nvfp4_kv_quantize_append_hadamard",
@@ -141,6 +143,11 @@ def _load():
     L.nvfp4_fp8_extend_attn.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, f32, f32,
                                         f32, vp, vp]
     L.nvfp4_fp8_extend_attn.restype = ctypes.c_int
+    L.nvfp4_fp8_extend_attn_split_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32]
+    L.nvfp4_fp8_extend_attn_split_workspace_bytes.restype = sz
+    L.nvfp4_fp8_extend_attn_split.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp, i32,
+                                              f32, f32, f32, vp, vp, sz, vp]
+    L.nvfp4_fp8_extend_attn_split.restype = ctypes.c_int
     mp = ctypes.POINTER(CMxLayer)
     L.mxfp4_kv_quantize_append.argtypes = [mp, vp, vp, ctypes.c_int, i32, i64, vp, vp]
     L.mxfp4_kv_quantize_append.restype = ctypes.c_int
@@ -467,10 +474,7 @@ def fp8_rows_to_workspace(k: torch.Tensor, v: torch.Tensor, ws_rows: torch.Tenso
     _check(st, "nvfp4_fp8_rows_to_workspace")
 
 
-def fp8_extend_attn(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.Tensor, prefix_lens: torch.Tensor,
-                    max_chunk_len: int, ws_k: torch.Tensor, ws_v: torch.Tensor, k_ws_scale: float, v_ws_scale: float,
-                    sm_scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Causal attention of chunk queries q [Tq, Hq, 128] over FP8 workspace rows; returns f32 [Tq, Hq, 128]."""
+def _extend_args(q, q_offsets, ws_offsets, prefix_lens, ws_k, ws_v, out):
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
         raise ValueError("q must be a contiguous [Tq, Hq, 128] tensor")
     _check_ws_pair(ws_k, ws_v)
@@ -484,11 +488,51 @@ def fp8_extend_attn(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.
         out = torch.empty((Tq, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     if out.dtype != torch.float32 or not out.is_contiguous() or out.shape != (Tq, Hq, HEAD_DIM):
         raise ValueError("out must be a contiguous float32 [Tq, Hq, 128] tensor")
+    return n, Tq, Hq, out
+
+
+def fp8_extend_attn(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.Tensor, prefix_lens: torch.Tensor,
+                    max_chunk_len: int, ws_k: torch.Tensor, ws_v: torch.Tensor, k_ws_scale: float, v_ws_scale: float,
+                    sm_scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal attention of chunk queries q [Tq, Hq, 128] over FP8 workspace rows; returns f32 [Tq, Hq, 128]."""
+    n, Tq, Hq, out = _extend_args(q, q_offsets, ws_offsets, prefix_lens, ws_k, ws_v, out)
     st = lib.nvfp4_fp8_extend_attn(_ptr(q), _dtype_code(q), Tq, Hq, ws_k.shape[1], n, _ptr(q_offsets),
                                    _ptr(ws_offsets), _ptr(prefix_lens), int(max_chunk_len), _ptr(ws_k), _ptr(ws_v),
                                    ws_k.shape[0], float(k_ws_scale), float(v_ws_scale), float(sm_scale), _ptr(out),
                                    _stream(stream))
     _check(st, "nvfp4_fp8_extend_attn")
+    return out
+
+
+def fp8_extend_attn_split_workspace_bytes(q_dtype: torch.dtype, num_q_tokens: int, num_q_heads: int,
+                                          num_kv_heads: int, num_seqs: int, max_chunk_len: int,
+                                          max_prefix_len: int) -> int:
+    code = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(q_dtype)
+    if code is None:
+        raise ValueError(f"unsupported q dtype {q_dtype} (bfloat16 or float32)")
+    return int(lib.nvfp4_fp8_extend_attn_split_workspace_bytes(code, num_q_tokens, num_q_heads, num_kv_heads,
+                                                                num_seqs, max_chunk_len, max_prefix_len))
+
+
+def fp8_extend_attn_split(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.Tensor,
+                          prefix_lens: torch.Tensor, max_chunk_len: int, max_prefix_len: int, ws_k: torch.Tensor,
+                          ws_v: torch.Tensor, k_ws_scale: float, v_ws_scale: float, sm_scale: float,
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """fp8_extend_attn with each tile's keys shared among workgroups when the chunks are few tiles
+    (short chunks over long prefixes); workspace: device bytes of fp8_extend_attn_split_workspace_bytes."""
+    n, Tq, Hq, out = _extend_args(q, q_offsets, ws_offsets, prefix_lens, ws_k, ws_v, out)
+    need = fp8_extend_attn_split_workspace_bytes(q.dtype, Tq, Hq, ws_k.shape[1], n, int(max_chunk_len),
+                                                 int(max_prefix_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.nvfp4_fp8_extend_attn_split(_ptr(q), _dtype_code(q), Tq, Hq, ws_k.shape[1], n, _ptr(q_offsets),
+                                         _ptr(ws_offsets), _ptr(prefix_lens), int(max_chunk_len), int(max_prefix_len),
+                                         _ptr(ws_k), _ptr(ws_v), ws_k.shape[0], float(k_ws_scale), float(v_ws_scale),
+                                         float(sm_scale), _ptr(out), _ptr(workspace),
+                                         ws_bytes, _stream(stream))
+    _check(st, "nvfp4_fp8_extend_attn_split")
     return out
 
 

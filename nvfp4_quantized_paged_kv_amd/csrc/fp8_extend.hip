@@ -28,6 +28,8 @@
 // The FP32 per-tensor workspace scales go on the logits (K) and on the output
 // (V); Q is converted to f16 after an exact power-of-two prescale (float32 Q
 // as an f16 hi + lo pair), as in the decode kernel.
+#include <algorithm>
+
 #include "nvfp4_device.h"
 #include "nvfp4_kv_internal.h"
 
@@ -148,7 +150,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int er = lane & 15, eq = lane >> 4;
   const int seq = blockIdx.z, h = blockIdx.y;
-  const int tile = gridDim.x - 1 - blockIdx.x;  // the tiles with the most keys start first
+  // blockIdx.x = tile-from-the-end * splits + split: the tiles with the most keys start first
+  const int S = p.splits;
+  const int split = (int)(blockIdx.x % (uint32_t)S);
+  const int tile = (int)(gridDim.x / (uint32_t)S) - 1 - (int)(blockIdx.x / (uint32_t)S);
   const int G = p.G, H = p.H;
 
   // ---- the sequence (device data is clamped, never trusted)
@@ -164,6 +169,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
   const int n_keys = P + t0 + ntok;  // keys the tile's last token sees
   const int n_all = P + t0 + 1;      // keys every token of the tile sees
   const int n_kt = (n_keys + kExtKeys - 1) / kExtKeys;
+  // this workgroup's key tiles [kt0, kt1): an equal share of the tile's keys
+  // (a share may be empty; it then stores an empty partial)
+  const int kt0 = (int)((int64_t)split * n_kt / S), kt1 = (int)((int64_t)(split + 1) * n_kt / S);
 
   // ---- tile loads: thread tid < 256 moves 16 K bytes (key tid/8, dims 16*(tid%8)..+15)
   // and a 4x4 block of V (keys 4*vg..+3, dims 4*vd..+3, with tid bits 0-1 and 4 giving
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
     for (int e = 0; e < 4; ++e)
       *reinterpret_cast<uint2*>(vt + e * kVStride) = uint2{fp8x2_to_f16x2<false>(t[e]), fp8x2_to_f16x2<true>(t[e])};
   };
-  load_tile(0);
+  if (kt0 < kt1) load_tile(kt0);
 
   // ---- this wave's two row blocks: query heads 2*wave and 2*wave+1, tokens t0 .. t0+15
   const bool active = 2 * wave < G;
@@ -283,11 +291,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[rb][d] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
     store_tile(buf);
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);  // in flight while this tile is computed
+    if (kt + 1 < kt1) load_tile(kt + 1);  // in flight while this tile is computed
     if (!active) continue;
 
     // ---- S^T = K . Q^T for the tile's two 16-key blocks
@@ -394,12 +402,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
   }
   if (!active) return;
 
-  // ---- normalise and store: lane holds O[token 4*eq + i][dim 16*db + er]
+  // ---- lane holds O[token 4*eq + i][dim 16*db + er]
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int g = 2 * wave + rb;
     const float l_tot = sum_over_groups(l_run[rb]);  // lane er: the row sum of token er
     if (g >= G) continue;
+    if (S > 1) {
+      // a share of the keys: the unnormalised partial, its maximum and sum (merged by extend_merge_kernel)
+      auto part_row = [&](int row) {
+        return p.part + (((int64_t)split * p.num_q_tokens + q0 + t0 + row) * p.Hq + (int64_t)h * G + g) * kExtPartStride;
+      };
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * eq + i;
+        if (row >= ntok) continue;
+        float* pp = part_row(row) + er;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) pp[16 * db] = acc[rb][db][i];
+      }
+      if (eq == 0 && er < ntok) {
+        float* pp = part_row(er);
+        pp[kHeadDim] = m_run[rb];
+        pp[kHeadDim + 1] = l_tot;
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * eq + i;
@@ -413,7 +441,97 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
   }
 }
 
+// The split extend's merge, one workgroup per (chunk token, query head):
+//   out = v_scale * sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s
+// over the splits' partials (an empty share has m_s = -FLT_MAX, l_s = 0 and
+// O_s = 0, so it weighs nothing).  Thread s < S first takes split s's
+// maximum and sum; then 8 groups of 32 threads each sum every 8th split's
+// O (4 dims a thread, independent loads in flight) and LDS adds the groups.
+__global__ __launch_bounds__(256) void extend_merge_kernel(ExtendParams p) {
+  __shared__ float s_f[kExtMaxSplits];
+  __shared__ float s_wm[4], s_wl[4];
+  __shared__ float4 s_o[8][32];
+  const int seq = blockIdx.y;
+  const int t = (int)(blockIdx.x / (uint32_t)p.Hq), qh = (int)(blockIdx.x % (uint32_t)p.Hq);
+  const int nq = p.num_q_tokens;
+  const int q0 = min(max(p.q_offsets[seq], 0), nq);
+  const int q1 = min(max(p.q_offsets[seq + 1], q0), nq);
+  if (t >= min(q1 - q0, p.max_chunk)) return;
+  const int S = p.splits, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t tok = q0 + t;
+  const int64_t split_stride = (int64_t)nq * p.Hq * kExtPartStride;
+  const float* base = p.part + (tok * p.Hq + qh) * kExtPartStride;
+
+  const float m = tid < S ? base[tid * split_stride + kHeadDim] : -__FLT_MAX__;
+  const float l = tid < S ? base[tid * split_stride + kHeadDim + 1] : 0.0f;
+  float wm = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+  if (lane == 0) s_wm[wave] = wm;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_wm[0], s_wm[1]), fmaxf(s_wm[2], s_wm[3]));
+  const float f = tid < S ? exp2f(m - M) : 0.0f;
+  s_f[tid] = f;
+  float wl = l * f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
+  if (lane == 0) s_wl[wave] = wl;
+  __syncthreads();
+
+  const int sg = tid >> 5, d = 4 * (tid & 31);
+  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = sg; s < S; s += 8) {
+    const float fs = s_f[s];
+    const float4 o = *reinterpret_cast<const float4*>(base + s * split_stride + d);
+    O.x += o.x * fs;
+    O.y += o.y * fs;
+    O.z += o.z * fs;
+    O.w += o.w * fs;
+  }
+  s_o[sg][tid & 31] = O;
+  __syncthreads();
+  if (tid < 32) {
+    float4 a = s_o[0][tid];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) {
+      const float4 b = s_o[g][tid];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    const float L = (s_wl[0] + s_wl[1]) + (s_wl[2] + s_wl[3]);
+    const float r = L > 0.0f ? p.v_scale / L : 0.0f;
+    *reinterpret_cast<float4*>(p.out + (tok * p.Hq + qh) * kHeadDim + d) = make_float4(a.x * r, a.y * r, a.z * r, a.w * r);
+  }
+}
+
 }  // namespace
+
+ExtendGeometry extend_geometry(nvfp4_dtype_t q_dtype, int32_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t max_chunk, int32_t max_prefix) {
+  ExtendGeometry geo{1, 0};
+  if (num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_seqs <= 0 || max_chunk <= 0 || max_prefix < 0)
+    return geo;
+  // split a tile's keys only when the tiles alone fill at most half a round
+  // of resident workgroups: 4-wave workgroups (up to 8 query heads per kv
+  // head) take 3 per CU with bf16 queries (161 VGPRs, 3 waves per SIMD) and
+  // 2 with float32 ones (211 VGPRs), 8-wave workgroups 1.  The split then
+  // fills one round without starting a second (whose stragglers would take
+  // as long as the whole first round), each share at least kExtMinShareKeys keys.
+  const int32_t G = num_q_heads / num_kv_heads;
+  const int64_t round = 256 * (G > 8 ? 1 : q_dtype == NVFP4_DTYPE_F32 ? 2 : 3);
+  const int64_t tiles = (int64_t)((max_chunk + kExtTok - 1) / kExtTok) * num_kv_heads * num_seqs;
+  const int64_t keys = (int64_t)max_prefix + max_chunk;
+  int64_t s = round / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(keys / kExtMinShareKeys, 1));
+  s = std::min<int64_t>(s, kExtMaxSplits);
+  if (s <= 1) return geo;
+  geo.splits = (int32_t)s;
+  const size_t bytes = (size_t)s * (size_t)num_q_tokens * (size_t)num_q_heads * kExtPartStride * sizeof(float);
+  geo.workspace_bytes = (bytes + 255) / 256 * 256;
+  return geo;
+}
 
 hipError_t launch_fp8_rows(const Fp8RowsParams& p, nvfp4_dtype_t dtype, hipStream_t stream) {
   const int64_t n = (int64_t)p.num_tokens * p.H * 8;
@@ -428,12 +546,19 @@ hipError_t launch_fp8_rows(const Fp8RowsParams& p, nvfp4_dtype_t dtype, hipStrea
 
 hipError_t launch_extend(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_chunk == 0 || p.num_q_tokens == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.max_chunk + kExtTok - 1) / kExtTok), (unsigned)p.H, (unsigned)p.num_seqs);
+  if (p.splits < 1 || p.splits > kExtMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((p.max_chunk + kExtTok - 1) / kExtTok * p.splits), (unsigned)p.H, (unsigned)p.num_seqs);
   const dim3 block(p.G <= 8 ? 256 : 512);  // at least 256 threads: the tile loaders
   if (q_dtype == NVFP4_DTYPE_F32)
     hipLaunchKernelGGL(extend_kernel<true>, grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL(extend_kernel<false>, grid, block, 0, stream, p);
+  if (p.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)p.max_chunk * (unsigned)p.Hq, (unsigned)p.num_seqs), dim3(256),
+                       0, stream, p);
+  }
   return hipGetLastError();
 }
 

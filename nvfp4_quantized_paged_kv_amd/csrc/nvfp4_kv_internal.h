@@ -165,7 +165,21 @@ struct ExtendParams {
   int32_t ws_capacity;
   float qk_scale_log2;         // sm_scale * k_ws_scale * log2(e)
   float v_scale;               // v_ws_scale
+  int32_t splits;              // workgroups sharing one tile's keys (1: no split, outputs written directly)
+  float* part;                 // splits > 1: [splits][num_q_tokens][Hq][kExtPartStride] partials (O, max, sum)
 };
+
+constexpr int kExtMaxSplits = 256;      // the merge takes one split per thread of a 256-thread workgroup
+constexpr int kExtMinShareKeys = 1024;  // fewest keys a split workgroup takes
+constexpr int kExtPartStride = 132;     // floats per (split, query token, head) partial: O[128], max (log2), sum, 2 pad
+
+// Workgroups per tile for the split extend (1: none) and its workspace bytes.
+struct ExtendGeometry {
+  int32_t splits;
+  size_t workspace_bytes;
+};
+ExtendGeometry extend_geometry(nvfp4_dtype_t q_dtype, int32_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t max_chunk, int32_t max_prefix);
 
 hipError_t launch_extend(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
 

@@ -199,6 +199,48 @@ def test_fp8_extend_checks():
     assert _ext(nk, wk=FAKE + 8) == 2
 
 
+def _ext_split(nk, q=FAKE, nq=64, hq=64, h=8, n=2, mc=4, mp=8192, ks=1.0, out=FAKE, ws=FAKE, wsb=1 << 26):
+    return nk.lib.nvfp4_fp8_extend_attn_split(ctypes.c_void_p(q), 1, nq, hq, h, n, ctypes.c_void_p(FAKE),
+                                              ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), mc, mp,
+                                              ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 1000, ks, 1.0, 0.088,
+                                              ctypes.c_void_p(out), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_fp8_extend_split_checks_and_sizes():
+    import torch
+
+    nk = _lib()
+
+    def size(*a, dtype=torch.bfloat16):
+        return nk.fp8_extend_attn_split_workspace_bytes(dtype, *a)
+
+    # short chunks over long prefixes: a split, one partial row of 132 floats per split, token and head
+    need = size(64, 64, 8, 2, 4, 8192)
+    assert need > 0 and need % 256 == 0
+    splits = need // (64 * 64 * 132 * 4)
+    assert 2 <= splits <= 256 and need == -(-splits * 64 * 64 * 132 * 4 // 256) * 256
+    assert size(64, 64, 8, 2, 4, 0) == 0              # a 4-token chunk alone: not worth a split
+    assert size(8192, 64, 8, 2, 4096, 8192) == 0      # enough tiles without one
+    assert size(64, 60, 8, 2, 4, 8192) == 0           # invalid grouping
+    assert size(0, 64, 8, 2, 4, 8192) == 0
+    assert size(64, 64, 8, 2, 4, 1 << 16) >= need     # longer prefixes: no fewer splits
+    # one round of resident workgroups: 3 per CU for bf16 queries, 2 for float32 ones
+    assert size(64, 64, 8, 2, 4, 1 << 20) == 768 // 16 * 64 * 64 * 132 * 4
+    assert size(64, 64, 8, 2, 4, 1 << 20, dtype=torch.float32) == 512 // 16 * 64 * 64 * 132 * 4
+    assert nk.lib.nvfp4_fp8_extend_attn_split_workspace_bytes(7, 64, 64, 8, 2, 4, 8192) == 0  # no such dtype
+    assert size(64, 8 * 17, 8, 2, 4, 8192) == 0       # more than 16 query heads per kv head
+    # argument checks, all before any HIP call
+    assert _ext_split(nk, mp=-1) == 1
+    assert _ext_split(nk, ks=0.0) == 1
+    assert _ext_split(nk, hq=60) == 1
+    assert _ext_split(nk, q=FAKE + 4) == 2
+    assert _ext_split(nk, out=0) == 1
+    assert _ext_split(nk, wsb=need - 1) == 3           # workspace too small
+    assert _ext_split(nk, ws=0) == 1                   # a needed workspace missing
+    assert _ext_split(nk, ws=FAKE + 4) == 2            # misaligned workspace
+    assert _ext_split(nk, n=0, q=0, out=0, ws=0, wsb=0) == 0
+
+
 def test_multi_token_decode_checks_and_sizes():
     nk = _lib()
     L = _layer(nk)

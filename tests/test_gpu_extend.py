@@ -95,7 +95,9 @@ def _case(rng, prefixes, chunks, H, gap=5):
 
 
 def _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, qdt, seed, q_scale=1.0, sm=0.088, rows=None,
-                 max_chunk=None, extra_q_rows=0, q=None):
+                 max_chunk=None, extra_q_rows=0, q=None, split_max_prefix=None, oracle_ref=True):
+    """The extend through the C ABI (the split entry point when split_max_prefix
+    is given, its workspace pre-filled with NaN bytes) and the oracle's rows."""
     import nvfp4_quantized_paged_kv_amd as nk
 
     Tq = int(qo[-1]) + extra_q_rows
@@ -106,15 +108,23 @@ def _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, qdt, seed, q_scale=
     pl = np.asarray(prefixes, np.int32)
     mc = int(np.diff(qo).max()) if max_chunk is None else max_chunk
     out = torch.full((Tq, Hq, 128), 12345.0, dtype=torch.float32, device="cuda")
-    nk.fp8_extend_attn(q.cuda(), torch.from_numpy(qo).cuda(), torch.from_numpy(offs).cuda(),
-                       torch.from_numpy(pl).cuda(), mc, torch.from_numpy(ws_k).cuda(), torch.from_numpy(ws_v).cuda(),
-                       ks, vs, sm, out=out)
+    args = (q.cuda(), torch.from_numpy(qo).cuda(), torch.from_numpy(offs).cuda(), torch.from_numpy(pl).cuda(), mc)
+    wsk, wsv = torch.from_numpy(ws_k).cuda(), torch.from_numpy(ws_v).cuda()
+    if split_max_prefix is None:
+        nk.fp8_extend_attn(*args, wsk, wsv, ks, vs, sm, out=out)
+    else:
+        need = nk.fp8_extend_attn_split_workspace_bytes(qdt, Tq, Hq, ws_k.shape[1], len(prefixes), mc,
+                                                        split_max_prefix)
+        _say(f"  split workspace {need} bytes")
+        assert need > 0, "the split extend chose no split for this case"
+        part = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+        nk.fp8_extend_attn_split(*args, split_max_prefix, wsk, wsv, ks, vs, sm, out=out, workspace=part)
     torch.cuda.synchronize()
     got = out.cpu().numpy().reshape(Tq * Hq, 128)
     qf = host_f32(q)[: int(qo[-1])]
     if rows is None:
         rows = np.arange(int(qo[-1]) * Hq, dtype=np.int64)
-    ref = oracle.extend_attention(ws_k, ws_v, ks, vs, qf, qo, offs, pl, sm, rows=rows)
+    ref = oracle.extend_attention(ws_k, ws_v, ks, vs, qf, qo, offs, pl, sm, rows=rows) if oracle_ref else None
     return got, rows, ref
 
 
@@ -285,3 +295,70 @@ def test_extend_mixed_step_shape_sampled():
     got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, torch.bfloat16, seed=6, rows=rows)
     err = row_rel_err(got[rows], ref)
     assert err.max() <= ATTN_TOL, err.max()
+
+
+# ------------------------------------------------- split extend (keys shared)
+@pytest.mark.parametrize("prefixes,chunks,H,G,qdt,max_prefix", [
+    ([5000, 3071], [1, 16], 2, 8, torch.bfloat16, None),          # verification-like: short chunks, long prefixes
+    ([4000, 0, 2500], [7, 5, 33], 1, 16, torch.float32, None),    # 512-thread workgroups, float32 Q, 3-tile chunk
+    ([2047, 2049, 3000], [4, 0, 9], 3, 3, torch.bfloat16, None),  # odd group, an empty chunk
+    ([10, 3], [3, 2], 2, 4, torch.bfloat16, 1 << 20),             # over-stated prefix bound: most shares empty
+])
+def test_extend_split_matches_oracle_and_unsplit(prefixes, chunks, H, G, qdt, max_prefix):
+    _say(f"case: split extend prefixes={prefixes} chunks={chunks} H={H} G={G} q={qdt} max_prefix={max_prefix}")
+    rng = np.random.default_rng(sum(prefixes) + sum(chunks) + G + 1)
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, H)
+    mp = max(prefixes) if max_prefix is None else max_prefix
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, H * G, qdt, seed=G, split_max_prefix=mp)
+    err = row_rel_err(got[rows], ref)
+    assert err.max() <= ATTN_TOL, (err.max(), int(np.argmax(err)))
+    whole, _, _ = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, H * G, qdt, seed=G, oracle_ref=False)
+    d = row_rel_err(got[rows], whole[rows])
+    _say(f"  max row rel err: vs oracle {err.max():.2e}, vs unsplit {d.max():.2e}")
+    assert d.max() <= 2e-5, d.max()  # the same sums in another fp32 order
+
+
+def test_extend_split_rows_outside_chunks_are_untouched():
+    """With keys shared: tokens past max_chunk_len and query rows after the last chunk are not written."""
+    _say("case: split extend untouched rows")
+    rng = np.random.default_rng(63)
+    prefixes, chunks = [5000, 300], [20, 12]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    Hq = 8
+    got, rows, ref = _extend_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, torch.bfloat16, seed=4, max_chunk=16,
+                                  extra_q_rows=5, split_max_prefix=5000)
+    got = got.reshape(-1, Hq, 128)
+    ref = ref.reshape(-1, Hq, 128)
+    computed = [t for i in range(2) for t in range(qo[i], qo[i] + min(16, chunks[i]))]
+    assert row_rel_err(got[computed], ref[computed]).max() <= ATTN_TOL
+    skipped = [t for t in range(got.shape[0]) if t not in computed]
+    assert np.all(got[skipped] == 12345.0)
+
+
+def test_extend_split_workspace_reuse_smaller_call():
+    """One workspace, two calls in a row, the second smaller: its results do not depend on the first's partials."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say("case: split extend workspace reuse")
+    rng = np.random.default_rng(64)
+    H, Hq = 2, 16
+    big = _case(rng, [6000, 4000], [9, 3], H)
+    small = _case(rng, [3000], [2], H)
+    bf = torch.bfloat16
+    need = nk.fp8_extend_attn_split_workspace_bytes(bf, 12, Hq, H, 2, 9, 6000)
+    assert need >= nk.fp8_extend_attn_split_workspace_bytes(bf, 2, Hq, H, 1, 2, 3000) > 0
+    part = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for (ws_k, ws_v, ks, vs, offs, qo), prefixes in ((big, [6000, 4000]), (small, [3000])):
+        Tq, mc = int(qo[-1]), int(np.diff(qo).max())
+        q = synth.queries(Tq, Hq, torch.bfloat16, "cpu", 9, 7)
+        out = nk.fp8_extend_attn_split(q.cuda(), torch.from_numpy(qo).cuda(), torch.from_numpy(offs).cuda(),
+                                       torch.from_numpy(np.asarray(prefixes, np.int32)).cuda(), mc, max(prefixes),
+                                       torch.from_numpy(ws_k).cuda(), torch.from_numpy(ws_v).cuda(), ks, vs, 0.088,
+                                       workspace=part)
+        torch.cuda.synchronize()
+        ref = oracle.extend_attention(ws_k, ws_v, ks, vs, host_f32(q), qo, offs, np.asarray(prefixes, np.int32), 0.088,
+                                      rows=np.arange(Tq * Hq, dtype=np.int64))
+        outs.append(row_rel_err(out.cpu().numpy().reshape(-1, 128), ref).max())
+    _say(f"  max row rel err per call {outs}")
+    assert max(outs) <= ATTN_TOL, outs
