@@ -340,6 +340,40 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_split(const void* q, nvfp4_dtype_
                                                      float sm_scale, float* out, void* workspace,
                                                      size_t workspace_bytes, void* stream);
 
+/* The same extend attention in FP8 arithmetic, on gfx950's FP8 (E4M3) MFMA:
+ * the workspace's E4M3 K and V bytes enter the matrix cores as they are
+ * (blog section 3: extend attention consumes the FP8 workspace directly),
+ * and so do Q and the softmax weights, each rounded to E4M3:
+ *   Q8 = E4M3(q * 2^-E) per (query token, query head) row, E the smallest
+ *        integer with max|q| <= 448 * 2^E (round to nearest, ties to even);
+ *   x_t = sum_d Q8_d * E4M3(ws_k[row_t][h][d]) * c * 2^E, c = float32 of
+ *        sm_scale * k_ws_scale * log2(e)  (base-2 logits, fp32 accumulation);
+ *   M  = ceil(max_t x_t);  W8_t = E4M3(2^(x_t - M + 8))  (at most 256; 2^(x_t - M)
+ *        when |M| >= 2^27, where float32 cannot hold M - 8 exactly);
+ *   out = v_ws_scale * sum_t W8_t * E4M3(ws_v[row_t][h][d]) / sum_t W8_t.
+ * The kernel keeps an integer running maximum instead of M (rescales by
+ * exact powers of two), so weights below 2^-14 of the row's largest can round
+ * at a finer scale than M's; the accumulation error of the FP8 matrix cores
+ * is within 2^-11 of the largest product per 64-term dot product.  Each
+ * element of Q and of the weights carries up to 2^-4 relative rounding error:
+ * this is a lower-precision contract than nvfp4_fp8_extend_attn's (about
+ * 1e-2 of a row's largest value on the synthetic workloads, against 1e-3),
+ * for about 4x less matrix-core work per key.  Arguments, layouts, errors and
+ * the optional key split (with its workspace) are those of
+ * nvfp4_fp8_extend_attn_split; the split sizes differ, so the workspace size
+ * comes from nvfp4_fp8_extend_attn_f8_workspace_bytes. */
+NVFP4_API size_t nvfp4_fp8_extend_attn_f8_workspace_bytes(nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                                           int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                                           int32_t max_chunk_len, int32_t max_prefix_len);
+NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_f8(const void* q, nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                                  const int32_t* q_offsets, const int32_t* ws_offsets,
+                                                  const int32_t* prefix_lens, int32_t max_chunk_len,
+                                                  int32_t max_prefix_len, const uint8_t* ws_k, const uint8_t* ws_v,
+                                                  int32_t ws_capacity_tokens, float k_ws_scale, float v_ws_scale,
+                                                  float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                                  void* stream);
+
 /* ------------------------------------------------------------------ MXFP4
  * The 4-bit format the NVFP4 pages compare against (nmedialink.com, accuracy
  * section and Fig. 6: NVFP4 KV caches score above MXFP4 ones, credited to the

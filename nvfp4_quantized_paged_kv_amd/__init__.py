@@ -49,6 +49,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_fp8_extend_attn",
     "nvfp4_fp8_extend_attn_split_workspace_bytes",
     "nvfp4_fp8_extend_attn_split",
+    "nvfp4_fp8_extend_attn_f8_workspace_bytes",
+    "nvfp4_fp8_extend_attn_f8",
     "mxfp4_kv_quantize_append",
     "mxfp4_paged_decode_attn",
     "nvfp4_kv_quantize_append_hadamard",
@@ -148,6 +150,10 @@ def _load():
     L.nvfp4_fp8_extend_attn_split.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp, i32,
                                               f32, f32, f32, vp, vp, sz, vp]
     L.nvfp4_fp8_extend_attn_split.restype = ctypes.c_int
+    L.nvfp4_fp8_extend_attn_f8_workspace_bytes.argtypes = L.nvfp4_fp8_extend_attn_split_workspace_bytes.argtypes
+    L.nvfp4_fp8_extend_attn_f8_workspace_bytes.restype = sz
+    L.nvfp4_fp8_extend_attn_f8.argtypes = L.nvfp4_fp8_extend_attn_split.argtypes
+    L.nvfp4_fp8_extend_attn_f8.restype = ctypes.c_int
     mp = ctypes.POINTER(CMxLayer)
     L.mxfp4_kv_quantize_append.argtypes = [mp, vp, vp, ctypes.c_int, i32, i64, vp, vp]
     L.mxfp4_kv_quantize_append.restype = ctypes.c_int
@@ -512,6 +518,36 @@ def fp8_extend_attn_split_workspace_bytes(q_dtype: torch.dtype, num_q_tokens: in
         raise ValueError(f"unsupported q dtype {q_dtype} (bfloat16 or float32)")
     return int(lib.nvfp4_fp8_extend_attn_split_workspace_bytes(code, num_q_tokens, num_q_heads, num_kv_heads,
                                                                 num_seqs, max_chunk_len, max_prefix_len))
+
+
+def fp8_extend_attn_f8_workspace_bytes(q_dtype: torch.dtype, num_q_tokens: int, num_q_heads: int,
+                                       num_kv_heads: int, num_seqs: int, max_chunk_len: int,
+                                       max_prefix_len: int) -> int:
+    code = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(q_dtype)
+    if code is None:
+        raise ValueError(f"unsupported q dtype {q_dtype} (bfloat16 or float32)")
+    return int(lib.nvfp4_fp8_extend_attn_f8_workspace_bytes(code, num_q_tokens, num_q_heads, num_kv_heads,
+                                                             num_seqs, max_chunk_len, max_prefix_len))
+
+
+def fp8_extend_attn_f8(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.Tensor, prefix_lens: torch.Tensor,
+                       max_chunk_len: int, max_prefix_len: int, ws_k: torch.Tensor, ws_v: torch.Tensor,
+                       k_ws_scale: float, v_ws_scale: float, sm_scale: float, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp8_extend_attn in FP8 arithmetic (Q and the softmax weights rounded to E4M3, FP8 MFMA);
+    workspace: device bytes of fp8_extend_attn_f8_workspace_bytes (allocated when needed and not given)."""
+    n, Tq, Hq, out = _extend_args(q, q_offsets, ws_offsets, prefix_lens, ws_k, ws_v, out)
+    need = fp8_extend_attn_f8_workspace_bytes(q.dtype, Tq, Hq, ws_k.shape[1], n, int(max_chunk_len),
+                                              int(max_prefix_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.nvfp4_fp8_extend_attn_f8(_ptr(q), _dtype_code(q), Tq, Hq, ws_k.shape[1], n, _ptr(q_offsets),
+                                      _ptr(ws_offsets), _ptr(prefix_lens), int(max_chunk_len), int(max_prefix_len),
+                                      _ptr(ws_k), _ptr(ws_v), ws_k.shape[0], float(k_ws_scale), float(v_ws_scale),
+                                      float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_fp8_extend_attn_f8")
+    return out
 
 
 def fp8_extend_attn_split(q: torch.Tensor, q_offsets: torch.Tensor, ws_offsets: torch.Tensor,

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libnvfp4kv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["api.cpp", "quant_append.hip", "decode_attn.hip", "decode_noalloc.hip", "dequant_ws.hip", "fp8_extend.hip",
-           "mxfp4_append.hip", "mla_decode.hip"]
+           "extend_f8.hip", "mxfp4_append.hip", "mla_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -463,6 +463,43 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_split(const void* q, nvfp4_dtype_
   return from_hip(launch_extend(p, q_dtype, static_cast<hipStream_t>(stream)));
 }
 
+NVFP4_API size_t nvfp4_fp8_extend_attn_f8_workspace_bytes(nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                                           int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                                           int32_t max_chunk_len, int32_t max_prefix_len) {
+  if (!dtype_ok(q_dtype) || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      num_q_heads / num_kv_heads > kMaxGroup)
+    return 0;
+  return extend_f8_geometry(num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_chunk_len, max_prefix_len)
+      .workspace_bytes;
+}
+
+NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_f8(const void* q, nvfp4_dtype_t q_dtype, int32_t num_q_tokens,
+                                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                                  const int32_t* q_offsets, const int32_t* ws_offsets,
+                                                  const int32_t* prefix_lens, int32_t max_chunk_len,
+                                                  int32_t max_prefix_len, const uint8_t* ws_k, const uint8_t* ws_v,
+                                                  int32_t ws_capacity_tokens, float k_ws_scale, float v_ws_scale,
+                                                  float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                                  void* stream) {
+  if (max_prefix_len < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  ExtendParams p;
+  bool empty = false;
+  const nvfp4_status_t st = extend_params(q, q_dtype, num_q_tokens, num_q_heads, num_kv_heads, num_seqs, q_offsets,
+                                          ws_offsets, prefix_lens, max_chunk_len, ws_k, ws_v, ws_capacity_tokens,
+                                          k_ws_scale, v_ws_scale, sm_scale, out, p, &empty);
+  if (st != NVFP4_OK || empty) return st;
+  const ExtendGeometry geo =
+      extend_f8_geometry(num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_chunk_len, max_prefix_len);
+  if (geo.splits > 1) {
+    if (workspace_bytes < geo.workspace_bytes) return NVFP4_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 16)) return NVFP4_ERR_UNSUPPORTED;
+    p.splits = geo.splits;
+    p.part = static_cast<float*>(workspace);
+  }
+  return from_hip(launch_extend_f8(p, q_dtype, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- MXFP4
 
 }  // extern "C"

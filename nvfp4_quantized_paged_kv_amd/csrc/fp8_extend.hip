@@ -556,9 +556,14 @@ hipError_t launch_extend(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream
   if (p.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)p.max_chunk * (unsigned)p.Hq, (unsigned)p.num_seqs), dim3(256),
-                       0, stream, p);
+    return launch_extend_merge(p, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_extend_merge(const ExtendParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)p.max_chunk * (unsigned)p.Hq, (unsigned)p.num_seqs), dim3(256),
+                     0, stream, p);
   return hipGetLastError();
 }
 

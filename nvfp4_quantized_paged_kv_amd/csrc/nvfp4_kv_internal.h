@@ -182,5 +182,11 @@ ExtendGeometry extend_geometry(nvfp4_dtype_t q_dtype, int32_t num_q_tokens, int3
                                int32_t num_seqs, int32_t max_chunk, int32_t max_prefix);
 
 hipError_t launch_extend(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
+// the split extend's merge of p.splits partials in p.part into p.out
+hipError_t launch_extend_merge(const ExtendParams& p, hipStream_t stream);
+// the extend in FP8 arithmetic (Q and the softmax weights in E4M3, FP8 MFMA)
+ExtendGeometry extend_f8_geometry(int32_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                  int32_t max_chunk, int32_t max_prefix);
+hipError_t launch_extend_f8(const ExtendParams& p, nvfp4_dtype_t q_dtype, hipStream_t stream);
 
 }  // namespace nvfp4kv

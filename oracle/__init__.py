@@ -91,6 +91,8 @@ def lib():
     L.nvfp4o_extend_attention.argtypes = [_u8p, _u8p, _int, _flt, _flt, _f32p, _int, _int, _i32p, _i32p, _i32p, _flt,
                                           _i64p, _i64, _f64p]
     L.nvfp4o_extend_attention.restype = None
+    L.nvfp4o_extend_attention_fp8.argtypes = L.nvfp4o_extend_attention.argtypes + [_f64p]
+    L.nvfp4o_extend_attention_fp8.restype = None
     L.nvfp4o_e8m0_value.argtypes = [_int]
     L.nvfp4o_e8m0_value.restype = _dbl
     L.nvfp4o_e8m0_scale_for.argtypes = [_dbl]
@@ -259,6 +261,34 @@ def extend_attention(ws_k: np.ndarray, ws_v: np.ndarray, k_ws_scale: float, v_ws
                                   float(np.float32(k_ws_scale)), float(np.float32(v_ws_scale)), q, Hq, n, qo, wo, pl,
                                   float(np.float32(sm_scale)), rows, rows.size, out)
     return out
+
+
+def extend_attention_fp8(ws_k: np.ndarray, ws_v: np.ndarray, k_ws_scale: float, v_ws_scale: float, q: np.ndarray,
+                         q_offsets, ws_offsets, prefix_lens, sm_scale: float, rows=None):
+    """extend_attention in FP8 arithmetic (reading R11: Q and the softmax weights rounded to E4M3).
+
+    Returns (out float64 [len(rows), 128], tol float64 [len(rows)]): tol bounds the
+    difference to a kernel computing the same with float32 logits, an integer running
+    maximum and FP8 matrix cores (see the C source)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    Tq, Hq, D = q.shape
+    H = ws_k.shape[1]
+    assert D == 128 and Hq % H == 0 and ws_k.shape == ws_v.shape
+    qo = np.ascontiguousarray(q_offsets, dtype=np.int32)
+    wo = np.ascontiguousarray(ws_offsets, dtype=np.int32)
+    pl = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+    n = pl.size
+    assert qo.size == n + 1 and wo.size >= n and qo[-1] == Tq
+    assert all(wo[i] + pl[i] + (qo[i + 1] - qo[i]) <= ws_k.shape[0] for i in range(n))
+    if rows is None:
+        rows = np.arange(Tq * Hq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, 128), np.float64)
+    tol = np.zeros(rows.size, np.float64)
+    lib().nvfp4o_extend_attention_fp8(np.ascontiguousarray(ws_k).reshape(-1), np.ascontiguousarray(ws_v).reshape(-1),
+                                      H, float(np.float32(k_ws_scale)), float(np.float32(v_ws_scale)), q, Hq, n, qo,
+                                      wo, pl, float(np.float32(sm_scale)), rows, rows.size, out, tol)
+    return out, tol
 
 
 # -------------------------------------------------------------------- MXFP4

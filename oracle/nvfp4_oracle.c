@@ -35,6 +35,9 @@
  *      the MXFP4 section below.
  *   R10 the Hadamard rotation of K (and Q) is the 128-point Sylvester matrix
  *      with power-of-two scales; see the Hadamard section below.
+ *   R11 extend attention in FP8 arithmetic rounds Q (per row, power-of-two
+ *      scale) and the softmax weights (relative to the ceiling of the row's
+ *      maximum base-2 logit, 2^8 headroom) to E4M3; see that section below.
  *
  * Exactness of the float64 quotients used below.  Inputs are float32 (24-bit
  * significands), g is float32, block scales are E4M3 (4-bit significands) and
@@ -391,6 +394,130 @@ void nvfp4o_extend_attention(const uint8_t* ws_k, const uint8_t* ws_v, int Hkv, 
     }
     free(s);
     for (int d = 0; d < 128; ++d) o[d] /= l;
+  }
+}
+
+/* ------------------------------- extend attention in FP8 arithmetic
+ * [MW] §3: extend attention consumes the FP8 workspace directly.  On
+ * hardware whose matrix cores take E4M3 operands, Q and the softmax weights
+ * enter them as E4M3 too; the pages do not spell that arithmetic out, so this
+ * is reading R11 (the plainest FP8 statement of the same attention):
+ *   Q8_d = E4M3(q_d * 2^-E)   E = the smallest integer with max_d |q_d| <= 448 * 2^E
+ *                             (0 for a zero row); nearest, ties to even (R1, R4);
+ *   x_t  = sum_d Q8_d * E4M3(k_td) * c * 2^E,  c = float32(sm_scale * k_ws_scale * log2 e)
+ *   M    = ceil(max_t x_t);   W_t = E4M3(2^(x_t - M + h))   (<= 256)
+ *                             h = 8 for |M| < 2^27, else 0 (float32 holds M - 8
+ *                             exactly only below 2^27);
+ *   o_d  = v_ws_scale * sum_t W_t E4M3(v_td) / sum_t W_t.
+ * Keys and sequences as in nvfp4o_extend_attention.  The sums are exact in
+ * float64 up to the one rounding of each product with c (E4M3 products have
+ * at most 8 significant bits over 36 binades; 128 of them fit 53 bits).
+ *
+ * tol[r] bounds |o_GPU - o| for one row of a kernel that computes the same
+ * thing with float32 logits and an integer running maximum (it rescales by
+ * exact powers of two), on FP8 matrix cores whose dot products of up to 64
+ * terms are within 2^-11 of their largest product.  It sums:
+ *   - accumulation: 2^-10 * sum_t W_t * vmax_t over the numerator, 2^-10 * L
+ *     over the sum L = sum_t W_t (vmax_t = max_d |v_td| in output units);
+ *   - rounding flips: a weight whose exact value lies within the relative
+ *     error e_t of the kernel's 2^(x - m + 8) from an E4M3 midpoint may take
+ *     the neighbouring value; e_t = ln2 * (c * 2^E * (2^-10 * max_d |Q8_d k_td|
+ *     + 2^-23 * sum_d |Q8_d k_td|) + 2^-22 * |x_t| + 2^-22) + 2^-21;
+ *   - small weights (below 2^-5 at M): rounded at another power-of-two
+ *     scale, within 2^-8 of this one;
+ * each weight change times vmax_t in the numerator and alone in L, then
+ * |dN| / (L - |dL|) + max_d |o_d| * |dL| / (L - |dL|), plus 2^-20 * max |o|.
+ * rows[r] = (query row) * Hq + qh; out is n_rows x 128, tol n_rows. */
+static int e4m3_code_of(double y) { return nvfp4o_e4m3_encode(y); }
+
+void nvfp4o_extend_attention_fp8(const uint8_t* ws_k, const uint8_t* ws_v, int Hkv, float k_ws_scale,
+                                 float v_ws_scale, const float* q, int Hq, int num_seqs, const int32_t* q_offsets,
+                                 const int32_t* ws_offsets, const int32_t* prefix_lens, float sm_scale,
+                                 const int64_t* rows, int64_t n_rows, double* out, double* tol) {
+  const int G = Hq / Hkv;
+  const float c = (float)((double)sm_scale * (double)k_ws_scale * 1.4426950408889634);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t qrow = rows[r] / Hq;
+    const int qh = (int)(rows[r] % Hq), h = qh / G;
+    int i = 0;
+    while (i < num_seqs - 1 && q_offsets[i + 1] <= qrow) ++i;
+    const int64_t j = qrow - q_offsets[i];
+    const int64_t n = (int64_t)prefix_lens[i] + j + 1;
+    const float* qv = q + rows[r] * 128;
+    double* o = out + r * 128;
+    /* Q8 */
+    double amax = 0.0;
+    for (int d = 0; d < 128; ++d) amax = fmax(amax, fabs((double)qv[d]));
+    int E = 0;
+    if (amax > 0.0) {
+      E = -200;
+      while (amax > 448.0 * ldexp(1.0, E)) ++E;
+    }
+    double q8[128];
+    for (int d = 0; d < 128; ++d) {
+      const double a = ldexp((double)qv[d], -E);
+      const double mag = nvfp4o_e4m3_value(e4m3_code_of(fabs(a)));
+      q8[d] = signbit(a) ? -mag : mag;
+    }
+    const double cs = (double)c * ldexp(1.0, E);
+    double* x = (double*)malloc((size_t)n * sizeof(double));
+    double* ex = (double*)malloc((size_t)n * sizeof(double));
+    double xmax = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+      const uint8_t* kr = ws_k + (((int64_t)ws_offsets[i] + t) * Hkv + h) * 128;
+      double sdot = 0.0, pmax = 0.0, psum = 0.0;
+      for (int d = 0; d < 128; ++d) {
+        const double pr = q8[d] * nvfp4o_e4m3_value(kr[d]);
+        sdot += pr;
+        pmax = fmax(pmax, fabs(pr));
+        psum += fabs(pr);
+      }
+      x[t] = sdot * cs;
+      ex[t] = 0.6931471805599453 * (fabs(cs) * (ldexp(pmax, -10) + ldexp(psum, -23)) + ldexp(fabs(x[t]), -22) + ldexp(1.0, -22)) +
+              ldexp(1.0, -21);
+      if (x[t] > xmax) xmax = x[t];
+    }
+    const double M = ceil(xmax);
+    double l = 0.0;
+    for (int d = 0; d < 128; ++d) o[d] = 0.0;
+    double wsum_v = 0.0, flip_l = 0.0, flip_n = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+      const uint8_t* vr = ws_v + (((int64_t)ws_offsets[i] + t) * Hkv + h) * 128;
+      const double y = exp2(x[t] - M + (fabs(M) < 134217728.0 ? 8.0 : 0.0));
+      const int code = e4m3_code_of(y);
+      const double w = nvfp4o_e4m3_value(code);
+      double vmax = 0.0;
+      for (int d = 0; d < 128; ++d) {
+        const double v = nvfp4o_e4m3_value(vr[d]) * (double)v_ws_scale;
+        o[d] += w * v;
+        vmax = fmax(vmax, fabs(v));
+      }
+      l += w;
+      wsum_v += w * vmax;
+      /* a flip to a neighbouring code, or a small weight rounded at another scale */
+      double dw = 0.0;
+      if (y < 0.03125) dw = ldexp(1.0, -8);
+      const double lo = code > 0 ? 0.5 * (nvfp4o_e4m3_value(code - 1) + w) : -1.0;
+      const double hi = code < 0x7E ? 0.5 * (w + nvfp4o_e4m3_value(code + 1)) : INFINITY;
+      if (y * (1.0 - ex[t]) <= lo || y * (1.0 + ex[t]) >= hi) {
+        const double step = fmax(code > 0 ? w - nvfp4o_e4m3_value(code - 1) : 0.0,
+                                 code < 0x7E ? nvfp4o_e4m3_value(code + 1) - w : 0.0);
+        dw = fmax(dw, step);
+      }
+      flip_l += dw;
+      flip_n += dw * vmax;
+    }
+    free(x);
+    free(ex);
+    double omax = 0.0;
+    for (int d = 0; d < 128; ++d) {
+      o[d] = l > 0.0 ? o[d] / l : 0.0;
+      omax = fmax(omax, fabs(o[d]));
+    }
+    const double dn = ldexp(wsum_v, -10) + flip_n;
+    const double dl = ldexp(l, -10) + flip_l;
+    tol[r] = (l > dl) ? (dn + omax * dl) / (l - dl) + ldexp(omax, -20) : INFINITY;
   }
 }
 

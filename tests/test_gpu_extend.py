@@ -362,3 +362,133 @@ def test_extend_split_workspace_reuse_smaller_call():
         outs.append(row_rel_err(out.cpu().numpy().reshape(-1, 128), ref).max())
     _say(f"  max row rel err per call {outs}")
     assert max(outs) <= ATTN_TOL, outs
+
+
+# ------------------------------------------- extend attention in FP8 arithmetic
+def _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, qdt, seed, q_scale=1.0, sm=0.088, rows=None,
+                    max_chunk=None, max_prefix=None, extra_q_rows=0):
+    """The FP8-arithmetic extend through the C ABI (a needed split workspace pre-filled
+    with NaN bytes), the oracle's FP8 statement with its per-row bound, and the exact oracle."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    Tq = int(qo[-1]) + extra_q_rows
+    q = synth.queries(Tq, Hq, qdt, "cpu", seed, 7)
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(qdt)
+    pl = np.asarray(prefixes, np.int32)
+    mc = int(np.diff(qo).max()) if max_chunk is None else max_chunk
+    mp = int(pl.max()) if max_prefix is None else max_prefix
+    out = torch.full((Tq, Hq, 128), 12345.0, dtype=torch.float32, device="cuda")
+    need = nk.fp8_extend_attn_f8_workspace_bytes(qdt, Tq, Hq, ws_k.shape[1], len(prefixes), mc, mp)
+    part = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    _say(f"  f8 split workspace {need} bytes")
+    nk.fp8_extend_attn_f8(q.cuda(), torch.from_numpy(qo).cuda(), torch.from_numpy(offs).cuda(),
+                          torch.from_numpy(pl).cuda(), mc, mp, torch.from_numpy(ws_k).cuda(),
+                          torch.from_numpy(ws_v).cuda(), ks, vs, sm, out=out, workspace=part)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(Tq * Hq, 128)
+    qf = host_f32(q)[: int(qo[-1])]
+    if rows is None:
+        rows = np.arange(int(qo[-1]) * Hq, dtype=np.int64)
+    emul, tol = oracle.extend_attention_fp8(ws_k, ws_v, ks, vs, qf, qo, offs, pl, sm, rows=rows)
+    exact = oracle.extend_attention(ws_k, ws_v, ks, vs, qf, qo, offs, pl, sm, rows=rows)
+    return got, rows, emul, tol, exact, need
+
+
+def _check_f8(got, rows, emul, tol, exact):
+    d = np.abs(got[rows] - emul).max(axis=1)
+    scale = np.abs(emul).max(axis=1)
+    bad = np.nonzero(d > tol + 1e-6 * scale)[0]
+    rel = d / np.maximum(scale, 1e-30)
+    ex = row_rel_err(got[rows], exact)
+    _say(f"  vs FP8 statement: max row err {rel.max():.2e} (median {np.median(rel):.2e}), bound median "
+         f"{np.median(tol / np.maximum(scale, 1e-30)):.2e}; vs exact attention: max {ex.max():.2e} "
+         f"(median {np.median(ex):.2e})")
+    assert bad.size == 0, (bad[:5], d[bad[:5]], tol[bad[:5]])
+    return ex
+
+
+@pytest.mark.parametrize("prefixes,chunks,H,G,qdt", [
+    ([0], [100], 2, 4, torch.bfloat16),                 # prefill: the chunk only
+    ([0, 37, 300], [1, 50, 33], 2, 8, torch.bfloat16),  # ragged extends, single-token chunk
+    ([200], [40], 1, 16, torch.float32),                # 512-thread workgroups, float32 Q
+    ([70, 5], [17, 64], 3, 3, torch.bfloat16),          # odd group: a half-empty wave
+    ([31, 32, 33], [15, 16, 17], 1, 1, torch.float32),  # tile and page boundaries, one head
+    ([63, 64, 65, 127], [1, 64, 65, 2], 2, 8, torch.bfloat16),  # 64-key tile boundaries
+])
+def test_extend_f8_matches_fp8_statement(prefixes, chunks, H, G, qdt):
+    _say(f"case: f8 extend prefixes={prefixes} chunks={chunks} H={H} G={G} q={qdt}")
+    rng = np.random.default_rng(sum(prefixes) + sum(chunks) + G + 2)
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, H)
+    got, rows, emul, tol, exact, _ = _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, H * G, qdt, seed=G)
+    ex = _check_f8(got, rows, emul, tol, exact)
+    assert ex.max() <= 0.1  # the E4M3 roundings of Q and of the weights (2^-4 each), well inside
+
+
+@pytest.mark.parametrize("prefixes,chunks,H,G,qdt,max_prefix", [
+    ([5000, 3071], [1, 16], 2, 8, torch.bfloat16, None),          # short chunks over long prefixes: keys split
+    ([4000, 0, 2500], [7, 5, 33], 1, 16, torch.float32, None),    # 512-thread workgroups, float32 Q
+    ([10, 3], [3, 2], 2, 4, torch.bfloat16, 1 << 20),             # over-stated prefix bound: most shares empty
+])
+def test_extend_f8_split_matches_fp8_statement(prefixes, chunks, H, G, qdt, max_prefix):
+    _say(f"case: f8 split extend prefixes={prefixes} chunks={chunks} H={H} G={G} q={qdt} max_prefix={max_prefix}")
+    rng = np.random.default_rng(sum(prefixes) + sum(chunks) + G + 3)
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, H)
+    got, rows, emul, tol, exact, need = _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, H * G, qdt, seed=G,
+                                                        max_prefix=max_prefix)
+    assert need > 0, "no split chosen"
+    _check_f8(got, rows, emul, tol, exact)
+
+
+@pytest.mark.parametrize("q_scale", [30.0, 300.0])
+def test_extend_f8_peaked_softmax(q_scale):
+    _say(f"case: f8 extend peaked q_scale={q_scale}")
+    rng = np.random.default_rng(161)
+    prefixes, chunks = [150, 9], [40, 70]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    got, rows, emul, tol, exact, _ = _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, 16, torch.bfloat16, 3,
+                                                     q_scale=q_scale)
+    _check_f8(got, rows, emul, tol, exact)
+
+
+def test_extend_f8_huge_logits_stay_finite():
+    _say("case: f8 extend huge logits")
+    rng = np.random.default_rng(167)
+    prefixes, chunks = [90, 0], [33, 20]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    got, rows, emul, tol, exact, _ = _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, 16, torch.bfloat16, 5,
+                                                     sm=1e12)
+    assert np.isfinite(got[rows]).all()
+    _check_f8(got, rows, emul, tol, exact)
+
+
+def test_extend_f8_rows_outside_chunks_are_untouched():
+    _say("case: f8 extend untouched rows")
+    rng = np.random.default_rng(162)
+    prefixes, chunks = [20, 40], [30, 12]
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, 2)
+    Hq = 8
+    got, rows, emul, tol, exact, _ = _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, torch.bfloat16, 4,
+                                                     max_chunk=16, extra_q_rows=5)
+    got = got.reshape(-1, Hq, 128)
+    computed = [t for i in range(2) for t in range(qo[i], qo[i] + min(16, chunks[i]))]
+    crow = np.array([t * Hq + h for t in computed for h in range(Hq)], np.int64)
+    _check_f8(got.reshape(-1, 128), crow, emul[crow], tol[crow], exact[crow])
+    skipped = [t for t in range(got.shape[0]) if t not in computed]
+    assert np.all(got[skipped] == 12345.0)
+
+
+def test_extend_f8_mixed_step_shape_sampled():
+    """The mixed serving step's extend shape (64 q / 8 kv heads, 2048-token chunks over
+    long prefixes) in FP8 arithmetic, on sampled rows."""
+    _say("case: f8 extend mixed-step shape, sampled rows")
+    rng = np.random.default_rng(181)
+    prefixes, chunks = [9000, 700], [2048, 2048]
+    H, Hq = 8, 64
+    ws_k, ws_v, ks, vs, offs, qo = _case(rng, prefixes, chunks, H, gap=0)
+    Tq = int(qo[-1])
+    rows = np.unique(np.concatenate([rng.integers(0, Tq * Hq, 150),
+                                     [0, Hq - 1, 2047 * Hq, 2048 * Hq, Tq * Hq - 1]])).astype(np.int64)
+    got, rows, emul, tol, exact, _ = _extend_f8_both(ws_k, ws_v, ks, vs, offs, qo, prefixes, Hq, torch.bfloat16, 6,
+                                                     rows=rows)
+    _check_f8(got, rows, emul, tol, exact)
