@@ -344,10 +344,11 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_split(const void* q, nvfp4_dtype_
  * the workspace's E4M3 K and V bytes enter the matrix cores as they are
  * (blog section 3: extend attention consumes the FP8 workspace directly),
  * and so do Q and the softmax weights, each rounded to E4M3:
- *   Q8 = E4M3(q * 2^-E) per (query token, query head) row, E the smallest
- *        integer with max|q| <= 448 * 2^E (round to nearest, ties to even);
- *   x_t = sum_d Q8_d * E4M3(ws_k[row_t][h][d]) * c * 2^E, c = float32 of
- *        sm_scale * k_ws_scale * log2(e)  (base-2 logits, fp32 accumulation);
+ *   c  = float32 of sm_scale * k_ws_scale * log2(e), u = float32(q * c);
+ *   Q8 = E4M3(u * 2^-E) per (query token, query head) row, E the smallest
+ *        integer with max|u| <= 448 * 2^E (round to nearest, ties to even);
+ *   x_t = 2^E * sum_d Q8_d * E4M3(ws_k[row_t][h][d])  (base-2 logits, fp32
+ *        accumulation);
  *   M  = ceil(max_t x_t);  W8_t = E4M3(2^(x_t - M + 8))  (at most 256; 2^(x_t - M)
  *        when |M| >= 2^27, where float32 cannot hold M - 8 exactly);
  *   out = v_ws_scale * sum_t W8_t * E4M3(ws_v[row_t][h][d]) / sum_t W8_t.

@@ -6,11 +6,11 @@
 // prefix from the FP8 workspace and over its own FP8 K/V.  The K and V bytes
 // enter the MFMA as they are (no widening); so do Q and the softmax weights,
 // each rounded to E4M3:
-//   - Q row (query token, query head): codes E4M3(q * 2^-E), E the smallest
-//     integer with max|q| <= 448 * 2^E (an exact power-of-two scale; the
-//     rounding is to nearest, ties to even);
-//   - logits x_t = sum_d Q8_d K8_td * (sm_scale * k_ws_scale * log2 e) * 2^E
-//     (fp32 accumulation in the MFMA);
+//   - Q row (query token, query head) times the base-2 logit scale c =
+//     float32(sm_scale * k_ws_scale * log2 e), one float32 product per value:
+//     codes E4M3(q c 2^-E), E the smallest integer with max|q c| <= 448 * 2^E
+//     (an exact power-of-two scale; rounding to nearest, ties to even);
+//   - logits x_t = 2^E sum_d Q8_d K8_td (fp32 accumulation in the MFMA);
 //   - weights W8_t = E4M3(2^(x_t - m + 8)), m an integer >= every logit so
 //     far (the ceiling of the running maximum: rescales are exact powers of
 //     two), so every weight lies in (0, 256]; for |m| >= 2^27, where float32
@@ -214,30 +214,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void e
         }
       }
     }
+    // the logit scale goes on Q before the rounding (one float32 product per
+    // value): the logits are then 2^E times the MFMA's sums, exactly
     float qmax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 64; ++k) qmax = fmaxf(qmax, __builtin_fabsf(qv[k]));
+    for (int k = 0; k < 64; ++k) {
+      qv[k] *= p.qk_scale_log2;
+      qmax = fmaxf(qmax, __builtin_fabsf(qv[k]));
+    }
     qmax = max_halves(qmax);
     // E: the smallest integer with qmax <= 448 * 2^E (qmax = f 2^e, f in [0.5, 1); 448 = 0.875 * 2^9)
     int e = 0;
     const float f = __builtin_frexpf(qmax, &e);
     const int E = qmax > 0.0f ? (f <= 0.875f ? e - 9 : e - 8) : 0;
-    // the sign of the logit scale goes on Q, so that tscale >= 0 (the row's
-    // maximum logit is then the scaled maximum score)
-    const bool neg = p.qk_scale_log2 < 0.0f;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         float x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = __builtin_ldexpf(qv[32 * c + 4 * w + j], -E);  // exact: |v| <= 448
-          x[j] = neg ? -v : v;
-        }
+        for (int j = 0; j < 4; ++j) x[j] = __builtin_ldexpf(qv[32 * c + 4 * w + j], -E);  // exact: |x| <= 448
         qb[c][w] = pack_e4m3(x[0], x[1], x[2], x[3]);
       }
-    tscale = fmaxf(fminf(__builtin_ldexpf(__builtin_fabsf(p.qk_scale_log2), E), __FLT_MAX__), __FLT_MIN__);
+    tscale = __builtin_ldexpf(1.0f, E);  // exact (a subnormal or 0 only for logits below 2^-117)
   }
 
   // running integer maximum (log2 domain) of this lane's row; -1e30 (an
@@ -290,7 +289,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void e
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) lm = fmaxf(lm, Sb[kb][i]);
-    const float pm = max_halves(lm) * tscale;
+    const float pm = max_halves(lm) * tscale;  // exact
     if (__any(pm > m_run)) {
       const float m_new = fmaxf(m_run, __builtin_ceilf(pm));
       const float f = __builtin_amdgcn_exp2f(m_run - m_new);  // a power of two (or 0), exact
@@ -308,8 +307,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void e
     // above it m - 8 could round down by 16, so the headroom is dropped there
     const float msub = __builtin_fabsf(m_run) < 134217728.0f ? m_run - kF8Headroom : m_run;
 
-    // ---- weights: E4M3 of 2^(x - m + 8), the rounded product x = score * tscale
-    // (x <= m, so the argument is at most 8 however large the logit)
+    // ---- weights: E4M3 of 2^(x - m + 8), x = score * 2^E exact, one rounding in
+    // the fused multiply-add (x <= m, so the argument is at most 8)
     v8i_t w8;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -317,7 +316,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void e
       for (int w = 0; w < 4; ++w) {
         float x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(Sb[kb][4 * w + j] * tscale - msub);
+        for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sb[kb][4 * w + j], tscale, -msub));
         w8[4 * kb + w] = pack_e4m3(x[0], x[1], x[2], x[3]);
       }
 

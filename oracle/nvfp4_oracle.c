@@ -402,16 +402,18 @@ void nvfp4o_extend_attention(const uint8_t* ws_k, const uint8_t* ws_v, int Hkv, 
  * hardware whose matrix cores take E4M3 operands, Q and the softmax weights
  * enter them as E4M3 too; the pages do not spell that arithmetic out, so this
  * is reading R11 (the plainest FP8 statement of the same attention):
- *   Q8_d = E4M3(q_d * 2^-E)   E = the smallest integer with max_d |q_d| <= 448 * 2^E
+ *   c    = float32(sm_scale * k_ws_scale * log2 e);   u_d = float32(q_d * c)
+ *   Q8_d = E4M3(u_d * 2^-E)   E = the smallest integer with max_d |u_d| <= 448 * 2^E
  *                             (0 for a zero row); nearest, ties to even (R1, R4);
- *   x_t  = sum_d Q8_d * E4M3(k_td) * c * 2^E,  c = float32(sm_scale * k_ws_scale * log2 e)
+ *   x_t  = 2^E * sum_d Q8_d * E4M3(k_td)
  *   M    = ceil(max_t x_t);   W_t = E4M3(2^(x_t - M + h))   (<= 256)
  *                             h = 8 for |M| < 2^27, else 0 (float32 holds M - 8
  *                             exactly only below 2^27);
  *   o_d  = v_ws_scale * sum_t W_t E4M3(v_td) / sum_t W_t.
- * Keys and sequences as in nvfp4o_extend_attention.  The sums are exact in
- * float64 up to the one rounding of each product with c (E4M3 products have
- * at most 8 significant bits over 36 binades; 128 of them fit 53 bits).
+ * Keys and sequences as in nvfp4o_extend_attention.  The logits are exact in
+ * float64 (E4M3 products have at most 8 significant bits over 36 binades;
+ * 128 of them fit 53 bits), and so is u_d (a product of two float32 values,
+ * rounded once to float32).
  *
  * tol[r] bounds |o_GPU - o| for one row of a kernel that computes the same
  * thing with float32 logits and an integer running maximum (it rescales by
@@ -421,7 +423,7 @@ void nvfp4o_extend_attention(const uint8_t* ws_k, const uint8_t* ws_v, int Hkv, 
  *     over the sum L = sum_t W_t (vmax_t = max_d |v_td| in output units);
  *   - rounding flips: a weight whose exact value lies within the relative
  *     error e_t of the kernel's 2^(x - m + 8) from an E4M3 midpoint may take
- *     the neighbouring value; e_t = ln2 * (c * 2^E * (2^-10 * max_d |Q8_d k_td|
+ *     the neighbouring value; e_t = ln2 * (2^E * (2^-10 * max_d |Q8_d k_td|
  *     + 2^-23 * sum_d |Q8_d k_td|) + 2^-22 * |x_t| + 2^-22) + 2^-21;
  *   - small weights (below 2^-5 at M): rounded at another power-of-two
  *     scale, within 2^-8 of this one;
@@ -447,8 +449,11 @@ void nvfp4o_extend_attention_fp8(const uint8_t* ws_k, const uint8_t* ws_v, int H
     const float* qv = q + rows[r] * 128;
     double* o = out + r * 128;
     /* Q8 */
-    double amax = 0.0;
-    for (int d = 0; d < 128; ++d) amax = fmax(amax, fabs((double)qv[d]));
+    double u[128], amax = 0.0;
+    for (int d = 0; d < 128; ++d) {
+      u[d] = (double)(float)((double)qv[d] * (double)c);
+      amax = fmax(amax, fabs(u[d]));
+    }
     int E = 0;
     if (amax > 0.0) {
       E = -200;
@@ -456,11 +461,11 @@ void nvfp4o_extend_attention_fp8(const uint8_t* ws_k, const uint8_t* ws_v, int H
     }
     double q8[128];
     for (int d = 0; d < 128; ++d) {
-      const double a = ldexp((double)qv[d], -E);
+      const double a = ldexp(u[d], -E);
       const double mag = nvfp4o_e4m3_value(e4m3_code_of(fabs(a)));
       q8[d] = signbit(a) ? -mag : mag;
     }
-    const double cs = (double)c * ldexp(1.0, E);
+    const double cs = ldexp(1.0, E);
     double* x = (double*)malloc((size_t)n * sizeof(double));
     double* ex = (double*)malloc((size_t)n * sizeof(double));
     double xmax = -INFINITY;

@@ -241,6 +241,41 @@ def test_fp8_extend_split_checks_and_sizes():
     assert _ext_split(nk, n=0, q=0, out=0, ws=0, wsb=0) == 0
 
 
+def test_fp8_extend_f8_checks_and_sizes():
+    import torch
+
+    nk = _lib()
+
+    def size(*a, dtype=torch.bfloat16):
+        return nk.fp8_extend_attn_f8_workspace_bytes(dtype, *a)
+
+    need = size(64, 64, 8, 2, 4, 8192)
+    assert need > 0 and need % 256 == 0
+    # one round of resident workgroups: two 4-wave workgroups per CU (2 waves per SIMD)
+    assert size(64, 64, 8, 2, 4, 1 << 20) == 512 // 16 * 64 * 64 * 132 * 4
+    assert size(64, 128, 8, 2, 4, 1 << 20) == 256 // 16 * 64 * 128 * 132 * 4  # 8-wave workgroups: one per CU
+    assert size(64, 64, 8, 2, 4, 0) == 0
+    assert size(8192, 64, 8, 2, 4096, 8192) == 0
+    assert size(64, 60, 8, 2, 4, 8192) == 0
+    assert nk.lib.nvfp4_fp8_extend_attn_f8_workspace_bytes(7, 64, 64, 8, 2, 4, 8192) == 0
+
+    def call(q=FAKE, hq=64, mp=8192, ks=1.0, out=FAKE, ws=FAKE, wsb=1 << 26, n=2):
+        return nk.lib.nvfp4_fp8_extend_attn_f8(ctypes.c_void_p(q), 1, 64, hq, 8, n, ctypes.c_void_p(FAKE),
+                                               ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 4, mp,
+                                               ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 1000, ks, 1.0, 0.088,
+                                               ctypes.c_void_p(out), ctypes.c_void_p(ws), wsb, None)
+    assert call(mp=-1) == 1
+    assert call(ks=0.0) == 1
+    assert call(hq=60) == 1
+    assert call(hq=8 * 17) == 2
+    assert call(q=FAKE + 4) == 2
+    assert call(out=0) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(ws=0) == 1
+    assert call(ws=FAKE + 4) == 2
+    assert call(n=0, q=0, out=0, ws=0, wsb=0) == 0
+
+
 def test_multi_token_decode_checks_and_sizes():
     nk = _lib()
     L = _layer(nk)

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LLVM = "/opt/rocm/lib/llvm"
 CLANG = os.path.join(LLVM, "bin", "clang")
 ORACLE_TESTS = ["tests/test_oracle_formats.py", "tests/test_oracle_pages.py", "tests/test_oracle_attention.py",
-                "tests/test_oracle_extend.py", "tests/test_oracle_mx.py", "tests/test_oracle_hadamard.py",
+                "tests/test_oracle_extend.py", "tests/test_oracle_extend_fp8.py", "tests/test_oracle_mx.py", "tests/test_oracle_hadamard.py",
                 "tests/test_oracle_mla.py"]
 ABI_TESTS = ["tests/test_abi.py"]
 

@@ -37,7 +37,7 @@ def _torch_reference(ws_k, ws_v, ks, vs, q, qo, offs, pl, sm, rows):
         i = int(np.searchsorted(qo, qrow, side="right") - 1)
         j = qrow - qo[i]
         keys = np.arange(pl[i] + j + 1) + offs[i]
-        qv = q[qrow, qh].astype(np.float64)
+        qv = (q[qrow, qh] * np.float32(c)).astype(np.float64)  # float32 products
         amax = np.abs(qv).max()
         E = 0
         if amax > 0:
@@ -45,7 +45,7 @@ def _torch_reference(ws_k, ws_v, ks, vs, q, qo, offs, pl, sm, rows):
             while amax > 448.0 * 2.0 ** E:
                 E += 1
         q8 = torch.from_numpy((qv * 2.0 ** -E).astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-        x = (K[keys, qh // G] @ q8) * (c * 2.0 ** E)
+        x = (K[keys, qh // G] @ q8) * 2.0 ** E
         M = math.ceil(x.max())
         y = np.exp2(x - M + (8.0 if abs(M) < 2.0 ** 27 else 0.0)).astype(np.float32)
         w = torch.from_numpy(y).to(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -141,33 +141,47 @@ def test_fp8_extend_identical_keys_give_the_mean_of_visible_values():
 
 
 def test_fp8_extend_bound_grows_near_midpoints():
-    """Two keys: logit 0 (weight 2^8) and the logit scale c itself (Q8 = 1, K = 1).
-    With c = log2(17) - 8 the second weight 2^(c + 8) is 17 to float32 precision,
-    the midpoint of the E4M3 values 16 and 18, so a kernel may round it either
-    way: the bound takes that step.  c = -4 (weight exactly 16) and c = -3.5
-    (22.6, far from the midpoints 21 and 23) leave only the accumulation terms."""
+    """Two keys: logit 0 (weight 2^8) and x = -a*b for E4M3 values a (in Q) and b
+    (in K), logit scale exactly 1.  The pair is chosen so that 2^(x + 8) lies
+    0.3-2% from an E4M3 midpoint: with nothing else in the row a kernel's
+    float32 logit cannot cross it, so the bound is only the accumulation terms.
+    Adding two cancelling products of 64 leaves x unchanged but lets the FP8
+    matrix cores' accumulation move it by up to 2^-11 * 64: now the weight may
+    round either way, and the bound takes that step."""
     H, Hq, ks = 1, 1, 0.5
+    sm = 1.0 / (ks * LOG2E)
+    assert np.float32(sm * ks * LOG2E) == 1.0
+    vals = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    pick = None
+    for ia in range(0x30, 0x48):        # a, b in [0.5, 4): x in (-16, -0.25]
+        for ib in range(0x30, 0x48):
+            y = 2.0 ** (8.0 - vals[ia] * vals[ib])
+            if y < 0.25:
+                continue
+            rel = np.min(np.abs(mids - y)) / y
+            if 0.003 <= rel <= 0.02:
+                pick = (ia, ib, y)
+                break
+        if pick:
+            break
+    assert pick is not None
+    ia, ib, y = pick
+    w1 = vals[np.argmin(np.abs(vals - y))]
     ws_k = np.zeros((2, H, 128), np.uint8)
-    ws_k[0, 0, 0] = 0x38  # key 0 meets q[0] = 0: logit 0
-    ws_k[1, 0, 1] = 0x38  # key 1 meets q[1] = 1: logit c
+    ws_k[0, 0, 0] = 0x38        # key 0 meets q[0] = 0: logit 0
+    ws_k[1, 0, 1] = 0x80 | ib   # key 1: -b against q[1] = a
     ws_v = np.zeros((2, H, 128), np.uint8)
     ws_v[0, 0, :] = 0x38
     ws_v[1, 0, :] = 0xB8
     q = np.zeros((1, Hq, 128), np.float32)
-    q[0, 0, 1] = 1.0
-    q[0, 0, 127] = 448.0  # E = 0
+    q[0, 0, 1] = vals[ia]
+    q[0, 0, 127] = 448.0        # E = 0
     qo, offs, pl = np.array([0, 1], np.int32), np.array([0], np.int32), np.array([1], np.int32)
-
-    def run(c):
-        sm = c / (ks * LOG2E)
-        assert abs(float(np.float32(sm * ks * LOG2E)) - c) <= 2.0 ** -20
-        out, tol = oracle.extend_attention_fp8(ws_k, ws_v, ks, 1.0, q, qo, offs, pl, sm)
-        return out[0, 0], tol[0]
-
-    o_grid, t_grid = run(-4.0)
-    assert o_grid == pytest.approx((256 - 16) / (256 + 16), abs=1e-15)
-    o_far, t_far = run(-3.5)
-    assert o_far == pytest.approx((256 - 22) / (256 + 22), abs=1e-15)
-    _, t_mid = run(math.log2(17.0) - 8.0)
-    assert t_mid > 4 * max(t_grid, t_far)
-    assert max(t_grid, t_far) < 0.01
+    out_a, t_a = oracle.extend_attention_fp8(ws_k, ws_v, ks, 1.0, q, qo, offs, pl, sm)
+    assert out_a[0, 0] == pytest.approx((256 - w1) / (256 + w1), abs=1e-15)
+    q[0, 0, 2] = q[0, 0, 3] = 64.0
+    ws_k[1, 0, 2], ws_k[1, 0, 3] = 0x38, 0xB8   # +64 and -64: x unchanged
+    out_b, t_b = oracle.extend_attention_fp8(ws_k, ws_v, ks, 1.0, q, qo, offs, pl, sm)
+    assert out_b[0, 0] == out_a[0, 0]
+    assert t_a[0] < 0.01 and t_b[0] > 4 * t_a[0]
