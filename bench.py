@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0  # dense f16 / bf16 MFMA
+PEAK_F8_TFLOPS = 5000.0   # dense fp8 MFMA
 METRIC = "decode-attn effective HBM GB/s (% of 8 TB/s) + quantize-append GB/s"
 # Windows of the headline step timing (each exactly --steps calls between two synchronizations)
 STEP_WINDOWS = 7
@@ -379,10 +380,18 @@ def bench_mixed(args, wl, dev):
         nk.fp8_extend_attn(st.ext_q, st.ext_q_offsets, st.ext_offsets[:-1], st.ext_prefix, st.ext_chunk, ws_k, ws_v,
                            *scales(st), sm, out=ext_out)
     ext_s = back_to_back(stream, max(4, args.steps // 5), ext_call, windows=3)
+    ext8_out = torch.empty_like(ext_out)
+
+    def ext8_call(i):  # the same attention in FP8 arithmetic (Q and the weights in E4M3, FP8 MFMA)
+        st = steps[i % L]
+        nk.fp8_extend_attn_f8(st.ext_q, st.ext_q_offsets, st.ext_offsets[:-1], st.ext_prefix, st.ext_chunk,
+                              st.max_prefix, ws_k, ws_v, *scales(st), sm, out=ext8_out)
+    ext8_s = back_to_back(stream, max(4, args.steps // 5), ext8_call, windows=3)
     C = s0.ext_chunk
     pairs = sum(C * int(p) + C * (C + 1) // 2 for p in s0.ext_prefix.cpu().numpy())  # (query token, key) pairs
     ext_flops = pairs * Hq * 4 * 128  # QK^T and PV: 2 x 128 multiply-adds per (query row, key)
     ext_tf = ext_flops / ext_s / 1e12
+    ext8_tf = ext_flops / ext8_s / 1e12
 
     b_step = b_app + b_ws + b_dec
     achieved = b_dec / dec_b2b / 1e9
@@ -413,6 +422,13 @@ def bench_mixed(args, wl, dev):
                             "unit": "TFLOP/s", "frac": round(ext_tf / PEAK_F16_TFLOPS, 4),
                             "kernel": "nvfp4_fp8_extend_attn (extend_kernel)", "flops_per_call": int(ext_flops),
                             "query_tokens": t_ext, "key_pairs": int(pairs)},
+        "extend_attn_f8_us": round(ext8_s * 1e6, 2),
+        "extend_attn_f8_tflops": round(ext8_tf, 2),
+        "extend_f8_roofline": {"bound": "mfma", "achieved": round(ext8_tf, 2), "peak": PEAK_F8_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(ext8_tf / PEAK_F8_TFLOPS, 4),
+                               "frac_of_f16_peak": round(ext8_tf / PEAK_F16_TFLOPS, 4),
+                               "kernel": "nvfp4_fp8_extend_attn_f8 (extend_f8_kernel)",
+                               "flops_per_call": int(ext_flops)},
         "quantize_append_bulk_gbs": round(bulk_gbs, 2),
         "quantize_append_bulk_us": round(bulk_us, 2),
         "quantize_append_bulk_gbs_single_call": round(sum(append_bytes) / (sum(append_ms) / 1e3) / 1e9, 2),

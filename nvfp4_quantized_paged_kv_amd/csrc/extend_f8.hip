@@ -65,9 +65,11 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// four floats -> four E4M3 bytes (round to nearest, ties to even)
+// four floats -> four E4M3 bytes (round to nearest, ties to even).  The
+// first conversion writes the low half of a's register (its high half is
+// replaced by the second), so no register has to be cleared first.
 __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void e
     for (int i = 0; i < 16; ++i) acc[d][i] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) lsum[i] = 0.0f;
-  const v8i_t ones = {kF8One, kF8One, kF8One, kF8One, kF8One, kF8One, kF8One, kF8One};
+  v8i_t ones = {kF8One, kF8One, kF8One, kF8One, kF8One, kF8One, kF8One, kF8One};
+  asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt every tile
   const int lim = P + t0 + tq;  // last key of this lane's row
 
   for (int kt = kt0; kt < kt1; ++kt) {
