@@ -204,7 +204,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
                                                        int32_t max_seq_len, float sm_scale, float* out,
                                                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* One decode step in one launch: quantize-on-append of each sequence's
+/* One decode step in one call: quantize-on-append of each sequence's
  * q_per_seq new tokens (blog section 3, first data flow) and the decode
  * attention over the cache that now holds them (third data flow), fused.
  * The new tokens of sequence b sit at positions
@@ -212,7 +212,7 @@ NVFP4_API nvfp4_status_t nvfp4_paged_decode_attn_multi(const nvfp4_kv_layer_t* l
  * their slots come from block_table.  The result is the same as
  * nvfp4_kv_quantize_append of those tokens followed by
  * nvfp4_paged_decode_attn_multi: the same cache bytes and the same output.
- * Schedule: when a unit holds at most 16384 pages (max_seq_len <= 262,144) the
+ * Schedule: when a unit holds at most 64 pages (max_seq_len <= 1024) the
  * step is one launch -- the workgroup that reads a page holding a new token
  * quantizes and stores that token itself before it loads the page, so no
  * workgroup waits on another.  Longer units take two launches on `stream`

@@ -397,7 +397,7 @@ def paged_decode_step(layer: KVCacheLayer, k_new: torch.Tensor, v_new: torch.Ten
                       block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
                       out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                       stream=None) -> torch.Tensor:
-    """One decode step in one launch: append k_new, v_new [B, T, H, 128] at the last T positions
+    """One decode step in one call: append k_new, v_new [B, T, H, 128] at the last T positions
     (seq_lens counts them) and attend with q [B, T, Hq, 128]; returns f32 [B, T, Hq, 128]."""
     if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B, T, Hq, 128] tensor")

@@ -137,13 +137,14 @@ namespace {
 // k_new / v_new the kernel first appends the q_per_seq new tokens itself.
 // A decode step whose units hold more pages than this appends its new tokens
 // with the append kernel and then decodes (two launches); shorter ones append
-// inside the decode kernel.  Measured on MI355X: 8K-token contexts (512 pages)
-// run the step 1.4-2.5% faster fused; at 128K (8192 pages) the fused step runs
-// as fast as two launches with a precomputed slot array and about 2% faster
-// than two launches that take the slots from the block table on the device; a
-// 2M-token context (125,000 pages) runs the fused kernel about 20 us (4%)
-// longer than append + decode.
-constexpr int64_t kStepFusedMaxPages = 16384;
+// inside the decode kernel.  Measured on MI355X with clocks in their sustained
+// state (B=32, 8 kv heads, 64 q heads, 1 new token per sequence): the fused
+// step takes 21.7 / 18.0 / 25.0 / 39.1 / 66.7 us at 512 / 1K / 2K / 4K / 8K
+// tokens against 21.9 / 18.6 / 24.7 / 36.5 / 60.2 us for two launches, and
+// 235 vs 217 us at 128K, 466 vs 423 us at 2M: the fused kernel's page loop
+// runs about 9% slower (cause not found: the loop's compute blocks and waits
+// match the plain kernel's), which only the saved launch outweighs.
+constexpr int64_t kStepFusedMaxPages = 64;
 
 nvfp4_status_t decode_impl(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new, const void* q,
                            nvfp4_dtype_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads,

@@ -400,17 +400,18 @@ def test_decode_multi_one_token_is_plain_decode():
 @pytest.mark.parametrize("lens,H,G,T,qdt", [
     ([33, 16, 17, 1000], 2, 8, 1, torch.bfloat16),   # the new token opens a page / ends one / mid-page
     ([17, 40, 2], 2, 8, 2, torch.bfloat16),          # two new tokens straddling pages 0 and 1
-    ([12000, 50, 9000], 2, 4, 4, torch.float32),     # units split over several workgroups, float32
+    ([1000, 50, 900], 2, 4, 4, torch.float32),       # one launch, units split over several workgroups, float32
     ([1, 3, 5], 1, 2, 4, torch.bfloat16),            # sequences shorter than the new tokens
 ])
 def test_decode_step_equals_append_then_decode(lens, H, G, T, qdt):
     _step_case(lens, H, G, T, qdt, max(lens))
 
 
-@pytest.mark.parametrize("lens,H,G,T", [([33, 16, 17, 1000], 2, 8, 1), ([17, 40, 2], 2, 8, 2), ([1, 3, 5], 1, 2, 4)])
-def test_decode_step_two_launch_schedule(lens, H, G, T):
-    """max_seq_len above 262,144 tokens: the step appends with the append kernel, then decodes."""
-    _step_case(lens, H, G, T, torch.bfloat16, 270000)
+@pytest.mark.parametrize("lens,H,G,T,msl", [([33, 16, 17, 1000], 2, 8, 1, 270000), ([17, 40, 2], 2, 8, 2, 1025),
+                                             ([1, 3, 5], 1, 2, 4, 4096), ([12000, 50, 9000], 2, 4, 4, 12000)])
+def test_decode_step_two_launch_schedule(lens, H, G, T, msl):
+    """max_seq_len above 1024 tokens: the step appends with the append kernel, then decodes."""
+    _step_case(lens, H, G, T, torch.bfloat16 if msl != 12000 else torch.float32, msl)
 
 
 def _step_case(lens, H, G, T, qdt, msl):

@@ -159,11 +159,12 @@ def test_multi_token_full_size():
 
 
 def test_decode_step_full_size():
-    """The step in one launch: each sequence's new token (position ctx - 1) is
-    quantized into its page by the decode kernel, which then attends over ctx keys."""
+    """The step at full size: each sequence's new token (position ctx - 1) is
+    quantized into its page (the append kernel, then the decode: 8K-token units
+    take two launches), then the decode attends over ctx keys."""
     import nvfp4_quantized_paged_kv_amd as nk
 
-    _say(f"case: full-size decode step in one launch {WL}, samples {SAMPLES}")
+    _say(f"case: full-size decode step {WL}, samples {SAMPLES}")
     wl, fl, raw = _fill(8192 - 1, 8192)
     B, Hq, H, G, ctx = wl.batch, wl.q_heads, wl.kv_heads, wl.group, wl.ctx
     g_k, g_v = fl.layer.k_global, fl.layer.v_global
