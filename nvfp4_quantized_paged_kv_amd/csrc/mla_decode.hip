@@ -103,8 +103,12 @@ __global__ __launch_bounds__(WAVES * 64) void mla_decode_kernel(MlaDecodeParams 
   constexpr int NT = WAVES * 64;
   constexpr int kHeads = 16 * WAVES;
   constexpr int kPer = (kStageJobs + NT - 1) / NT;  // staging jobs per thread
-  __shared__ __align__(16) _Float16 s_k[2][kTile * kRow];
-  __shared__ int s_valid[2][kTile];
+  // One-wave workgroups (16 heads) stage into a single buffer: two 37 KB
+  // buffers let only 2 such workgroups (2 of the CU's 4 SIMDs) be resident,
+  // one lets 4; the next tile's rows are then written after this tile's PV.
+  constexpr int kBufs = WAVES == 1 ? 1 : 2;
+  __shared__ __align__(16) _Float16 s_k[kBufs][kTile * kRow];
+  __shared__ int s_valid[kBufs][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(WAVES * 64) void mla_decode_kernel(MlaDecodeParams 
   for (int m = 0; m < 32; ++m) acc[m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
+    const int buf = kBufs == 1 ? 0 : (kt & 1);
     // the next tile's rows go out before this tile is computed, the tile
     // after's slots too -- unconditionally (past the share's end the clamped
     // loads read valid memory and stage as zeros): a branch here would make the
@@ -316,9 +320,14 @@ __global__ __launch_bounds__(WAVES * 64) void mla_decode_kernel(MlaDecodeParams 
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bv, acc[m], 0, 0, 0);
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv, acc[m], 0, 0, 0);
       constexpr int kEvery = 32 / kPer;  // 32 / kEvery >= kPer slots
-      if (m % kEvery == kEvery - 1 && m / kEvery < kPer) write_stage(buf ^ 1, tid + (m / kEvery) * NT, st[m / kEvery]);
+      if (kBufs == 2 && m % kEvery == kEvery - 1 && m / kEvery < kPer) write_stage(buf ^ 1, tid + (m / kEvery) * NT, st[m / kEvery]);
     }
     __syncthreads();
+    if constexpr (kBufs == 1) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) write_stage(0, tid + k * NT, st[k]);
+      __syncthreads();
+    }
   }
 
   // ---- per-head totals: l over the 4 entry groups; each accumulator row i is head 4*g4 + i
