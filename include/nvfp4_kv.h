@@ -36,8 +36,9 @@
  *   k_codes  [num_pages][H][1024] u8: byte o*64 + d/2 of the tile holds dims
  *            d (even: low nibble) and d+1 (high nibble) of token o.
  *   k_scales [num_pages][H][128]  u8: byte o*8 + b = E4M3 scale of dims 16b..16b+15.
- *   v_codes  [num_pages][H][1024] u8: byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2
- *            holds dims d (low nibble, d even) and d+1 of token o.
+ *   v_codes  [num_pages][H][1024] u8: byte (o/4)*256 + (d/8)*16 + ((o/2)%2)*8
+ *            + (d%2)*4 + (d%8)/2 holds dim d of tokens o (o even: low nibble)
+ *            and o^1 (high nibble).
  *   v_scales [num_pages][H][128]  u8: byte (d/16)*16 + o.
  *   An E2M1 code is sign<<3 | magnitude code (0..7 <-> 0, .5, 1, 1.5, 2, 3, 4, 6).
  *   A value reads back as E2M1(code) * E4M3(scale) * global (k_global or v_global).
@@ -111,8 +112,8 @@ typedef struct nvfp4_kv_layer {
  *                  are token_stride_elems elements apart (>= num_kv_heads*128);
  *                  16-byte aligned base and token stride.  Values must be finite.
  *   slot_mapping : [num_tokens] int32.
- * Slots that appear twice in one call are written by both tokens in an
- * unspecified order.  num_tokens == 0 is a no-op.
+ * A slot that appears twice in one call ends with an unspecified mix of both
+ * tokens' codes and scales.  num_tokens == 0 is a no-op.
  *   Supported: ceil(num_tokens/16) * num_kv_heads < 2^31. */
 NVFP4_API nvfp4_status_t nvfp4_kv_quantize_append(const nvfp4_kv_layer_t* layer, const void* k_new, const void* v_new,
                                                   nvfp4_dtype_t dtype, int32_t num_tokens, int64_t token_stride_elems,
@@ -386,8 +387,11 @@ NVFP4_API nvfp4_status_t nvfp4_fp8_extend_attn_f8(const void* q, nvfp4_dtype_t q
  * (X = 2^(byte - 127)); code = sign(x) | E2M1 nearest to |x|/X (ties to even,
  * saturating at 6).  No tensor-wide scale.  17/32 byte per value.
  *
- * Layout: the code planes are laid out exactly as the NVFP4 ones; a scale
- * tile is 64 bytes:
+ * Layout: k_codes as the NVFP4 k_codes; v_codes keeps each token's nibbles
+ * in bytes of its own (its two values share that token's E8M0 scale):
+ *   v_codes  [num_pages][H][1024] u8: byte (o/4)*256 + (d/8)*16 + (o%4)*4 +
+ *            (d%8)/2 holds dims d (low nibble, d even) and d+1 of token o.
+ * A scale tile is 64 bytes:
  *   k_scales [num_pages][H][64] u8: byte o*4 + d/32 = E8M0 scale of dims
  *            32*(d/32) .. +31 of token o.
  *   v_scales [num_pages][H][64] u8: byte (d/32)*16 + o. */

@@ -22,16 +22,18 @@
 //   online softmax in fp32 (exp2 domain), with a lazy max: the running max is
 //         only raised when a page exceeds it by more than 2^8, so P <= 2^8;
 //         row maxima across the 4 token groups use v_permlane16/32_swap
-//   PV    O[16 q x 128] += P[16 x 16 tok] . V_page : 8 x mfma_f32_16x16x32_f16
-//         (the QK^T output lane layout is exactly the PV A-operand layout; the
-//          32-wide contraction carries P as an f16 hi + lo pair against the same
-//          V twice; the V tile layout gives lane l the 4 tokens 4*(l/16)..+3 of
-//          dims 8*(l%16)..+7 in 16 contiguous bytes; nibbles of two tokens are
-//          re-paired with bit-field inserts so that one byte = one MFMA k-pair)
-// Dequantization: v_cvt_scalef32_pk_f16_fp4 widens two E2M1 codes (times 2^8),
-// and one v_pk_mul_f16 by (E4M3 scale * 2^-8, taken from the scale byte's bit
-// pattern) gives e2m1 * bs exactly in f16 (at most 6 significant bits,
-// magnitude in [2^-10, 2688]).  The FP32 global scales are applied to the
+//   PV    O[16 q x 128] += P[16 x 16 tok] . V_page : 16 x mfma_f32_16x16x16f16
+//         (the QK^T output lane layout is exactly the PV A-operand layout; P
+//          enters as an f16 hi + lo pair, one MFMA each against the same V
+//          operand; the V tile gives lane l the 4 tokens 4*(l/16)..+3 of dims
+//          8*(l%16)..+7 in 16 contiguous bytes, each byte one dimension of two
+//          neighbouring tokens, so one conversion yields one MFMA k-pair)
+// Dequantization: v_cvt_scalef32_pk_f16_fp4 widens two E2M1 codes, and one
+// v_pk_mul_f16 by the E4M3 scale pair gives e2m1 * bs exactly in f16 (at most
+// 6 significant bits, magnitude in [2^-10, 2688]).  K: the codes times 2^8 and
+// the scale byte's bit pattern << 7 as f16 (bs * 2^-8), one pair per block;
+// V: two tokens' scale bytes widened by v_cvt_scalef32_pk_f16_fp8 (exact).
+// The FP32 global scales are applied to the
 // logits (K) and to the final output (V).  Q is converted to f16 after an
 // exact power-of-two prescale (float32 Q: as an f16 hi + lo pair).
 // MXFP4 planes (kMX; E8M0 scale per 32 values, the format the NVFP4 pages
@@ -67,8 +69,6 @@ constexpr int kMaxPagesPerWave = 128;                       // page indices a wa
 constexpr int kChunkPages = kMaxPagesPerWave * kWaves;      // pages of one unit a workgroup loads indices for at once
 constexpr int kPartStride = kHeadDim + 2;                   // floats per (partial slot, q head)
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max must move
-
-__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -190,7 +190,7 @@ __device__ __forceinline__ void hadamard_rotate_q(float (&v)[32], int q4) {
 struct PageRegs {
   uint4 kw;      // K codes: token r, dims 32*q4 .. 32*q4+31
   uint32_t ksw;  // K scales: token r, blocks 2*q4, 2*q4+1 (MXFP4: block q4)
-  uint4 vw;      // V codes: tokens 4*q4 .. 4*q4+3, dims 8*r .. 8*r+7
+  uint4 vw;      // V codes, dims 8*r .. 8*r+7: even and odd dims of tokens 4*q4 + {0,1}, then of + {2,3}
   uint32_t vsw;  // V scales: block r/2 (MXFP4: r/4), tokens 4*q4 .. 4*q4+3
 };
 
@@ -300,8 +300,12 @@ __device__ __forceinline__ void append_own_tokens(const DecodeParams& p, int b, 
       else load_block<uint16_t>(reinterpret_cast<const uint16_t*>(which ? p.v_new : p.k_new) + src, x);
       const float g = which ? p.v_global : p.k_global;
       const QuantBlock q = quantize_block16(x, g, 1.0 / (6.0 * (double)g));
-      store_block(const_cast<uint8_t*>(which ? p.v_codes : p.k_codes), const_cast<uint8_t*>(which ? p.v_scales : p.k_scales),
-                  p.H, which != 0, page * kPageSize + pos % kPageSize, h, blk, q);
+      // V: a token's slot pair partner is either older (in the cache) or not
+      // yet written, or another lane's job: each token sets its own nibbles
+      if (which) store_v_alone(const_cast<uint8_t*>(p.v_codes), const_cast<uint8_t*>(p.v_scales), p.H,
+                               page * kPageSize + pos % kPageSize, h, blk, q);
+      else store_k_block(const_cast<uint8_t*>(p.k_codes), const_cast<uint8_t*>(p.k_scales), p.H,
+                         page * kPageSize + pos % kPageSize, h, blk, q);
     }
   }
 }
@@ -678,17 +682,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int nv = min(max(rem - 4 * q4, 0), 4);
         vsw &= nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);  // zero the scales of tokens past the end
       }
-      // scale bytes (s0, s1) -> f16 pair (s0 << 7, s1 << 7): bytes moved to 0 and 2, then one shift
-      const half2_t vs01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, vsw, 0x0C010C00u) << 7);
-      const half2_t vs23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, vsw, 0x0C030C02u) << 7);
-      const uint32_t E01 = bfi(0x0F0F0F0Fu, cur.vw.x, cur.vw.y << 4), O01 = bfi(0x0F0F0F0Fu, cur.vw.x >> 4, cur.vw.y);
-      const uint32_t E23 = bfi(0x0F0F0F0Fu, cur.vw.z, cur.vw.w << 4), O23 = bfi(0x0F0F0F0Fu, cur.vw.z >> 4, cur.vw.w);
+      // scale bytes of tokens (0, 1) and (2, 3) -> exact f16 pairs
+      const half2_t vs01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsw, 1.0f, false);
+      const half2_t vs23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsw, 1.0f, true);
+      // byte C of a word: dim 8r + 2C (E) or 8r + 2C + 1 (O) of two tokens
+      const uint32_t E01 = cur.vw.x, O01 = cur.vw.y, E23 = cur.vw.z, O23 = cur.vw.w;
   #define NVFP4_PV_STEP(C)                                                                   \
     {                                                                                        \
-      const half2_t a0 = fp4x2_to_f16_x256<C>(E01) * vs01;                                   \
-      const half2_t a1 = fp4x2_to_f16_x256<C>(E23) * vs23;                                   \
-      const half2_t b0 = fp4x2_to_f16_x256<C>(O01) * vs01;                                   \
-      const half2_t b1 = fp4x2_to_f16_x256<C>(O23) * vs23;                                   \
+      const half2_t a0 = fp4x2_to_f16<C>(E01) * vs01;                                        \
+      const half2_t a1 = fp4x2_to_f16<C>(E23) * vs23;                                        \
+      const half2_t b0 = fp4x2_to_f16<C>(O01) * vs01;                                        \
+      const half2_t b1 = fp4x2_to_f16<C>(O23) * vs23;                                        \
       const half4_t ve = {a0[0], a0[1], a1[0], a1[1]};                                       \
       const half4_t vo = {b0[0], b0[1], b1[0], b1[1]};                                       \
       acc[2 * C] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, ve, acc[2 * C], 0, 0, 0);        \

@@ -112,9 +112,14 @@ __global__ __launch_bounds__(kWsWaves * 64) void dequant_ws_kernel(DequantWsPara
         dst[1] = make_uint4(d.x, d.y, e.x, e.y);
       }
     } else {
-      // V tile: lane = (tokens 4*(lane/16) .. +3, dims 8*(lane%16) .. +7), one code dword per token
+      // V tile: lane = (tokens 4*(lane/16) .. +3, dims 8*(lane%16) .. +7) as even- and
+      // odd-dimension words of the token pairs (0, 1) and (2, 3) (a byte holds one
+      // dimension of both tokens); regrouped here into one code dword per token
       const int o0 = 4 * (lane >> 4), d0 = 8 * (lane & 15);
-      const uint32_t cw[4] = {t.c.x, t.c.y, t.c.z, t.c.w};
+      const uint32_t cw[4] = {(t.c.x & 0x0F0F0F0Fu) | ((t.c.y << 4) & 0xF0F0F0F0u),
+                              ((t.c.x >> 4) & 0x0F0F0F0Fu) | (t.c.y & 0xF0F0F0F0u),
+                              (t.c.z & 0x0F0F0F0Fu) | ((t.c.w << 4) & 0xF0F0F0F0u),
+                              ((t.c.z >> 4) & 0x0F0F0F0Fu) | (t.c.w & 0xF0F0F0F0u)};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t row = out0 + (int64_t)t.pg * kPageSize + o0 + k;

@@ -56,4 +56,10 @@ __device__ __forceinline__ half2_t fp4x2_to_f16_x256(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, SEL);
 }
 
+// The same without the factor: the two E2M1 values exactly.
+template <int SEL>
+__device__ __forceinline__ half2_t fp4x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
 }  // namespace nvfp4kv

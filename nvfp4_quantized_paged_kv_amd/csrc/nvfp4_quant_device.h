@@ -247,23 +247,78 @@ __device__ __forceinline__ QuantBlock quantize_block16(const float (&x)[16], flo
 }
 
 // Store block b (dims 16b .. 16b+15) of the token in `slot` (>= 0, inside the
-// cache) and kv head h into one tensor's planes: K tiles are token-major
-// (row o: 64 code bytes, 8 scale bytes); V tiles are token-quad interleaved
-// (byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2, scale byte b*16 + o).
-__device__ __forceinline__ void store_block(uint8_t* codes, uint8_t* scales, int H, bool is_v, int32_t slot, int h,
-                                            int b, const QuantBlock& q) {
+// cache) and kv head h into the K planes: K tiles are token-major (row o: 64
+// code bytes, 8 scale bytes).
+__device__ __forceinline__ void store_k_block(uint8_t* codes, uint8_t* scales, int H, int32_t slot, int h, int b,
+                                              const QuantBlock& q) {
   const int64_t page = (uint32_t)slot / kPageSize;
   const int o = (int)((uint32_t)slot % kPageSize);
   const int64_t tile = page * H + h;
-  if (!is_v) {
-    *reinterpret_cast<uint2*>(codes + tile * kTileCodeBytes + o * 64 + 8 * b) = make_uint2(q.packed[0], q.packed[1]);
-    scales[tile * kTileScaleBytes + o * 8 + b] = (uint8_t)q.sb;
-  } else {
-    uint8_t* base = codes + tile * kTileCodeBytes + (o >> 2) * 256 + (o & 3) * 4;
-    *reinterpret_cast<uint32_t*>(base + (2 * b) * 16) = q.packed[0];
-    *reinterpret_cast<uint32_t*>(base + (2 * b + 1) * 16) = q.packed[1];
-    scales[tile * kTileScaleBytes + b * 16 + o] = (uint8_t)q.sb;
+  *reinterpret_cast<uint2*>(codes + tile * kTileCodeBytes + o * 64 + 8 * b) = make_uint2(q.packed[0], q.packed[1]);
+  scales[tile * kTileScaleBytes + o * 8 + b] = (uint8_t)q.sb;
+}
+
+// V tiles: lane r = d/8 of token quad o/4 owns bytes (o/4)*256 + r*16 .. +15,
+// two 8-byte halves for the slot pairs (o/4)*4 + {0,1} and + {2,3}; a half is
+// an even-dimension word then an odd-dimension word, and byte c of a word
+// holds dimension 8r + 2c (+1 in the odd word) of the pair's even slot in its
+// low nibble and of the odd slot in its high nibble.  The decode's PV operand
+// is then a plain conversion of those bytes.  Scale byte b*16 + o.
+//
+// Block b covers lanes 2b and 2b+1.  The words of lane 2b + k for a slot pair
+// from the pair's packed code words k (even slot e, odd slot f):
+__device__ __forceinline__ uint2 v_pair_words(uint32_t e, uint32_t f) {
+  return make_uint2((e & 0x0F0F0F0Fu) | ((f << 4) & 0xF0F0F0F0u), ((e >> 4) & 0x0F0F0F0Fu) | (f & 0xF0F0F0F0u));
+}
+
+__device__ __forceinline__ uint8_t* v_half(uint8_t* codes, int H, int32_t slot, int h, int r) {
+  const int64_t page = (uint32_t)slot / kPageSize;
+  const int o = (int)((uint32_t)slot % kPageSize);
+  return codes + (page * H + h) * kTileCodeBytes + (o >> 2) * 256 + r * 16 + ((o >> 1) & 1) * 8;
+}
+
+// Both slots of a pair are written in this call by two lanes: the lane of slot
+// parity k writes lane 2b + k's half of the pair from its own packed word k
+// and the partner's (`other` = the partner's packed word k), and the even
+// slot's lane writes both scale bytes (`other_sb` = the partner's).
+__device__ __forceinline__ void store_v_pair(uint8_t* codes, uint8_t* scales, int H, int32_t slot, int h, int b,
+                                             const QuantBlock& q, uint32_t other, uint32_t other_sb) {
+  const int k = slot & 1;
+  const uint32_t mine = k ? q.packed[1] : q.packed[0];
+  *reinterpret_cast<uint2*>(v_half(codes, H, slot, h, 2 * b + k)) = k ? v_pair_words(other, mine) : v_pair_words(mine, other);
+  if (k == 0) {
+    const int64_t page = (uint32_t)slot / kPageSize;
+    const int o = (int)((uint32_t)slot % kPageSize);
+    *reinterpret_cast<uint16_t*>(scales + (page * H + h) * kTileScaleBytes + b * 16 + o) =
+        (uint16_t)(q.sb | (other_sb << 8));
   }
+}
+
+// A slot written without its pair partner: only this slot's nibbles change,
+// by atomic AND then OR on the four words (the partner's nibbles may be
+// written by another lane of the same call).
+__device__ __forceinline__ void store_v_alone(uint8_t* codes, uint8_t* scales, int H, int32_t slot, int h, int b,
+                                              const QuantBlock& q) {
+  const bool odd = slot & 1;
+  const uint32_t keep = odd ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint2 w = odd ? v_pair_words(0u, q.packed[k]) : v_pair_words(q.packed[k], 0u);
+    uint32_t* at = reinterpret_cast<uint32_t*>(v_half(codes, H, slot, h, 2 * b + k));
+    __hip_atomic_fetch_and(at, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(at, w.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_and(at + 1, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(at + 1, w.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int64_t page = (uint32_t)slot / kPageSize;
+  const int o = (int)((uint32_t)slot % kPageSize);
+  scales[(page * H + h) * kTileScaleBytes + b * 16 + o] = (uint8_t)q.sb;
+}
+
+// Lane exchange with lane l ^ 1 (ds_swizzle, bitmask mode); every lane of the
+// 32-lane group must be active.
+__device__ __forceinline__ uint32_t swz_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (1 << 10) | 0x1F);
 }
 
 }  // namespace nvfp4kv

@@ -8,9 +8,10 @@
 //
 // One thread owns one 16-value block of one (token, kv head): it reads the 16
 // inputs (32 B bf16 / 64 B f32), so the block's amax needs no cross-lane work,
-// and writes 8 code bytes plus 1 scale byte.  Lane order, fastest first: token
-// within a group of 4, block, group of 4 within 16 consecutive tokens, kv head,
-// group of 16 tokens.  Sixteen consecutive tokens usually fill one page, so a
+// and writes 8 code bytes plus 1 scale byte (K), or with the neighbouring lane
+// 16 code bytes and 2 scale bytes of two slots that share V bytes.  Lane order,
+// fastest first: token within a group of 4, block, group of 4 within 16
+// consecutive tokens, kv head, group of 16 tokens.  Sixteen consecutive tokens usually fill one page, so a
 // 256-lane workgroup writes whole (page, kv head) tiles of two heads: its K and
 // V code runs and its 128-B scale rows are complete lines written by one CU.
 // A thread's input load never waits for its slot: the slot is checked at the
@@ -32,12 +33,6 @@
 
 namespace nvfp4kv {
 namespace {
-
-// Quantize one 16-value block x and store its codes and scale byte at `slot`.
-__device__ __forceinline__ void quantize_store(const float (&x)[16], const AppendTensor& T, const AppendParams& p,
-                                               int which, int32_t slot, int h, int b) {
-  store_block(T.codes, T.scales, p.H, which != 0, slot, h, b, quantize_block16(x, T.g, T.r6));
-}
 
 // Block index i of the flattened work -> (token t, kv head h, block b); t < 0 if past the end.
 __device__ __forceinline__ void block_coords(int64_t i, const AppendParams& p, int64_t& t, int& h, int& b) {
@@ -118,13 +113,30 @@ __device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const Appen
   return j;
 }
 
+// which (0 = K, 1 = V) is uniform across the wave, and every lane of the wave
+// runs this (lanes without a live job hold token 0 and store nothing): the V
+// path exchanges codes with lane l ^ 1, the job of the other token of the same
+// group of 4 tokens, kv head and block.  When that token's slot is this
+// slot's pair partner (slot ^ 1), the two lanes write the pair's V bytes with
+// plain stores; otherwise this slot's nibbles are set alone.
 template <typename InT, bool kRotK>
 __device__ __forceinline__ void finish_job(const Job<InT>& j, const AppendTensor& T, const AppendParams& p, int which) {
   float x[16];
   widen<InT>(j.raw, x);
   if (kRotK && which == 0) hadamard_rotate_k<16, 8>(x, j.b);
-  if (j.live && j.slot >= 0 && (int64_t)j.slot < (int64_t)p.num_pages * kPageSize)
-    quantize_store(x, T, p, which, j.slot, j.h, j.b);
+  const bool ok = j.live && j.slot >= 0 && (int64_t)j.slot < (int64_t)p.num_pages * kPageSize;
+  if (which == 0) {
+    if (ok) store_k_block(T.codes, T.scales, p.H, j.slot, j.h, j.b, quantize_block16(x, T.g, T.r6));
+    return;
+  }
+  const QuantBlock q = quantize_block16(x, T.g, T.r6);
+  // the partner needs this lane's packed word of its own parity: word 1 from an even slot, word 0 from an odd one
+  const int32_t other_slot = (int32_t)swz_xor1((uint32_t)(ok ? j.slot : -1));
+  const uint32_t other = swz_xor1((j.slot & 1) ? q.packed[0] : q.packed[1]);
+  const uint32_t other_sb = swz_xor1(q.sb);
+  if (!ok) return;
+  if (other_slot == (j.slot ^ 1)) store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, other, other_sb);
+  else store_v_alone(T.codes, T.scales, p.H, j.slot, j.h, j.b, q);
 }
 
 // One job per thread: a single load, quantize and store chain per thread.

@@ -319,7 +319,8 @@ def mx_dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 class MxPlanes:
-    """One layer's paged MXFP4 cache: NVFP4-layout code planes, 64-byte scale tiles."""
+    """One layer's paged MXFP4 cache: 1 KiB code tiles (K as NVFP4 K; V with each
+    slot's nibbles in bytes of its own), 64-byte scale tiles."""
 
     def __init__(self, num_pages: int, num_kv_heads: int):
         self.num_pages = int(num_pages)

@@ -170,18 +170,28 @@ void nvfp4o_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t
  * A page holds 16 token slots; slot s -> page p = s/16, offset o = s%16.
  * Per (page, kv head) each plane holds a 1 KiB code tile and a 128 B scale
  * tile (64 + 8 bytes per token and head: 9/16 byte per value, [MW] §1).
- *   K codes : tile byte o*64 + d/2                              nibble d%2
+ *   K codes : tile byte o*64 + d/2                                   nibble d%2
  *   K scales: tile byte o*8 + d/16
- *   V codes : tile byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2 nibble d%2
+ *   V codes : tile byte (o/4)*256 + (d/8)*16 + ((o/2)%2)*8 + (d%2)*4 + (d%8)/2
+ *                                                                    nibble o%2
  *   V scales: tile byte (d/16)*16 + o
- * Tile (p, h) starts at (p*H + h)*1024 in a code plane and at (p*H + h)*128
- * in a scale plane. */
+ * (nibble 0 = low).  A V code byte holds one dimension of two neighbouring
+ * slots (o even in the low nibble, o+1 in the high one).  The pages fix no
+ * in-page arrangement; this one is the library's.  Tile (p, h) starts at
+ * (p*H + h)*1024 in a code plane and at (p*H + h)*128 in a scale plane. */
 static int64_t k_code_byte(int64_t p, int h, int H, int o, int d) { return (p * H + h) * 1024 + o * 64 + d / 2; }
 static int64_t k_scale_byte(int64_t p, int h, int H, int o, int b) { return (p * H + h) * 128 + o * 8 + b; }
 static int64_t v_code_byte(int64_t p, int h, int H, int o, int d) {
-  return (p * H + h) * 1024 + (o / 4) * 256 + (d / 8) * 16 + (o % 4) * 4 + (d % 8) / 2;
+  return (p * H + h) * 1024 + (o / 4) * 256 + (d / 8) * 16 + ((o / 2) % 2) * 8 + (d % 2) * 4 + (d % 8) / 2;
 }
 static int64_t v_scale_byte(int64_t p, int h, int H, int o, int b) { return (p * H + h) * 128 + b * 16 + o; }
+
+/* Byte and nibble shift (0 or 4) of dimension d of slot offset o in the
+ * tile (p, h) of an NVFP4 code plane. */
+static int64_t code_at(int is_v, int64_t p, int h, int H, int o, int d, int* shift) {
+  *shift = 4 * (is_v ? (o & 1) : (d & 1));
+  return is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+}
 
 /* Write quantized rows (row index t*H + h) into the planes at slot_mapping[t];
  * negative slots are skipped. is_v selects the V layout. */
@@ -197,8 +207,8 @@ void nvfp4o_scatter_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_
       const uint8_t* sr = scales + (t * H + h) * 8;
       for (int d = 0; d < 128; ++d) {
         int code = (cr[d / 2] >> (4 * (d & 1))) & 15;
-        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
-        int sh = 4 * (d & 1);
+        int sh;
+        int64_t at = code_at(is_v, p, h, H, o, d, &sh);
         code_plane[at] = (uint8_t)((code_plane[at] & ~(15 << sh)) | (code << sh));
       }
       for (int b = 0; b < 8; ++b)
@@ -212,8 +222,9 @@ static double plane_value(const uint8_t* code_plane, const uint8_t* scale_plane,
                           double g) {
   int64_t p = s / 16;
   int o = (int)(s % 16);
-  int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
-  int code = (code_plane[at] >> (4 * (d & 1))) & 15;
+  int sh;
+  int64_t at = code_at(is_v, p, h, H, o, d, &sh);
+  int code = (code_plane[at] >> sh) & 15;
   int sb = scale_plane[is_v ? v_scale_byte(p, h, H, o, d / 16) : k_scale_byte(p, h, H, o, d / 16)];
   return nvfp4o_e2m1_value(code) * nvfp4o_e4m3_value(sb) * g;
 }
@@ -231,8 +242,9 @@ void nvfp4o_gather_rows(const uint8_t* code_plane, const uint8_t* scale_plane, i
       uint8_t* cr = codes + (t * H + h) * 64;
       memset(cr, 0, 64);
       for (int d = 0; d < 128; ++d) {
-        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
-        int code = (code_plane[at] >> (4 * (d & 1))) & 15;
+        int sh;
+        int64_t at = code_at(is_v, p, h, H, o, d, &sh);
+        int code = (code_plane[at] >> sh) & 15;
         cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
       }
       for (int b = 0; b < 8; ++b)
@@ -592,13 +604,20 @@ void nvfp4o_mx_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int6
     }
 }
 
-/* MXFP4 pages: the code planes have the NVFP4 code layouts; a scale tile is
- * 64 bytes (4 per token):
+/* MXFP4 pages: K codes as the NVFP4 K codes; V codes keep each slot's nibbles
+ * in bytes of its own (a V byte's two values share one E8M0 scale only if they
+ * are one slot's):
+ *   V codes : tile byte (o/4)*256 + (d/8)*16 + (o%4)*4 + (d%8)/2   nibble d%2
+ * A scale tile is 64 bytes (4 per token):
  *   K scales: tile byte o*4 + d/32         V scales: tile byte (d/32)*16 + o
  * Tile (p, h) starts at (p*H + h)*64 in a scale plane: 68 bytes per (token,
  * kv head) per tensor, 17/32 byte per value. */
 static int64_t mx_scale_byte(int is_v, int64_t p, int h, int H, int o, int b) {
   return (p * H + h) * 64 + (is_v ? b * 16 + o : o * 4 + b);
+}
+static int64_t mx_code_byte(int is_v, int64_t p, int h, int H, int o, int d) {
+  return is_v ? (p * H + h) * 1024 + (o / 4) * 256 + (d / 8) * 16 + (o % 4) * 4 + (d % 8) / 2
+              : k_code_byte(p, h, H, o, d);
 }
 
 void nvfp4o_mx_scatter_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_tokens, int H,
@@ -612,7 +631,7 @@ void nvfp4o_mx_scatter_rows(const uint8_t* codes, const uint8_t* scales, int64_t
       const uint8_t* cr = codes + (t * H + h) * 64;
       for (int d = 0; d < 128; ++d) {
         int code = (cr[d / 2] >> (4 * (d & 1))) & 15;
-        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+        int64_t at = mx_code_byte(is_v, p, h, H, o, d);
         int sh = 4 * (d & 1);
         code_plane[at] = (uint8_t)((code_plane[at] & ~(15 << sh)) | (code << sh));
       }
@@ -631,7 +650,7 @@ void nvfp4o_mx_gather_rows(const uint8_t* code_plane, const uint8_t* scale_plane
       uint8_t* cr = codes + (t * H + h) * 64;
       memset(cr, 0, 64);
       for (int d = 0; d < 128; ++d) {
-        int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+        int64_t at = mx_code_byte(is_v, p, h, H, o, d);
         int code = (code_plane[at] >> (4 * (d & 1))) & 15;
         cr[d / 2] |= (uint8_t)(code << (4 * (d & 1)));
       }
@@ -645,7 +664,7 @@ static double mx_plane_value(const uint8_t* code_plane, const uint8_t* scale_pla
   (void)g;
   int64_t p = s / 16;
   int o = (int)(s % 16);
-  int64_t at = is_v ? v_code_byte(p, h, H, o, d) : k_code_byte(p, h, H, o, d);
+  int64_t at = mx_code_byte(is_v, p, h, H, o, d);
   int code = (code_plane[at] >> (4 * (d & 1))) & 15;
   return nvfp4o_e2m1_value(code) * nvfp4o_e8m0_value(scale_plane[mx_scale_byte(is_v, p, h, H, o, d / 32)]);
 }

@@ -59,10 +59,20 @@ def test_layout_tile_positions():
     tile = (3 * H + 1)
     assert planes.k_codes[tile * 1024 + 9 * 64 + 37 // 2] == 0xF0  # odd dim -> high nibble
     assert planes.k_scales[tile * 128 + 9 * 8 + 2] == 0x38
-    v_at = tile * 1024 + (9 // 4) * 256 + (37 // 8) * 16 + (9 % 4) * 4 + (37 % 8) // 2
-    assert planes.v_codes[v_at] == 0xF0
+    # V: one byte holds one dimension of slots 2k (low nibble) and 2k+1 (high)
+    v_at = tile * 1024 + (9 // 4) * 256 + (37 // 8) * 16 + ((9 // 2) % 2) * 8 + (37 % 2) * 4 + (37 % 8) // 2
+    assert planes.v_codes[v_at] == 0xF0  # odd slot -> high nibble
     assert planes.v_scales[tile * 128 + 2 * 16 + 9] == 0x38
     assert np.count_nonzero(planes.k_codes) == 1 and np.count_nonzero(planes.v_codes) == 1
+    # the even neighbour (offset 8) at an even dimension lands in the low nibble of its own byte
+    row2 = np.zeros((1, H, 128), np.float32)
+    row2[0, 0, 100] = 6.0  # head 0, dim 100: code 0x7
+    oracle.quantize_append(planes, row2, row2, np.array([3 * 16 + 8], np.int32), 1.0, 1.0)
+    t0 = 3 * H
+    assert planes.k_codes[t0 * 1024 + 8 * 64 + 50] == 0x07
+    v2 = t0 * 1024 + (8 // 4) * 256 + (100 // 8) * 16 + ((8 // 2) % 2) * 8 + 0 * 4 + (100 % 8) // 2
+    assert planes.v_codes[v2] == 0x07
+    assert np.count_nonzero(planes.v_codes) == 2
 
 
 def _sdpa_ref(q, k_hat, v_hat, sm_scale):
