@@ -295,20 +295,18 @@ __device__ __forceinline__ void store_v_pair(uint8_t* codes, uint8_t* scales, in
 }
 
 // A slot written without its pair partner: only this slot's nibbles change,
-// by atomic AND then OR on the four words (the partner's nibbles may be
-// written by another lane of the same call).
+// by an atomic AND then OR on each of its two 8-byte halves (the partner's
+// nibbles may be written by another lane of the same call).
 __device__ __forceinline__ void store_v_alone(uint8_t* codes, uint8_t* scales, int H, int32_t slot, int h, int b,
                                               const QuantBlock& q) {
   const bool odd = slot & 1;
-  const uint32_t keep = odd ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+  const uint64_t keep = odd ? 0x0F0F0F0F0F0F0F0Full : 0xF0F0F0F0F0F0F0F0ull;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const uint2 w = odd ? v_pair_words(0u, q.packed[k]) : v_pair_words(q.packed[k], 0u);
-    uint32_t* at = reinterpret_cast<uint32_t*>(v_half(codes, H, slot, h, 2 * b + k));
+    uint64_t* at = reinterpret_cast<uint64_t*>(v_half(codes, H, slot, h, 2 * b + k));
     __hip_atomic_fetch_and(at, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_or(at, w.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_and(at + 1, keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_or(at + 1, w.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(at, (uint64_t)w.x | ((uint64_t)w.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int64_t page = (uint32_t)slot / kPageSize;
   const int o = (int)((uint32_t)slot % kPageSize);

@@ -83,6 +83,7 @@ __device__ __forceinline__ void widen(const RawBlock<InT>& r, float (&x)[16]) {
 template <typename InT>
 struct Job {
   RawBlock<InT> raw;
+  int64_t t;
   int32_t slot;
   bool live;
   int h, b;
@@ -108,17 +109,22 @@ __device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const Appen
   block_coords(i < n_jobs ? i : 0, p, t, j.h, j.b);
   j.live = i < n_jobs && t >= 0;
   const int64_t tt = j.live ? t : 0;
+  j.t = tt;
   j.slot = p.slots ? p.slots[tt] : step_slot(p, tt);  // issued first: waiting for it never waits for the inputs
   j.raw = load_raw<InT>(reinterpret_cast<const InT*>(T.x) + tt * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b);
   return j;
 }
 
 // which (0 = K, 1 = V) is uniform across the wave, and every lane of the wave
-// runs this (lanes without a live job hold token 0 and store nothing): the V
-// path exchanges codes with lane l ^ 1, the job of the other token of the same
-// group of 4 tokens, kv head and block.  When that token's slot is this
-// slot's pair partner (slot ^ 1), the two lanes write the pair's V bytes with
-// plain stores; otherwise this slot's nibbles are set alone.
+// runs this (lanes without a live job hold token 0 and store nothing).  A V
+// block shares its bytes with the same block of the slot's pair partner
+// (slot ^ 1).  The path exchanges codes with lane l ^ 1, the job of the
+// neighbouring token t ^ 1 (same kv head and block); when that token holds the
+// partner slot, the two lanes write the pair's bytes with plain stores.  Else,
+// when the token on the other side (t - 1 for even t, t + 1 for odd t) holds
+// it -- a run of consecutive slots that starts at an odd slot -- this lane
+// quantizes that token's block too (the same bytes its own lane computes) and
+// writes its half the same way.  Otherwise this slot's nibbles are set alone.
 template <typename InT, bool kRotK>
 __device__ __forceinline__ void finish_job(const Job<InT>& j, const AppendTensor& T, const AppendParams& p, int which) {
   float x[16];
@@ -135,8 +141,20 @@ __device__ __forceinline__ void finish_job(const Job<InT>& j, const AppendTensor
   const uint32_t other = swz_xor1((j.slot & 1) ? q.packed[0] : q.packed[1]);
   const uint32_t other_sb = swz_xor1(q.sb);
   if (!ok) return;
-  if (other_slot == (j.slot ^ 1)) store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, other, other_sb);
-  else store_v_alone(T.codes, T.scales, p.H, j.slot, j.h, j.b, q);
+  if (other_slot == (j.slot ^ 1)) {
+    store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, other, other_sb);
+    return;
+  }
+  const int64_t t2 = (j.t & 1) ? j.t + 1 : j.t - 1;
+  if (t2 >= 0 && t2 < p.num_tokens && (p.slots ? p.slots[t2] : step_slot(p, t2)) == (j.slot ^ 1)) {
+    float x2[16];
+    widen<InT>(load_raw<InT>(reinterpret_cast<const InT*>(T.x) + t2 * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b),
+               x2);
+    const QuantBlock q2 = quantize_block16(x2, T.g, T.r6);
+    store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, (j.slot & 1) ? q2.packed[1] : q2.packed[0], q2.sb);
+    return;
+  }
+  store_v_alone(T.codes, T.scales, p.H, j.slot, j.h, j.b, q);
 }
 
 // One job per thread: a single load, quantize and store chain per thread.

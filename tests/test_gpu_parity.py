@@ -67,6 +67,45 @@ def test_append_strided_and_skipped_slots():
     assert planes_equal(layer, planes) == []
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_append_v_slot_pairs(dt):
+    """V bytes are shared by slot pairs (2k, 2k+1).  Slot runs that start at an
+    even slot (neighbouring lanes pair), at an odd slot (a lane quantizes the
+    token on its other side too), in descending order, split pairs written by
+    far-apart tokens, lone slots and pairs with a skipped member, over planes
+    holding random bytes; then a second call fills the partners of the first
+    call's lone slots.  Every plane must match the oracle's bytes."""
+    import nvfp4_quantized_paged_kv_amd as nk
+
+    _say(f"case: append V slot pairs {dt}")
+    H, pool = 3, 16
+    even_run = list(range(16 * 2, 16 * 2 + 20))           # 20 slots from an even slot
+    odd_run = list(range(16 * 4 + 3, 16 * 4 + 3 + 21))     # 21 slots from an odd slot
+    down_run = list(range(16 * 7 + 9, 16 * 7 - 1, -1))     # 10 slots descending from an odd slot
+    lone = [16 * 9 + 4, 16 * 9 + 7, 16 * 10 + 0, 16 * 10 + 13]
+    split = [16 * 11 + 6]
+    skipped_pair = [16 * 12 + 2, -1]
+    slots1 = even_run + odd_run + split + down_run + lone + skipped_pair + [16 * 11 + 7] + [16 * 13 + 1]
+    slots2 = [x ^ 1 for x in lone] + [16 * 12 + 3, 16 * 13 + 0, 16 * 14 + 5, 16 * 14 + 6]
+    rng = np.random.default_rng(21)
+    init = {n: rng.integers(0, 256, (pool * H * (1024 if "codes" in n else 128),), dtype=np.uint8)
+            for n in ("k_codes", "k_scales", "v_codes", "v_scales")}
+    planes = oracle.Planes(pool, H)
+    layer = nk.KVCacheLayer.allocate(pool, H, 0.01, 0.02)
+    for n, a in init.items():
+        getattr(planes, n)[:] = a
+        getattr(layer, n).copy_(torch.from_numpy(a).reshape(getattr(layer, n).shape))
+    for call, slots in enumerate((slots1, slots2)):
+        T = len(slots)
+        k = synth.kv_values(T, H, "sparse6", 0.01, 0, dt, "cpu", 91 + call, 0)
+        v = synth.kv_values(T, H, "sparse6", 0.01, 1, dt, "cpu", 91 + call, 0)
+        sl = np.array(slots, np.int32)
+        oracle.quantize_append(planes, host_f32(k), host_f32(v), sl, 0.01, 0.02)
+        nk.quantize_append(layer, k.cuda(), v.cuda(), torch.from_numpy(sl).cuda())
+        torch.cuda.synchronize()
+        assert planes_equal(layer, planes) == [], f"call {call}"
+
+
 def _tie_rows():
     """Rows whose values sit exactly on E2M1 midpoints / whose amax sits on E4M3 midpoints."""
     mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
