@@ -665,13 +665,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // P as an f16 hi + lo pair (about 22 bits): with P alone in f16 (11
       // bits) a row whose output nearly cancels -- outliers of opposite sign
       // in a few tokens -- could miss 1e-3 relative to the row's largest value.
-      // hi = p cut to 11 significant bits (exact in f16 for p >= 2^-14), lo = the rest.
-      float hf[4];
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) hf[i] = __uint_as_float(__float_as_uint(pr[i]) & 0xFFFFE000u);
-      const half4_t ph = {(_Float16)hf[0], (_Float16)hf[1], (_Float16)hf[2], (_Float16)hf[3]};
-      const half4_t pl = {(_Float16)(pr[0] - hf[0]), (_Float16)(pr[1] - hf[1]), (_Float16)(pr[2] - hf[2]),
-                          (_Float16)(pr[3] - hf[3])};
+      // hi = p rounded toward zero to f16 (11 significant bits for p >= 2^-14),
+      // lo = p - hi (exact in float32) rounded to f16, by the mixed-precision
+      // FMA that reads hi from its packed register and writes f16 directly.
+      // The multiplier 1.0 is opaque to the compiler, which would otherwise
+      // fold the FMA into a subtraction with separate conversions.
+      float one = 1.0f;
+      asm volatile("" : "+s"(one));
+      const half2_t h01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]));
+      const half2_t h23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]));
+      const half4_t ph = {h01[0], h01[1], h23[0], h23[1]};
+      const half4_t pl = {(_Float16)__builtin_fmaf(pr[0], one, -(float)h01[0]),
+                          (_Float16)__builtin_fmaf(pr[1], one, -(float)h01[1]),
+                          (_Float16)__builtin_fmaf(pr[2], one, -(float)h23[0]),
+                          (_Float16)__builtin_fmaf(pr[3], one, -(float)h23[1])};
 
       // ---- O += P . V over the page; lane (dims 8*r .. 8*r+7, tokens 4*q4 .. 4*q4+3).
       // 16x16x16 MFMAs, one for P hi and one for P lo against the same V
