@@ -83,8 +83,10 @@ __device__ __forceinline__ void widen(const RawBlock<InT>& r, float (&x)[16]) {
 template <typename InT>
 struct Job {
   RawBlock<InT> raw;
+  RawBlock<InT> side_raw;  // V jobs at a wave edge: the other-side token's block (see finish_job)
   int64_t t;
   int32_t slot;
+  int32_t side_slot;       // that token's slot, -1 if there is none
   bool live;
   int h, b;
 };
@@ -102,8 +104,11 @@ __device__ __forceinline__ int32_t step_slot(const AppendParams& p, int64_t t) {
 // skipped token, loads token 0 (always in range) and is dropped at the store.
 // Both loads are unconditional (no branch around them), so the compiler can
 // count the memory operations in flight and wait only for the ones it needs.
+// side: also load the slot and block of the token on the other side of the
+// pair (see finish_job), issued with the job's own loads.
 template <typename InT>
-__device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const AppendTensor& T, int64_t i, int64_t n_jobs) {
+__device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const AppendTensor& T, int64_t i, int64_t n_jobs,
+                                              bool side = false) {
   Job<InT> j;
   int64_t t;
   block_coords(i < n_jobs ? i : 0, p, t, j.h, j.b);
@@ -111,8 +116,27 @@ __device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const Appen
   const int64_t tt = j.live ? t : 0;
   j.t = tt;
   j.slot = p.slots ? p.slots[tt] : step_slot(p, tt);  // issued first: waiting for it never waits for the inputs
-  j.raw = load_raw<InT>(reinterpret_cast<const InT*>(T.x) + tt * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b);
+  const InT* x = reinterpret_cast<const InT*>(T.x) + (int64_t)j.h * kHeadDim + 16 * j.b;
+  j.raw = load_raw<InT>(x + tt * p.token_stride);
+  j.side_slot = -1;
+  if (side) {
+    // unconditional (waiting for the slots before loading measured slower)
+    const int64_t t2 = (tt & 1) ? tt + 1 : tt - 1;
+    const bool in = t2 >= 0 && t2 < p.num_tokens;
+    const int64_t tc = in ? t2 : tt;
+    const int32_t s2 = p.slots ? p.slots[tc] : step_slot(p, tc);
+    j.side_slot = in ? s2 : -1;
+    j.side_raw = load_raw<InT>(x + tc * p.token_stride);
+  }
   return j;
+}
+
+// Lanes whose other-side token (t - 1 for even t, t + 1 for odd t) lies in
+// another wave: token 4*tg of an even group tg (lane < 32) and token 4*tg + 3
+// of an odd one.
+__device__ __forceinline__ bool edge_lane() {
+  const int lane = threadIdx.x & 63, tq = lane & 3;
+  return (tq == 0 && lane < 32) || (tq == 3 && lane >= 32);
 }
 
 // which (0 = K, 1 = V) is uniform across the wave, and every lane of the wave
@@ -122,10 +146,14 @@ __device__ __forceinline__ Job<InT> fetch_job(const AppendParams& p, const Appen
 // neighbouring token t ^ 1 (same kv head and block); when that token holds the
 // partner slot, the two lanes write the pair's bytes with plain stores.  Else,
 // when the token on the other side (t - 1 for even t, t + 1 for odd t) holds
-// it -- a run of consecutive slots that starts at an odd slot -- this lane
-// quantizes that token's block too (the same bytes its own lane computes) and
-// writes its half the same way.  Otherwise this slot's nibbles are set alone.
-template <typename InT, bool kRotK>
+// it -- a run of consecutive slots that starts at an odd slot -- the codes
+// come from that token's lane when it is in the same wave (lane l ^ 3 within
+// a group of 4 tokens, l -/+ 29 across the wave's two groups); at a wave edge
+// this lane quantizes that token's block too (the bytes that token's own lane
+// computes), from inputs loaded with its own when the job was fetched with
+// `side`, else loaded here.  Either way it writes its half as above.
+// Otherwise this slot's nibbles are set alone.
+template <typename InT, bool kRotK, bool kSide>
 __device__ __forceinline__ void finish_job(const Job<InT>& j, const AppendTensor& T, const AppendParams& p, int which) {
   float x[16];
   widen<InT>(j.raw, x);
@@ -136,20 +164,40 @@ __device__ __forceinline__ void finish_job(const Job<InT>& j, const AppendTensor
     return;
   }
   const QuantBlock q = quantize_block16(x, T.g, T.r6);
-  // the partner needs this lane's packed word of its own parity: word 1 from an even slot, word 0 from an odd one
-  const int32_t other_slot = (int32_t)swz_xor1((uint32_t)(ok ? j.slot : -1));
-  const uint32_t other = swz_xor1((j.slot & 1) ? q.packed[0] : q.packed[1]);
+  // a partner needs this lane's packed word of its own parity: word 1 from an even slot, word 0 from an odd one
+  const int32_t my_slot = ok ? j.slot : -1;
+  const uint32_t my_word = (j.slot & 1) ? q.packed[0] : q.packed[1];
+  const int32_t other_slot = (int32_t)swz_xor1((uint32_t)my_slot);
+  const uint32_t other = swz_xor1(my_word);
   const uint32_t other_sb = swz_xor1(q.sb);
+  const int lane = threadIdx.x & 63, tq = lane & 3;
+  int src = (tq == 1 || tq == 2) ? (lane ^ 3) : (tq == 0 ? lane - 29 : lane + 29);
+  const bool side_in_wave = src >= 0 && src < 64;
+  src = side_in_wave ? src : lane;
+  const int32_t side_slot = __shfl(my_slot, src);
+  const uint32_t side = (uint32_t)__shfl((int)my_word, src);
+  const uint32_t side_sb = (uint32_t)__shfl((int)q.sb, src);
   if (!ok) return;
   if (other_slot == (j.slot ^ 1)) {
     store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, other, other_sb);
     return;
   }
+  if (side_in_wave) {
+    if (side_slot == (j.slot ^ 1)) store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, side, side_sb);
+    else store_v_alone(T.codes, T.scales, p.H, j.slot, j.h, j.b, q);
+    return;
+  }
   const int64_t t2 = (j.t & 1) ? j.t + 1 : j.t - 1;
-  if (t2 >= 0 && t2 < p.num_tokens && (p.slots ? p.slots[t2] : step_slot(p, t2)) == (j.slot ^ 1)) {
+  RawBlock<InT> raw2 = j.side_raw;
+  int32_t slot2 = j.side_slot;
+  if (!kSide && t2 >= 0 && t2 < p.num_tokens) {
+    slot2 = p.slots ? p.slots[t2] : step_slot(p, t2);
+    if (slot2 == (j.slot ^ 1))
+      raw2 = load_raw<InT>(reinterpret_cast<const InT*>(T.x) + t2 * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b);
+  }
+  if (slot2 == (j.slot ^ 1)) {
     float x2[16];
-    widen<InT>(load_raw<InT>(reinterpret_cast<const InT*>(T.x) + t2 * p.token_stride + (int64_t)j.h * kHeadDim + 16 * j.b),
-               x2);
+    widen<InT>(raw2, x2);
     const QuantBlock q2 = quantize_block16(x2, T.g, T.r6);
     store_v_pair(T.codes, T.scales, p.H, j.slot, j.h, j.b, q, (j.slot & 1) ? q2.packed[1] : q2.packed[0], q2.sb);
     return;
@@ -167,7 +215,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendParams p, in
   const AppendTensor& T = p.t[which];
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_jobs) return;
-  finish_job<InT, kRotK>(fetch_job<InT>(p, T, i, n_jobs), T, p, which);
+  finish_job<InT, kRotK, true>(fetch_job<InT>(p, T, i, n_jobs, which == 1 && edge_lane()), T, p, which);
 }
 
 // Bulk rotated-K appends: a fixed grid of what the device holds at once walks the
@@ -191,13 +239,13 @@ __global__ __launch_bounds__(256) void quantize_append_stream_kernel(AppendParam
   while (true) {
     const Job<InT> b0 = fetch_job<InT>(p, T, i + 2 * stride, n_jobs);
     const Job<InT> b1 = fetch_job<InT>(p, T, i + 3 * stride, n_jobs);
-    finish_job<InT, kRotK>(a0, T, p, which);
-    finish_job<InT, kRotK>(a1, T, p, which);
+    finish_job<InT, kRotK, false>(a0, T, p, which);
+    finish_job<InT, kRotK, false>(a1, T, p, which);
     if (i + 2 * stride >= n_jobs) break;  // uniform across the wave
     a0 = fetch_job<InT>(p, T, i + 4 * stride, n_jobs);
     a1 = fetch_job<InT>(p, T, i + 5 * stride, n_jobs);
-    finish_job<InT, kRotK>(b0, T, p, which);
-    finish_job<InT, kRotK>(b1, T, p, which);
+    finish_job<InT, kRotK, false>(b0, T, p, which);
+    finish_job<InT, kRotK, false>(b1, T, p, which);
     i += 4 * stride;
     if (i >= n_jobs) break;
   }
