@@ -365,13 +365,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QF32 ? 2 : 
         for (int i = 0; i < 4; ++i)  // the rounded product, as in pm: t - m_run <= kExtLazyMax for any logit
           pr[i] = __builtin_amdgcn_exp2f(S[kb][rb][i] * tscale[rb] - m_run[rb]);
         l_run[rb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        // hi = p cut to 11 significant bits (exact in f16 for p >= 2^-14), lo = the rest
-        float hf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hf[i] = __uint_as_float(__float_as_uint(pr[i]) & 0xFFFFE000u);
-        pa[rb][kb] = half4_t{(_Float16)hf[0], (_Float16)hf[1], (_Float16)hf[2], (_Float16)hf[3]};
-        pl[rb][kb] = half4_t{(_Float16)(pr[0] - hf[0]), (_Float16)(pr[1] - hf[1]), (_Float16)(pr[2] - hf[2]),
-                             (_Float16)(pr[3] - hf[3])};
+        // hi = p rounded toward zero to f16 (11 significant bits for p >= 2^-14) by
+        // the packed conversion; lo = p - hi (exact in float32) rounded to f16 by
+        // the mixed-precision FMA, which reads hi from the packed register.  The
+        // multiplier 1.0 is opaque to the compiler, which would otherwise fold the
+        // FMA into a subtraction with separate conversions.
+        float one = 1.0f;
+        asm volatile("" : "+s"(one));
+        const half2_t h01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]));
+        const half2_t h23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]));
+        pa[rb][kb] = half4_t{h01[0], h01[1], h23[0], h23[1]};
+        pl[rb][kb] = half4_t{(_Float16)__builtin_fmaf(pr[0], one, -(float)h01[0]),
+                             (_Float16)__builtin_fmaf(pr[1], one, -(float)h01[1]),
+                             (_Float16)__builtin_fmaf(pr[2], one, -(float)h23[0]),
+                             (_Float16)__builtin_fmaf(pr[3], one, -(float)h23[1])};
       }
     }
 

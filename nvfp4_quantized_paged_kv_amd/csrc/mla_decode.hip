@@ -289,10 +289,18 @@ __global__ __launch_bounds__(WAVES * 64) void mla_decode_kernel(MlaDecodeParams 
     l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
     // P as an f16 hi + lo pair (about 22 bits); k-slot 8*g4 + j is entry 4*g4 + j (j < 4) or 16 + 4*g4 + j - 4
     half8_t ph, pl;
+    // hi by the packed round-toward-zero conversion, lo = p - hi by the
+    // mixed-precision FMA reading hi from the packed register (1.0 kept opaque
+    // so that the FMA is not folded into a subtraction with separate conversions)
+    float one = 1.0f;
+    asm volatile("" : "+s"(one));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ph[j] = (_Float16)pr[j];
-      pl[j] = (_Float16)(pr[j] - (float)ph[j]);
+    for (int j = 0; j < 8; j += 2) {
+      const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pr[j], pr[j + 1]));
+      ph[j] = h[0];
+      ph[j + 1] = h[1];
+      pl[j] = (_Float16)__builtin_fmaf(pr[j], one, -(float)h[0]);
+      pl[j + 1] = (_Float16)__builtin_fmaf(pr[j + 1], one, -(float)h[1]);
     }
 
     // ---- O += P . V; V operand of dims 16m .. 16m+15: lane (dim 16m + r, entries 4*g4 .. +3 and
